@@ -1,0 +1,240 @@
+"""Plain float64 reference of the attention forward and its ring-share pieces.
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.  Nothing here is
+blocked, fused or reordered: scores are materialised in full, softmax is the
+two-pass definition, and the ring share is computed as the local query rows
+against every key at its absolute position (no ring is emulated).
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# --------------------------------------------------------------------------
+# dtype rounding
+# --------------------------------------------------------------------------
+def round_to_dtype(x, dtype: str) -> np.ndarray:
+    """Round float64 values to ``dtype`` ("f32" or "bf16") with
+    round-to-nearest-even, returning them widened back to float64.
+
+    bf16 keeps 8 significant bits.  The rounding is done directly on the
+    float64 bit pattern (bit 45 is the last kept mantissa bit), so there is no
+    double rounding through float32 for normal numbers; values below the
+    bf16 normal range (|x| < 2^-126, never drawn here) go through float32.
+    Used for the reading that rotated q and k are rounded to the input dtype
+    before the dot product (RoPE applied to stored bf16 tensors).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    u = np.ascontiguousarray(x).view(np.uint64).copy()
+    keep = np.uint64(45)
+    lsb = (u >> keep) & np.uint64(1)
+    half = np.uint64((1 << 44) - 1)
+    r = ((u + half + lsb) >> keep) << keep
+    out = r.view(np.float64).reshape(x.shape)
+    tiny = np.abs(x) < 2.0 ** -126
+    if np.any(tiny):
+        t32 = x[tiny].astype(np.float32).view(np.uint32).astype(np.uint64)
+        t32 = ((t32 + np.uint64(0x7FFF) + ((t32 >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)) << np.uint64(16)
+        out = out.copy()
+        out[tiny] = t32.astype(np.uint32).view(np.float32).astype(np.float64)
+    return out
+
+
+# --------------------------------------------------------------------------
+# rotary position embedding
+# --------------------------------------------------------------------------
+def rope_frequencies(d: int, base: float) -> np.ndarray:
+    """theta_t = base^(-2t/d) for pair t = 0 .. d/2-1 (RoFormer's schedule;
+    the digest entry #4 of "Transformers and Attention" only states that an
+    even-dimensional vector is split into coordinate pairs, each rotated by a
+    positional angle).  Parity against an external RoPE: unpinned."""
+    t = np.arange(d // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * t / d)
+
+
+def rope_rotate(x, pos, base: float) -> np.ndarray:
+    """Rotate adjacent coordinate pairs (2t, 2t+1) of x[..., T, H, d] by the
+    angle pos[T] * theta_t ("Transformers and Attention", #4 RoFormer and #30:
+    sine/cosine rotations).  Pair (x0, x1) becomes
+    (x0 cos a - x1 sin a, x0 sin a + x1 cos a).  float64 throughout."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("RoPE needs an even head dimension")
+    pos = np.asarray(pos, dtype=np.float64)
+    ang = pos[:, None] * rope_frequencies(d, base)[None, :]          # (T, d/2)
+    c = np.cos(ang)[:, None, :]                                      # (T, 1, d/2) -> broadcast over heads
+    s = np.sin(ang)[:, None, :]
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = x0 * c - x1 * s
+    y[..., 1::2] = x0 * s + x1 * c
+    return y
+
+
+# --------------------------------------------------------------------------
+# scaled dot-product attention, plain definition
+# --------------------------------------------------------------------------
+def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=None,
+         rope_base: float = 0.0, dtype: str = "bf16") -> Tuple[np.ndarray, np.ndarray]:
+    """out, lse of softmax(q k^T / sqrt(d) + mask) v for every (batch, head).
+
+    q: (B, Tq, H, d), k and v: (B, Tkv, H, d) holding the exact input values;
+    q_pos[Tq], kv_pos[Tkv]: absolute token positions (causal test and RoPE).
+    kpm: (B, Tkv), nonzero = ignored key; attn_mask: (Tq, Tkv), nonzero =
+    forbidden pair.  Their exclusions combine ("Transformers and Attention"
+    #2), and causal order keeps the diagonal and everything before it (#24;
+    "CP: Split Long Contexts Across GPUs", "Why attention needs information
+    from other GPUs": t3 attends to t0..t3).
+
+    Scores are scaled by 1/sqrt(d) (#15, #22).  Row softmax is the two-pass
+    safe form (brunomaga.github.io post, "Improving numerical stability"):
+    m = max of the allowed scores, e = exp(s - m) on allowed entries and
+    exactly 0 elsewhere, l = sum e, out = (e / l) v, lse = m + ln l (the
+    log-sum-exp of the allowed scores, "LSE" in the same section).
+    A row with no allowed key returns out = 0 and lse = -inf.
+
+    Returns out (B, Tq, H, d_v) and lse (B, H, Tq), both float64 (the value
+    width d_v may differ from d, "Transformers and Attention" #24).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Tq, H, d = q.shape
+    Tkv = k.shape[1]
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    kv_pos = np.asarray(kv_pos, dtype=np.int64)
+    if rope_base > 0:
+        q = round_to_dtype(rope_rotate(q, q_pos, rope_base), dtype)
+        k = round_to_dtype(rope_rotate(k, kv_pos, rope_base), dtype)
+
+    allowed = np.ones((B, Tq, Tkv), dtype=bool)
+    if kpm is not None:
+        allowed &= ~(np.asarray(kpm) != 0)[:, None, :]
+    if attn_mask is not None:
+        allowed &= ~(np.asarray(attn_mask) != 0)[None, :, :]
+    if causal:
+        allowed &= (kv_pos[None, None, :] <= q_pos[None, :, None])
+
+    scale = 1.0 / math.sqrt(d)
+    dv = v.shape[-1]
+    out = np.zeros((B, Tq, H, dv), dtype=np.float64)
+    lse = np.full((B, H, Tq), NEG_INF, dtype=np.float64)
+    for b in range(B):
+        ok = allowed[b]
+        has = ok.any(axis=1)
+        for h in range(H):
+            s = scale * (q[b, :, h, :] @ k[b, :, h, :].T)            # (Tq, Tkv)
+            sm = np.where(ok, s, NEG_INF)
+            m = np.max(sm, axis=1) if Tkv else np.full(Tq, NEG_INF)
+            m_safe = np.where(has, m, 0.0)
+            with np.errstate(over="ignore"):                        # masked garbage may overflow; it is discarded
+                e = np.where(ok, np.exp(s - m_safe[:, None]), 0.0)
+            l = e.sum(axis=1)
+            l_safe = np.where(has, l, 1.0)
+            p = e / l_safe[:, None]
+            out[b, :, h, :] = p @ v[b, :, h, :]
+            lse[b, h, :] = np.where(has, m_safe + np.log(l_safe), NEG_INF)
+    return out, lse
+
+
+def attention(q, k, v, *, q_off: int = 0, kv_off: int = 0, **kw) -> Tuple[np.ndarray, np.ndarray]:
+    """``sdpa`` with contiguous positions q_off + i and kv_off + j."""
+    Tq = np.asarray(q).shape[1]
+    Tkv = np.asarray(k).shape[1]
+    return sdpa(q, k, v, q_off + np.arange(Tq), kv_off + np.arange(Tkv), **kw)
+
+
+# --------------------------------------------------------------------------
+# merge of partial (out, lse) results
+# --------------------------------------------------------------------------
+def merge(out_a, lse_a, out_b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
+    """Combine two partial results over disjoint key sets.
+
+    The pages call an accumulate function for each ring step but never define
+    it; this follows from the fraction form of attention (brunomaga.github.io
+    post, "Ring Attention": out = sum exp(s) v / sum exp(s)), the rescale of
+    both accumulators by exp of the max difference and the LogSumExp carry
+    ("Improving numerical stability"), and the warning that block outputs must
+    not simply be added or averaged ("CP: Split Long Contexts Across GPUs",
+    "Circulate K/V blocks with Ring").
+
+    lse = m* + ln(e^(lse_a - m*) + e^(lse_b - m*)), m* = max(lse_a, lse_b);
+    out = e^(lse_a - lse) out_a + e^(lse_b - lse) out_b.  (0, -inf) is the
+    identity; two empty partials give (0, -inf).
+    out_*: (B, Tq, H, d); lse_*: (B, H, Tq).
+    """
+    oa = np.asarray(out_a, dtype=np.float64)
+    ob = np.asarray(out_b, dtype=np.float64)
+    la = np.asarray(lse_a, dtype=np.float64)
+    lb = np.asarray(lse_b, dtype=np.float64)
+    mx = np.maximum(la, lb)
+    empty = ~np.isfinite(mx)
+    mx_safe = np.where(empty, 0.0, mx)
+    with np.errstate(invalid="ignore"):
+        tot = np.exp(la - mx_safe) + np.exp(lb - mx_safe)
+    lse = np.where(empty, NEG_INF, mx_safe + np.log(np.where(empty, 1.0, tot)))
+    lse_safe = np.where(empty, 0.0, lse)
+    wa = np.where(empty, 0.0, np.exp(la - lse_safe))                  # (B, H, Tq)
+    wb = np.where(empty, 0.0, np.exp(lb - lse_safe))
+    wa = np.transpose(wa, (0, 2, 1))[..., None]                      # (B, Tq, H, 1)
+    wb = np.transpose(wb, (0, 2, 1))[..., None]
+    out = wa * oa + wb * ob
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# ring placement and order (integer bookkeeping)
+# --------------------------------------------------------------------------
+def ring_order(P: int, rank: int) -> List[int]:
+    """Blocks rank ``rank`` sees, in order: its own, then the one of the
+    previous rank, and so on ("CP: Split Long Contexts Across GPUs", "Circulate
+    K/V blocks with Ring": GPU 0 of 4 sees K0, K3, K2, K1; brunomaga.github.io
+    post, "Distributed algorithm": P steps, receive from the previous rank)."""
+    return [(rank - s) % P for s in range(P)]
+
+
+def zigzag_chunks(P: int, rank: int) -> Tuple[int, int]:
+    """Chunks of size T/(2P) owned by ``rank`` under the load-balanced causal
+    placement: an early chunk and its mirror ("CP: Split Long Contexts Across
+    GPUs", "Balance the workload in causal attention": with P = 2 and 8 tokens
+    GPU 0 owns t0, t1, t6, t7)."""
+    return rank, 2 * P - 1 - rank
+
+
+def local_query_positions(T: int, P: int, rank: int, zigzag: bool) -> np.ndarray:
+    """Absolute positions of the query rows a rank owns (also the positions
+    of the K/V block it starts the ring with)."""
+    if zigzag:
+        c = T // (2 * P)
+        a, b = zigzag_chunks(P, rank)
+        return np.concatenate([np.arange(a * c, (a + 1) * c), np.arange(b * c, (b + 1) * c)])
+    c = T // P
+    return np.arange(rank * c, (rank + 1) * c)
+
+
+def allowed_pairs(q_pos: Iterable[int], kv_pos: Iterable[int], causal: bool = True) -> int:
+    """Brute-force count of allowed (query, key) pairs."""
+    qp = np.asarray(list(q_pos), dtype=np.int64)
+    kp = np.asarray(list(kv_pos), dtype=np.int64)
+    if not causal:
+        return int(qp.size * kp.size)
+    return int((kp[None, :] <= qp[:, None]).sum())
+
+
+def zigzag_pairs_closed_form(P: int, c: int) -> int:
+    """Causal pairs of one zigzag rank with chunk size c: the early chunk r
+    sees r*c earlier keys plus its own triangle, the late chunk 2P-1-r sees
+    (2P-1-r)*c earlier keys plus its own triangle; the sum is rank-independent,
+    (2P-1) c^2 + c (c+1)."""
+    return (2 * P - 1) * c * c + c * (c + 1)
