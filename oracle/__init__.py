@@ -27,6 +27,7 @@ implementation (none is available offline).
 from .reference import (  # noqa: F401
     round_to_dtype,
     rope_rotate,
+    rope_rotate_f32,
     rope_frequencies,
     sdpa,
     attention,

@@ -82,6 +82,39 @@ def rope_rotate(x, pos, base: float) -> np.ndarray:
     return y
 
 
+def rope_rotate_f32(x, pos, base: float) -> np.ndarray:
+    """The rotation evaluated in float32, the precision in which the rounded
+    operands q' and k' are decided.
+
+    The pages do not say in what precision a rotated vector is formed before
+    it is stored in the input dtype.  Since that rounding is a quantisation
+    decision, it is taken in the kernels' precision: cos and sin of the
+    float64 angle pos * theta_t rounded to float32, and each output formed as
+    one fused multiply-add over a float32 product,
+        y0 = fma(x0, c, -fl32(x1 s)),   y1 = fma(x0, s, fl32(x1 c)).
+    The fused multiply-add is evaluated in float64 (x0 c is exact there) and
+    rounded to float32; this differs from a single rounding only when the
+    float64 value lies exactly on a float32 rounding midpoint.
+    Input values must be float32-representable.  Returns float64 arrays
+    holding float32 values.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("RoPE needs an even head dimension")
+    pos = np.asarray(pos, dtype=np.float64)
+    ang = pos[:, None] * rope_frequencies(d, base)[None, :]
+    c = np.cos(ang).astype(np.float32).astype(np.float64)[:, None, :]
+    s = np.sin(ang).astype(np.float32).astype(np.float64)[:, None, :]
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    f32 = lambda a: a.astype(np.float32).astype(np.float64)  # noqa: E731
+    y = np.empty_like(x)
+    y[..., 0::2] = f32(x0 * c - f32(x1 * s))
+    y[..., 1::2] = f32(x0 * s + f32(x1 * c))
+    return y
+
+
 # --------------------------------------------------------------------------
 # scaled dot-product attention, plain definition
 # --------------------------------------------------------------------------
@@ -97,7 +130,9 @@ def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=No
     "CP: Split Long Contexts Across GPUs", "Why attention needs information
     from other GPUs": t3 attends to t0..t3).
 
-    Scores are scaled by 1/sqrt(d) (#15, #22).  Row softmax is the two-pass
+    With rope_base > 0, q and k are first rotated (``rope_rotate_f32``) and
+    rounded to ``dtype``, as if the rotation had been applied to the stored
+    tensors.  Scores are scaled by 1/sqrt(d) (#15, #22).  Row softmax is the two-pass
     safe form (brunomaga.github.io post, "Improving numerical stability"):
     m = max of the allowed scores, e = exp(s - m) on allowed entries and
     exactly 0 elsewhere, l = sum e, out = (e / l) v, lse = m + ln l (the
@@ -115,8 +150,8 @@ def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=No
     q_pos = np.asarray(q_pos, dtype=np.int64)
     kv_pos = np.asarray(kv_pos, dtype=np.int64)
     if rope_base > 0:
-        q = round_to_dtype(rope_rotate(q, q_pos, rope_base), dtype)
-        k = round_to_dtype(rope_rotate(k, kv_pos, rope_base), dtype)
+        q = round_to_dtype(rope_rotate_f32(q, q_pos, rope_base), dtype)
+        k = round_to_dtype(rope_rotate_f32(k, kv_pos, rope_base), dtype)
 
     allowed = np.ones((B, Tq, Tkv), dtype=bool)
     if kpm is not None:

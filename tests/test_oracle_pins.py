@@ -397,3 +397,21 @@ def test_fused_rope_equals_stored_bf16_rotation_then_attention():
 
 def workloads_bf16(shape, seed):
     return torch.from_numpy(_rand(shape, seed)).to(torch.float32).to(torch.bfloat16).double().numpy()
+
+
+def test_float32_rotation_is_the_rotation_to_float32_accuracy():
+    """The float32 evaluation agrees with the float64 rotation within its
+    error bound (a few float32 ulps of the pair norm), is the identity at
+    position 0, and keeps the turning sense.  Catches a sign, pairing or
+    operand-order mistake in the float32 path."""
+    d, base = 128, 10000.0
+    x = workloads_bf16((1, 50, 3, d), 70)
+    pos = np.concatenate([[0, 1, 2], np.arange(131000, 131047)])
+    a = oracle.rope_rotate(x, pos, base)
+    b = oracle.rope_rotate_f32(x, pos, base)
+    norm = np.sqrt(x[..., 0::2] ** 2 + x[..., 1::2] ** 2).repeat(2, axis=-1)
+    assert np.all(np.abs(a - b) <= norm * 2 ** -21 + 1e-30)
+    np.testing.assert_array_equal(b[:, 0], x[:, 0])
+    assert np.all(b == b.astype(np.float32).astype(np.float64))
+    y = oracle.rope_rotate_f32(np.tile(np.array([1.0, 0.0]), (1, 1, 1, d // 2)), np.array([1]), base)[0, 0, 0]
+    assert y[1] == np.float32(np.sin(1.0))           # pair 0 turns by +1 rad
