@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Attention-forward throughput of one MI355X on a seeded synthetic workload.
+
+Default workload: one rank's share of an 8-way zigzag ring at 128K context
+(B=1, H=32, d=128, bf16, causal, RoPE base 10000): 16384 local query rows
+against 131072 keys in ring order, 17 attention sub-calls merged into a float32
+accumulator and cast to bf16.  One step is one whole share (attn_ring_fwd),
+inputs resident in HBM.  `--workload N` selects another of the five workloads.
+
+value  = algorithmic TFLOP/s of the step: 4 d FLOPs per allowed (query, key)
+         pair (two contractions, 2 FLOPs per multiply-add); masked work that
+         tiles skip is not counted.
+roofline = the attention kernel alone: the same algorithmic FLOPs divided by
+         the kernel's own time, measured with HIP events recorded around every
+         launch on the launch's stream during the timed steps, against the
+         MI355X dense bf16 MFMA peak (2516.6 TFLOP/s).
+cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample
+         of the same workload (rank 0, one GPU only).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import blockwise_online_softmax_attn_amd as bosa  # noqa: E402
+import workloads  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s and % of MFMA bf16 peak (causal, d=128) on 1 MI355X"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_F32_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json")
+KERNEL_SOURCES = ["blockwise_online_softmax_attn_amd/csrc/fwd_bf16.hip",
+                  "blockwise_online_softmax_attn_amd/csrc/common.h"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+# ---------------------------------------------------------------- pair counts
+def causal_pairs(q_pos0: int, nq: int, kv_pos0: int, nk: int, valid=None) -> int:
+    """Allowed pairs of a contiguous query block against a contiguous key
+    block under causal order, optionally restricted to keys with valid=True."""
+    i = np.arange(nq, dtype=np.int64)
+    lim = np.clip(q_pos0 + i - kv_pos0 + 1, 0, nk)          # keys [0, lim) are not in the future
+    if valid is None:
+        return int(lim.sum())
+    prefix = np.concatenate([[0], np.cumsum(valid.astype(np.int64))])
+    return int(prefix[lim].sum())
+
+
+def step_pairs(w, plan, kpm) -> int:
+    """Allowed (query, key) pairs of one step, summed over batch and heads."""
+    total = 0
+    for b in range(w.B):
+        valid = None if kpm is None else (kpm[b].numpy() == 0)
+        if plan is None:
+            if w.causal:
+                total += causal_pairs(0, w.T, 0, w.T, valid)
+            else:
+                total += w.T * (w.T if valid is None else int(valid.sum()))
+        else:
+            for c in plan:
+                vb = None if valid is None else valid[c.kv_pos0:c.kv_pos0 + c.kv_rows]
+                if w.causal:
+                    total += causal_pairs(c.q_pos0, c.q_rows, c.kv_pos0, c.kv_rows, vb)
+                else:
+                    total += c.q_rows * (c.kv_rows if vb is None else int(vb.sum()))
+    return total * w.H
+
+
+# ---------------------------------------------------------------- inputs
+def build_inputs(w):
+    dev = torch.device("cuda:0")
+    kpm = workloads.key_padding_mask(w)
+    if w.ring_P > 1:
+        plan = bosa.attn_ring_plan(w.T, w.ring_P, w.ring_rank, w.zigzag, w.causal)
+        # the rank's local query chunks, in local order
+        firsts = {}
+        for c in plan:
+            firsts.setdefault(c.q_row0, c.q_pos0)
+        chunks = [firsts[r] // w.chunk for r in sorted(firsts)]
+        q = workloads.draw_tokens(w, 0, chunks)
+        qpos = np.concatenate([np.arange(firsts[r], firsts[r] + plan[0].q_rows) for r in sorted(firsts)])
+    else:
+        plan = None
+        q = workloads.draw_tokens(w, 0, range(w.n_chunks))
+        qpos = np.arange(w.T)
+    k = workloads.draw_tokens(w, 1, range(w.n_chunks))
+    v = workloads.draw_tokens(w, 2, range(w.n_chunks))
+    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    dkpm = None if kpm is None else kpm.to(dev)
+    return plan, (q, k, v, kpm, qpos), (dq, dk, dv, dkpm)
+
+
+def make_step(w, plan, dev_inputs):
+    dq, dk, dv, dkpm = dev_inputs
+    out = torch.empty_like(dq)
+    Tq = dq.shape[1]
+    lse = torch.empty((w.B, w.H, Tq), dtype=torch.float32, device=dq.device)
+    if plan is not None:
+        acc = out if dq.dtype == torch.float32 else torch.empty(dq.shape, dtype=torch.float32, device=dq.device)
+
+        def step():
+            bosa.attn_ring_fwd(dq, dk, dv, P=w.ring_P, rank=w.ring_rank, zigzag=w.zigzag, causal=w.causal,
+                               kpm=dkpm, rope_base=w.rope_base, out=out, lse=lse, acc=acc)
+        return step, len(plan)
+
+    def step():
+        bosa.attn_fwd(dq, dk, dv, out, lse, causal=w.causal, kpm=dkpm, rope_base=w.rope_base)
+    return step, 1
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(w, host_inputs, rows: int, heads: int):
+    """The fp64 oracle, as it stands, on the heaviest `rows` local query rows
+    of the first `heads` heads against every key (bounded sample)."""
+    import threadpoolctl
+
+    import oracle
+    q, k, v, kpm, qpos = host_inputs
+    sel = np.arange(q.shape[1] - rows, q.shape[1])
+    qs = q[:, sel, :heads].double().numpy()
+    ks = k[:, :, :heads].double().numpy()
+    vs = v[:, :, :heads].double().numpy()
+    info = threadpoolctl.threadpool_info()
+    blas_threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    oracle.sdpa(qs, ks, vs, qpos[sel], np.arange(w.T), causal=w.causal,
+                kpm=None if kpm is None else kpm.numpy(), rope_base=w.rope_base, dtype=w.dtype)
+    dt = time.perf_counter() - t0
+    pairs = 0
+    for b in range(w.B):
+        valid = None if kpm is None else (kpm[b].numpy() == 0)
+        for p in qpos[sel]:
+            lim = min(int(p) + 1, w.T) if w.causal else w.T
+            pairs += lim if valid is None else int(valid[:lim].sum())
+    flops = 4.0 * w.d * pairs * heads
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"{rows} query rows (local rows {sel[0]}..{sel[-1]}, positions {int(qpos[sel[0]])}.."
+                   f"{int(qpos[sel[-1]])}) x {heads} of {w.H} heads x B={w.B} against all {w.T} keys, "
+                   f"{'causal' if w.causal else 'non-causal'}{', RoPE' if w.rope_base else ''}: "
+                   f"{flops:.3e} algorithmic FLOPs in {dt:.2f} s (float64 numpy, BLAS threads={blas_threads}, "
+                   f"host cpus={os.cpu_count()})"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-heads", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the ring on a single GPU (the ring itself is emulated "
+              "on that GPU); runs on more than one GPU are not part of this build. Use --gpus 1.",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    bosa.load()
+    w = workloads.WORKLOADS[args.workload]
+    log(f"workload {w.name}: drawing inputs")
+    plan, host, dev = build_inputs(w)
+    step, launches = make_step(w, plan, dev)
+    pairs = step_pairs(w, plan, host[3])
+    flops = 4.0 * w.d * pairs
+    log(f"{pairs} allowed pairs/step = {flops:.4e} FLOPs; {launches} attention launches/step; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    with bosa.KernelTimer(max_launches=args.steps * launches + 16) as kt:
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            step()
+        end.record()
+        torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    kern_ms = float(np.sum(kt.ms))
+    n_launch = len(kt.ms)
+    achieved = flops * args.steps / (kern_ms * 1e-3) / 1e12 if kern_ms > 0 else None
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    log(f"{ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of peak); kernel-only "
+        f"{achieved:.1f} TFLOP/s over {n_launch} launches (avg {kern_ms / max(n_launch, 1):.4f} ms)")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sources_sha256") == kernel_sources_sha() and tr.get("workload") == w.name:
+            traffic = tr.get("bytes_per_launch")
+    roofline = {
+        "bound": "mfma",
+        "achieved": achieved,
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": (achieved / peak) if achieved else None,
+        "traffic": traffic,
+        "kernel": "attn_fwd_bf16_kernel<128>" if (w.dtype == "bf16" and w.d == 128) else
+                  ("attn_fwd_bf16_kernel<64>" if w.dtype == "bf16" else f"attn_fwd_f32_kernel<{w.d}>"),
+        "launches": n_launch,
+        "avg_launch_ms": kern_ms / max(n_launch, 1),
+        "flops_per_launch": flops * args.steps / max(n_launch, 1),
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows x {args.cpu_heads} heads")
+        cpu = cpu_baseline(w, host, args.cpu_rows, args.cpu_heads)
+        log(f"cpu baseline {cpu['value']:.3e} TFLOP/s")
+    line = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": 100.0 * tflops / peak,
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "Tq_local": int(dev[0].shape[1]), "d": w.d,
+            "causal": w.causal, "rope_base": w.rope_base, "kpm_len_range": w.kpm_len_range,
+            "ring_P": w.ring_P, "ring_rank": w.ring_rank, "zigzag": w.zigzag,
+            "attention_launches_per_step": launches, "algorithmic_flops_per_step": flops,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

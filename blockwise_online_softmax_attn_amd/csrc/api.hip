@@ -1,0 +1,409 @@
+// Host side of the C ABI: argument validation (before any HIP call), dtype /
+// head-dim dispatch, stream-ordered workspace for the rotary table and the
+// live-tile list, the ring-share plan and its executor.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+using namespace bosa;
+
+namespace {
+
+thread_local std::string g_err;
+
+// Launch timing (attn_profile_start / attn_profile_stop).
+struct Profile {
+    bool on = false;
+    int cap = 0, n = 0;
+    std::vector<hipEvent_t> ev;   // 2 per launch
+};
+thread_local Profile g_prof;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kTile = 64;   // key tile of the bf16 kernel (live-tile list granularity)
+
+// Stream-ordered scratch: allocated on the call's stream, released on it after
+// the last kernel that uses it, so nothing outlives the call.
+struct Scratch {
+    void* ptr = nullptr;
+    hipStream_t s = nullptr;
+    ~Scratch() {
+        if (ptr) (void)hipFreeAsync(ptr, s);
+    }
+    hipError_t alloc(size_t bytes, hipStream_t stream) {
+        s = stream;
+        if (bytes == 0) return hipSuccess;
+        return hipMallocAsync(&ptr, bytes, stream);
+    }
+};
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Call {
+    const void* q; const void* k; const void* v; void* out; float* lse;
+    int B, H, Tq, Tkv, d;
+    long long q_off, kv_off;
+    int causal;
+    const uint8_t* kpm; const uint8_t* amask;
+    int dtype; unsigned flags;
+    // strides (elements)
+    long long q_bstride, kv_bstride, o_bstride, kpm_bstride, lse_bstride;
+    int lse_hstride, amask_stride;
+    const float2* rope_q; const float2* rope_k;
+};
+
+Call plain_call(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Tq, int Tkv,
+                int d, long long q_off, long long kv_off, int causal, const uint8_t* kpm, const uint8_t* amask,
+                int dtype, unsigned flags) {
+    Call c{};
+    c.q = q; c.k = k; c.v = v; c.out = out; c.lse = lse;
+    c.B = B; c.H = H; c.Tq = Tq; c.Tkv = Tkv; c.d = d;
+    c.q_off = q_off; c.kv_off = kv_off; c.causal = causal;
+    c.kpm = kpm; c.amask = amask; c.dtype = dtype; c.flags = flags;
+    c.q_bstride = (long long)Tq * H * d;
+    c.kv_bstride = (long long)Tkv * H * d;
+    c.o_bstride = (long long)Tq * H * d;
+    c.kpm_bstride = Tkv;
+    c.lse_bstride = (long long)H * Tq;
+    c.lse_hstride = Tq;
+    c.amask_stride = Tkv;
+    return c;
+}
+
+size_t kpm_list_bytes(const Call& c) {
+    if (!c.kpm || c.dtype != ATTN_BF16 || (c.flags & ATTN_NO_TILE_SKIP)) return 0;
+    const long long ntk = (c.Tkv + kTile - 1) / kTile;
+    return align_up((size_t)c.B * (size_t)(ntk + 1) * sizeof(int));
+}
+
+// Enqueue one validated call.  `list` is scratch of kpm_list_bytes(c) bytes.
+int enqueue(const Call& c, int* list, hipStream_t s) {
+    hipError_t e;
+    if (c.Tkv == 0) {
+        if (c.flags & ATTN_ACCUMULATE) return ATTN_OK;  // merging an empty partial changes nothing
+        const bool f32out = c.dtype == ATTN_F32 || (c.flags & ATTN_OUT_F32);
+        e = launch_fill_empty(c.out, f32out ? 0 : 1, c.lse, c.B, c.H, c.Tq, c.d, c.o_bstride, c.H * c.d,
+                              c.lse_bstride, c.lse_hstride, s);
+        return e == hipSuccess ? ATTN_OK : hip_fail(e, "empty-key fill");
+    }
+    FwdParams p{};
+    p.q = c.q; p.k = c.k; p.v = c.v; p.out = c.out; p.lse = c.lse;
+    p.kpm = c.kpm; p.amask = c.amask;
+    p.rope_q = c.rope_q; p.rope_k = c.rope_k;
+    p.kpm_list = nullptr;
+    p.q_bstride = c.q_bstride; p.kv_bstride = c.kv_bstride; p.o_bstride = c.o_bstride;
+    p.kpm_bstride = c.kpm_bstride; p.lse_bstride = c.lse_bstride;
+    p.row_stride = c.H * c.d; p.lse_hstride = c.lse_hstride; p.amask_stride = c.amask_stride;
+    p.B = c.B; p.H = c.H; p.Tq = c.Tq; p.Tkv = c.Tkv;
+    p.q_off = c.q_off; p.kv_off = c.kv_off; p.causal = c.causal ? 1 : 0;
+    p.flags = c.flags;
+    p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.d));
+    if (c.dtype == ATTN_BF16) {
+        if (list) {
+            const int ntk = (c.Tkv + kTile - 1) / kTile;
+            e = launch_kpm_tiles(c.kpm, c.kpm_bstride, c.B, c.Tkv, kTile, list, ntk + 1, s);
+            if (e != hipSuccess) return hip_fail(e, "key-padding tile list launch");
+            p.kpm_list = list;
+            p.kpm_list_stride = ntk + 1;
+        }
+    }
+    const bool timed = g_prof.on && g_prof.n < g_prof.cap;
+    if (timed && (e = hipEventRecord(g_prof.ev[2 * g_prof.n], s)) != hipSuccess) return hip_fail(e, "event record");
+    e = c.dtype == ATTN_BF16 ? launch_fwd_bf16(p, c.d, s) : launch_fwd_f32(p, c.d, s);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    if (timed) {
+        if ((e = hipEventRecord(g_prof.ev[2 * g_prof.n + 1], s)) != hipSuccess) return hip_fail(e, "event record");
+        ++g_prof.n;
+    }
+    return ATTN_OK;
+}
+
+int check_sizes(int B, int H, int Tq, int Tkv, int d) {
+    if (B < 0 || H < 0 || Tq < 0 || Tkv < 0) return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d H=%d Tq=%d Tkv=%d)", B, H, Tq, Tkv);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", d);
+    const long long rs = (long long)H * d;
+    if (rs > (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "H*d=%lld too large", rs);
+    if ((long long)B * H * (long long)((Tq + 127) / 128) >= (1LL << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+int attn_version(void) { return 100; }
+
+int attn_profile_start(int max_launches) {
+    g_err.clear();
+    if (g_prof.on) return fail(ATTN_ERR_INVALID_ARG, "profiling already started");
+    if (max_launches <= 0 || max_launches > (1 << 20)) return fail(ATTN_ERR_INVALID_ARG, "max_launches out of range");
+    g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+    for (auto& ev : g_prof.ev) {
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) {
+            for (auto& x : g_prof.ev)
+                if (x) (void)hipEventDestroy(x);
+            g_prof.ev.clear();
+            return hip_fail(e, "event create");
+        }
+    }
+    g_prof.cap = max_launches;
+    g_prof.n = 0;
+    g_prof.on = true;
+    return ATTN_OK;
+}
+
+int attn_profile_stop(float* ms, int cap) {
+    g_err.clear();
+    if (!g_prof.on) return -fail(ATTN_ERR_INVALID_ARG, "profiling not started");
+    int rc = g_prof.n;
+    for (int i = 0; i < g_prof.n && rc >= 0; ++i) {
+        hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+        float t = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+        if (e != hipSuccess) rc = -hip_fail(e, "event timing");
+        else if (ms && i < cap) ms[i] = t;
+    }
+    for (auto& x : g_prof.ev) (void)hipEventDestroy(x);
+    g_prof = Profile{};
+    return rc;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Tq, int Tkv, int d,
+             long long q_off, long long kv_off, int causal, const uint8_t* kpm, const uint8_t* attn_mask,
+             double rope_base, int dtype, unsigned flags, attn_stream_t stream) {
+    g_err.clear();
+    if (int rc = check_sizes(B, H, Tq, Tkv, d)) return rc;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (flags & ~(unsigned)(ATTN_ACCUMULATE | ATTN_OUT_F32 | ATTN_NO_TILE_SKIP))
+        return fail(ATTN_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+    if ((flags & ATTN_ACCUMULATE) && dtype == ATTN_BF16 && !(flags & ATTN_OUT_F32))
+        return fail(ATTN_ERR_INVALID_ARG, "ATTN_ACCUMULATE needs a float32 out (ATTN_OUT_F32)");
+    if ((flags & ATTN_ACCUMULATE) && !lse) return fail(ATTN_ERR_INVALID_ARG, "ATTN_ACCUMULATE needs lse");
+    if (!(rope_base >= 0.0) || std::isinf(rope_base)) return fail(ATTN_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
+    if (B == 0 || H == 0 || Tq == 0) return ATTN_OK;
+    if (!q || !out) return fail(ATTN_ERR_INVALID_ARG, "q and out must not be NULL");
+    if (Tkv > 0 && (!k || !v)) return fail(ATTN_ERR_INVALID_ARG, "k and v must not be NULL");
+    if (!aligned16(q) || !aligned16(out) || (Tkv > 0 && (!aligned16(k) || !aligned16(v))))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    if (std::llabs(q_off) > (1LL << 52) || std::llabs(kv_off) > (1LL << 52))
+        return fail(ATTN_ERR_INVALID_ARG, "positions out of range");
+
+    Call c = plain_call(q, k, v, out, lse, B, H, Tq, Tkv, d, q_off, kv_off, causal, kpm, attn_mask, dtype, flags);
+    hipStream_t s = (hipStream_t)stream;
+    const bool rope = rope_base > 0.0 && Tkv > 0;
+    const size_t tab_q = rope ? align_up((size_t)Tq * (d / 2) * sizeof(float2)) : 0;
+    const size_t tab_k = rope ? align_up((size_t)Tkv * (d / 2) * sizeof(float2)) : 0;
+    const size_t lst = kpm_list_bytes(c);
+    Scratch ws;
+    hipError_t e = ws.alloc(tab_q + tab_k + lst, s);
+    if (e != hipSuccess) return hip_fail(e, "scratch allocation");
+    char* wp = (char*)ws.ptr;
+    if (rope) {
+        const double lb = std::log(rope_base);
+        c.rope_q = (const float2*)wp;
+        c.rope_k = (const float2*)(wp + tab_q);
+        e = launch_rope_table((float2*)wp, q_off, Tq, d, lb, s);
+        if (e == hipSuccess) e = launch_rope_table((float2*)(wp + tab_q), kv_off, Tkv, d, lb, s);
+        if (e != hipSuccess) return hip_fail(e, "rotary table launch");
+    }
+    return enqueue(c, lst ? (int*)(wp + tab_q + tab_k) : nullptr, s);
+}
+
+int attn_merge(float* out_a, float* lse_a, const void* out_b, const float* lse_b, int B, int H, int Tq, int d,
+               int b_dtype, attn_stream_t stream) {
+    g_err.clear();
+    if (B < 0 || H < 0 || Tq < 0) return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (d <= 0 || d % 4) return fail(ATTN_ERR_UNSUPPORTED, "d=%d must be a positive multiple of 4", d);
+    if (b_dtype != ATTN_F32 && b_dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", b_dtype);
+    if ((long long)B * Tq * H == 0) return ATTN_OK;
+    if (!out_a || !lse_a || !out_b || !lse_b) return fail(ATTN_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(out_a) || (b_dtype == ATTN_F32 ? !aligned16(out_b) : ((uintptr_t)out_b & 7)))
+        return fail(ATTN_ERR_INVALID_ARG, "out_a must be 16-byte aligned (out_b 16 for float32, 8 for bf16)");
+    hipError_t e = launch_merge(out_a, lse_a, out_b, lse_b, B, H, Tq, d, (long long)Tq * H * d, H * d,
+                                (long long)H * Tq, Tq, b_dtype == ATTN_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "merge launch");
+}
+
+int rope_apply(void* x, const long long* pos, double base, int B, int T, int H, int d, int dtype, attn_stream_t stream) {
+    g_err.clear();
+    if (B < 0 || T < 0 || H < 0) return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (d <= 0 || d % 2 || d > 256) return fail(ATTN_ERR_UNSUPPORTED, "d=%d must be even and <= 256", d);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (!(base > 0.0) || std::isinf(base)) return fail(ATTN_ERR_INVALID_ARG, "base must be finite and > 0");
+    if ((long long)B * T * H == 0) return ATTN_OK;
+    if (T > 65535 * 1024LL || B > 65535) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+    if (!x || !pos) return fail(ATTN_ERR_INVALID_ARG, "NULL pointer");
+    if ((uintptr_t)x & (dtype == ATTN_BF16 ? 3u : 7u)) return fail(ATTN_ERR_INVALID_ARG, "x misaligned");
+    hipError_t e = launch_rope_apply(x, pos, std::log(base), B, T, H, d, dtype == ATTN_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "rope launch");
+}
+
+int attn_cast(const float* src, void* dst, long long n, int dst_dtype, attn_stream_t stream) {
+    g_err.clear();
+    if (n < 0) return fail(ATTN_ERR_INVALID_ARG, "n must be >= 0");
+    if (dst_dtype != ATTN_F32 && dst_dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dst_dtype);
+    if (n == 0) return ATTN_OK;
+    if (!src || !dst) return fail(ATTN_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(src) || ((uintptr_t)dst & 7)) return fail(ATTN_ERR_INVALID_ARG, "src must be 16-byte and dst 8-byte aligned");
+    hipError_t e = launch_cast(src, dst, n, dst_dtype == ATTN_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "cast launch");
+}
+
+int attn_ring_plan(int T, int P, int rank, int zigzag, int causal, attn_ring_call* plan, int cap) {
+    g_err.clear();
+    if (P <= 0 || rank < 0 || rank >= P || T <= 0) return -fail(ATTN_ERR_INVALID_ARG, "need T > 0, P > 0, 0 <= rank < P");
+    const int parts = zigzag ? 2 * P : P;
+    if (T % parts) return -fail(ATTN_ERR_INVALID_ARG, "T=%d is not divisible by %d", T, parts);
+    if (cap < 0 || (cap > 0 && !plan)) return -fail(ATTN_ERR_INVALID_ARG, "bad plan buffer");
+    const int c = T / parts;
+    // local query chunks: (chunk index, first local row)
+    int qchunk[2] = {rank, 2 * P - 1 - rank};
+    const int nq = zigzag ? 2 : 1;
+    bool touched[2] = {false, false};
+    int n = 0;
+    for (int step = 0; step < P; ++step) {
+        const int blk = ((rank - step) % P + P) % P;
+        int kchunk[2] = {blk, 2 * P - 1 - blk};
+        const int nk = zigzag ? 2 : 1;
+        for (int qh = 0; qh < nq; ++qh) {
+            for (int kh = 0; kh < nk; ++kh) {
+                const int qc = qchunk[qh], kc = kchunk[kh];
+                if (causal && kc > qc) continue;   // every key after every query
+                if (n < cap) {
+                    attn_ring_call& e = plan[n];
+                    e.step = step;
+                    e.block = blk;
+                    e.q_row0 = qh * c;
+                    e.q_rows = c;
+                    e.q_pos0 = (long long)qc * c;
+                    e.kv_pos0 = (long long)kc * c;
+                    e.kv_rows = c;
+                    e.accumulate = touched[qh] ? 1 : 0;
+                }
+                touched[qh] = true;
+                ++n;
+            }
+        }
+    }
+    return n;
+}
+
+int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse, float* acc, int B, int H, int T,
+                  int d, int P, int rank, int zigzag, int causal, const uint8_t* kpm, double rope_base, int dtype,
+                  unsigned flags, attn_stream_t stream) {
+    g_err.clear();
+    const int n = attn_ring_plan(T, P, rank, zigzag, causal, nullptr, 0);
+    if (n < 0) return -n;
+    const int Tl = T / P;
+    if (int rc = check_sizes(B, H, Tl, T, d)) return rc;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (flags & ~(unsigned)ATTN_NO_TILE_SKIP) return fail(ATTN_ERR_INVALID_ARG, "only ATTN_NO_TILE_SKIP may be passed");
+    if (!(rope_base >= 0.0) || std::isinf(rope_base)) return fail(ATTN_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
+    if (B == 0 || H == 0) return ATTN_OK;
+    if (!q || !k || !v || !out || !lse || !acc) return fail(ATTN_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(acc) || ((uintptr_t)out & 7))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v, acc must be 16-byte aligned, out 8-byte");
+    std::vector<attn_ring_call> plan(n);
+    attn_ring_plan(T, P, rank, zigzag, causal, plan.data(), n);
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool rope = rope_base > 0.0;
+    const size_t tab_q = rope ? align_up((size_t)Tl * (d / 2) * sizeof(float2)) : 0;
+    const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(float2)) : 0;
+    std::vector<size_t> lst_off(n, 0);
+    size_t total = tab_q + tab_k;
+    std::vector<Call> calls(n);
+    const int rs = H * d;
+    const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
+    for (int i = 0; i < n; ++i) {
+        const attn_ring_call& e = plan[i];
+        Call c{};
+        c.q = (const char*)q + (size_t)e.q_row0 * rs * esz;
+        c.k = (const char*)k + (size_t)e.kv_pos0 * rs * esz;
+        c.v = (const char*)v + (size_t)e.kv_pos0 * rs * esz;
+        c.out = acc + (size_t)e.q_row0 * rs;
+        c.lse = lse + e.q_row0;
+        c.B = B; c.H = H; c.Tq = e.q_rows; c.Tkv = e.kv_rows; c.d = d;
+        c.q_off = e.q_pos0; c.kv_off = e.kv_pos0; c.causal = causal;
+        c.kpm = kpm ? kpm + e.kv_pos0 : nullptr;
+        c.amask = nullptr;
+        c.dtype = dtype;
+        c.flags = (flags & ATTN_NO_TILE_SKIP) | ATTN_OUT_F32 | (e.accumulate ? ATTN_ACCUMULATE : 0u);
+        c.q_bstride = (long long)Tl * rs;
+        c.kv_bstride = (long long)T * rs;
+        c.o_bstride = (long long)Tl * rs;
+        c.kpm_bstride = T;
+        c.lse_bstride = (long long)H * Tl;
+        c.lse_hstride = Tl;
+        c.amask_stride = 0;
+        calls[i] = c;
+        lst_off[i] = total;
+        total += kpm_list_bytes(c);
+    }
+    Scratch ws;
+    hipError_t err = ws.alloc(total, s);
+    if (err != hipSuccess) return hip_fail(err, "scratch allocation");
+    char* wp = (char*)ws.ptr;
+    if (rope) {
+        const double lb = std::log(rope_base);
+        // local rows: contiguous chunk(s) at their absolute positions
+        const int parts = zigzag ? 2 : 1;
+        const int c = Tl / parts;
+        for (int ph = 0; ph < parts && err == hipSuccess; ++ph) {
+            const long long pos0 = (long long)(ph == 0 ? rank : 2 * P - 1 - rank) * c;
+            err = launch_rope_table((float2*)wp + (size_t)ph * c * (d / 2), pos0, c, d, lb, s);
+        }
+        if (err == hipSuccess) err = launch_rope_table((float2*)(wp + tab_q), 0, T, d, lb, s);
+        if (err != hipSuccess) return hip_fail(err, "rotary table launch");
+    }
+    bool covered[2] = {false, false};
+    for (int i = 0; i < n; ++i) {
+        Call& c = calls[i];
+        if (rope) {
+            c.rope_q = (const float2*)wp + (size_t)plan[i].q_row0 * (d / 2);
+            c.rope_k = (const float2*)(wp + tab_q) + (size_t)plan[i].kv_pos0 * (d / 2);
+        }
+        const size_t lb = kpm_list_bytes(c);
+        if (int rc = enqueue(c, lb ? (int*)(wp + lst_off[i]) : nullptr, s)) return rc;
+        covered[plan[i].q_row0 == 0 ? 0 : 1] = true;
+    }
+    // rows no sub-call reached (not possible with a causal diagonal, kept for safety)
+    const int parts = zigzag ? 2 : 1;
+    for (int ph = 0; ph < parts; ++ph) {
+        if (covered[ph]) continue;
+        const int c = Tl / parts;
+        err = launch_fill_empty(acc + (size_t)ph * c * rs, 0, lse + (size_t)ph * c, B, H, c, d, (long long)Tl * rs, rs,
+                                (long long)H * Tl, Tl, s);
+        if (err != hipSuccess) return hip_fail(err, "fill launch");
+    }
+    const long long nel = (long long)B * Tl * rs;
+    if (dtype == ATTN_F32 && (void*)acc == out) return ATTN_OK;
+    err = launch_cast(acc, out, nel, dtype == ATTN_BF16, s);
+    return err == hipSuccess ? ATTN_OK : hip_fail(err, "cast launch");
+}
+
+}  // extern "C"

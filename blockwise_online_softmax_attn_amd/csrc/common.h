@@ -1,0 +1,130 @@
+// Internal declarations shared by the HIP translation units of libattn.
+// Device helpers here are the only definitions of the element arithmetic
+// that more than one kernel needs (bf16 rounding, the rotary pair rotation,
+// the partial-result merge weights), so that fused and standalone paths give
+// bit-identical results.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+
+namespace bosa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two float32 -> packed bf16 pair, round-to-nearest-even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------- RoPE
+// Angle of pair t at position pos: pos * base^(-2t/d), evaluated in float64 and
+// returned as float32 cos/sin.  Position magnitudes up to 2^20 lose nothing
+// here (the product is exact to ~1e-10 rad), unlike a float32 angle.
+__device__ __forceinline__ float2 rope_cos_sin(long long pos, int t, int d, double log_base) {
+    double theta = exp(-(2.0 * (double)t / (double)d) * log_base);
+    double a = (double)pos * theta;
+    double s, c;
+    sincos(a, &s, &c);
+    return make_float2((float)c, (float)s);
+}
+
+// Rotate one coordinate pair (x0, x1) by (c, s) in float32:
+// (x0 c - x1 s, x0 s + x1 c), with fixed fused-multiply-add placement.
+__device__ __forceinline__ float2 rot_pair(float x0, float x1, float c, float s) {
+    return make_float2(fmaf(x0, c, -(x1 * s)), fmaf(x0, s, x1 * c));
+}
+__device__ __forceinline__ uint32_t rot_pair_bf16(uint32_t u, float c, float s) {
+    float2 y = rot_pair(bf16_lo(u), bf16_hi(u), c, s);
+    return pack_bf16x2(y.x, y.y);
+}
+// 8 bf16 values (4 pairs) with their table entries (c0,s0,c1,s1), (c2,s2,c3,s3).
+__device__ __forceinline__ uint4 rope8_bf16(uint4 x, float4 a, float4 b) {
+    return make_uint4(rot_pair_bf16(x.x, a.x, a.y), rot_pair_bf16(x.y, a.z, a.w),
+                      rot_pair_bf16(x.z, b.x, b.y), rot_pair_bf16(x.w, b.z, b.w));
+}
+
+// ---------------------------------------------------------------- merge
+// Weights of two partial results with log-sum-exp la, lb over disjoint key
+// sets: lse = logaddexp(la, lb), wa = e^(la-lse), wb = e^(lb-lse).  Symmetric
+// in (a, b); (.., -inf) is the identity; two empty partials give (-inf, 0, 0).
+__device__ __forceinline__ void merge_weights(float la, float lb, float& lse, float& wa, float& wb) {
+    float mx = fmaxf(la, lb);
+    if (mx == -INFINITY) { lse = -INFINITY; wa = 0.f; wb = 0.f; return; }
+    float ea = expf(la - mx), eb = expf(lb - mx);
+    lse = mx + logf(ea + eb);
+    wa = expf(la - lse);
+    wb = expf(lb - lse);
+}
+// wa*oa + wb*ob with two roundings of the products and one of the sum; the
+// pragma forbids fusing a product into the sum (an FMA would make the result
+// depend on operand order), so swapping (a, b) gives the same bits.
+__device__ __forceinline__ float merge_value(float wa, float oa, float wb, float ob) {
+#pragma clang fp contract(off)
+    const float x = wa * oa;
+    const float y = wb * ob;
+    return x + y;
+}
+
+// ---------------------------------------------------------------- params
+// One attention forward launch.  Strides are in elements.
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    const uint8_t* kpm;        // row b at kpm + b * kpm_bstride, indexed by local key
+    const uint8_t* amask;      // [Tq][amask_stride]
+    const float2* rope_q;      // [Tq][d/2] (cos, sin) or null
+    const float2* rope_k;      // [Tkv][d/2] or null
+    const int* kpm_list;       // per batch: [count, entries...] of live key tiles, or null
+    long long q_bstride, kv_bstride, o_bstride, kpm_bstride, lse_bstride;
+    int row_stride;            // H * d
+    int lse_hstride;
+    int amask_stride;
+    int kpm_list_stride;
+    int B, H, Tq, Tkv;
+    long long q_off, kv_off;
+    int causal;
+    unsigned flags;
+    float scale_log2;          // log2(e) / sqrt(d)
+    int n_qtiles;
+};
+
+// Entry of a live-tile list: tile index, top bit set when no key of the tile is masked.
+constexpr uint32_t kTileClean = 0x80000000u;
+
+// Kernel launchers (each returns hipSuccess or the launch error).
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s);
+hipError_t launch_rope_table(float2* tab, long long pos0, int n, int d, double log_base, hipStream_t s);
+hipError_t launch_kpm_tiles(const uint8_t* kpm, long long kpm_bstride, int B, int Tkv, int tile,
+                            int* list, int list_stride, hipStream_t s);
+hipError_t launch_merge(float* oa, float* la, const void* ob, const float* lb, int B, int H, int Tq, int d,
+                        long long o_bstride, int row_stride, long long lse_bstride, int lse_hstride,
+                        int b_is_bf16, hipStream_t s);
+hipError_t launch_cast(const float* src, void* dst, long long n, int to_bf16, hipStream_t s);
+hipError_t launch_rope_apply(void* x, const long long* pos, double log_base, int B, int T, int H, int d,
+                             int is_bf16, hipStream_t s);
+hipError_t launch_fill_empty(void* out, int out_bf16, float* lse, int B, int H, int rows, int d, long long o_bstride,
+                             int row_stride, long long lse_bstride, int lse_hstride, hipStream_t s);
+
+}  // namespace bosa

@@ -1,0 +1,241 @@
+// Bandwidth-bound helpers of the attention path: the rotary cos/sin table,
+// the live key-tile list of a key-padding mask, the partial-result merge, the
+// float32 -> output dtype cast, the standalone rotary embedding and the
+// empty-row fill.  All are coalesced along the contiguous (H, d) axes.
+#include "common.h"
+
+namespace bosa {
+namespace {
+
+inline unsigned grid_for(long long n, int block) { return (unsigned)((n + block - 1) / block); }
+
+// tab[i][t] = (cos, sin) of (pos0 + i) * base^(-2t/d), i < n, t < d/2.
+__global__ void rope_table_kernel(float2* __restrict__ tab, long long pos0, int n, int d, double log_base) {
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int half = d / 2;
+    if (idx >= (long long)n * half) return;
+    const int i = (int)(idx / half), t = (int)(idx % half);
+    tab[idx] = rope_cos_sin(pos0 + i, t, d, log_base);
+}
+
+// Classification of a key tile under the key-padding mask.
+__device__ __forceinline__ void classify(const uint8_t* row, int k0, int k1, bool& any_ok, bool& all_ok) {
+    any_ok = false;
+    all_ok = true;
+    for (int k = k0; k < k1; ++k) {
+        const bool ok = row[k] == 0;
+        any_ok |= ok;
+        all_ok &= ok;
+    }
+}
+
+// One workgroup per batch row: list[0] = number of tiles with at least one
+// allowed key, followed by those tile indices in increasing order (top bit set
+// when every key of the tile is allowed).  Fully masked tiles are skipped by
+// the attention kernel without being read.
+__global__ __launch_bounds__(256) void kpm_tiles_kernel(const uint8_t* __restrict__ kpm, long long bstride, int Tkv,
+                                                        int tile, int* __restrict__ list, int list_stride) {
+    __shared__ int counts[256];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const uint8_t* row = kpm + b * bstride;
+    int* out = list + (long long)b * list_stride;
+    const int ntk = (Tkv + tile - 1) / tile;
+    const int per = (ntk + 255) / 256;
+    const int t0 = min(tid * per, ntk), t1 = min(t0 + per, ntk);
+    int cnt = 0;
+    for (int t = t0; t < t1; ++t) {
+        bool any_ok, all_ok;
+        classify(row, t * tile, min((t + 1) * tile, Tkv), any_ok, all_ok);
+        cnt += any_ok ? 1 : 0;
+    }
+    counts[tid] = cnt;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int c = counts[i];
+            counts[i] = run;
+            run += c;
+        }
+        out[0] = run;
+    }
+    __syncthreads();
+    int pos = counts[tid];
+    for (int t = t0; t < t1; ++t) {
+        bool any_ok, all_ok;
+        classify(row, t * tile, min((t + 1) * tile, Tkv), any_ok, all_ok);
+        if (any_ok) out[1 + pos++] = (int)((uint32_t)t | (all_ok ? kTileClean : 0u));
+    }
+}
+
+// (out_a, lse_a) <- merge((out_a, lse_a), (out_b, lse_b)).  Each 32-lane half of
+// a wave owns one (b, t, h) row, so the row's lse is read by every lane before
+// lane 0 of the half writes the merged value.
+template <bool B_BF16>
+__global__ __launch_bounds__(256) void merge_kernel(float* __restrict__ oa, float* __restrict__ la,
+                                                    const void* __restrict__ ob_, const float* __restrict__ lb,
+                                                    int B, int H, int Tq, int d, long long o_bstride, int row_stride,
+                                                    long long lse_bstride, int lse_hstride) {
+    const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long rowid = gtid >> 5;
+    const int sub = (int)(gtid & 31);
+    if (rowid >= (long long)B * Tq * H) return;
+    const int h = (int)(rowid % H);
+    const long long bt = rowid / H;
+    const int t = (int)(bt % Tq);
+    const int b = (int)(bt / Tq);
+    const long long lidx = b * lse_bstride + (long long)h * lse_hstride + t;
+    const long long oidx = b * o_bstride + (long long)t * row_stride + (long long)h * d;
+    float lse, wa, wb;
+    merge_weights(la[lidx], lb[lidx], lse, wa, wb);
+    for (int c = 4 * sub; c < d; c += 128) {
+        float4* pa = (float4*)(oa + oidx + c);
+        const float4 a = *pa;
+        float4 bv;
+        if (B_BF16) {
+            const uint2 u = *(const uint2*)((const uint16_t*)ob_ + oidx + c);
+            bv = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+        } else {
+            bv = *(const float4*)((const float*)ob_ + oidx + c);
+        }
+        float4 r;
+        r.x = merge_value(wa, a.x, wb, bv.x);
+        r.y = merge_value(wa, a.y, wb, bv.y);
+        r.z = merge_value(wa, a.z, wb, bv.z);
+        r.w = merge_value(wa, a.w, wb, bv.w);
+        *pa = r;
+    }
+    if (sub == 0) la[lidx] = lse;
+}
+
+__global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst,
+                                                        long long n) {
+    const long long i4 = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i4 + 4 <= n) {
+        const float4 x = *(const float4*)(src + i4);
+        uint2 r;
+        r.x = pack_bf16x2(x.x, x.y);
+        r.y = pack_bf16x2(x.z, x.w);
+        *(uint2*)(dst + i4) = r;
+    } else {
+        for (long long i = i4; i < n; ++i) dst[i] = (uint16_t)pack_bf16x2(src[i], 0.f);
+    }
+}
+
+__global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                       long long n) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src[i];
+}
+
+// Rotary embedding of one token (all heads of one batch item) per workgroup:
+// the token's d/2 cos/sin pairs are computed once in LDS.
+template <bool BF16>
+__global__ __launch_bounds__(256) void rope_apply_kernel(void* __restrict__ x, const long long* __restrict__ pos,
+                                                         int T, int H, int d, double log_base) {
+    __shared__ float2 cs[128];
+    const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int half = d / 2;
+    const long long ps = pos[i];
+    for (int t = tid; t < half; t += blockDim.x) cs[t] = rope_cos_sin(ps, t, d, log_base);
+    __syncthreads();
+    const long long base = ((long long)b * T + i) * (long long)H * d;
+    const int npairs = H * half;
+    for (int pi = tid; pi < npairs; pi += blockDim.x) {
+        const float2 c = cs[pi % half];
+        if (BF16) {
+            uint32_t* pp = (uint32_t*)((uint16_t*)x + base) + pi;
+            *pp = rot_pair_bf16(*pp, c.x, c.y);
+        } else {
+            float2* pp = (float2*)((float*)x + base) + pi;
+            const float2 v = *pp;
+            *pp = rot_pair(v.x, v.y, c.x, c.y);
+        }
+    }
+}
+
+// Rows [0, rows) become the merge identity: out = 0 (float32 or bf16), lse = -inf.
+template <bool BF16>
+__global__ __launch_bounds__(256) void fill_empty_kernel(void* __restrict__ out, float* __restrict__ lse, int B, int H,
+                                                         int rows, int d, long long o_bstride, int row_stride,
+                                                         long long lse_bstride, int lse_hstride) {
+    const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long total = (long long)B * rows * H * d;
+    if (gtid >= total) return;
+    const int c = (int)(gtid % d);
+    long long r = gtid / d;
+    const int h = (int)(r % H);
+    r /= H;
+    const int t = (int)(r % rows);
+    const int b = (int)(r / rows);
+    if (out) {
+        const long long oi = b * o_bstride + (long long)t * row_stride + (long long)h * d + c;
+        if (BF16) ((uint16_t*)out)[oi] = 0;
+        else ((float*)out)[oi] = 0.f;
+    }
+    if (lse && c == 0) lse[b * lse_bstride + (long long)h * lse_hstride + t] = -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(float2* tab, long long pos0, int n, int d, double log_base, hipStream_t s) {
+    const long long total = (long long)n * (d / 2);
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, tab, pos0, n, d, log_base);
+    return hipGetLastError();
+}
+
+hipError_t launch_kpm_tiles(const uint8_t* kpm, long long kpm_bstride, int B, int Tkv, int tile, int* list,
+                            int list_stride, hipStream_t s) {
+    hipLaunchKernelGGL(kpm_tiles_kernel, dim3(B), dim3(256), 0, s, kpm, kpm_bstride, Tkv, tile, list, list_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(float* oa, float* la, const void* ob, const float* lb, int B, int H, int Tq, int d,
+                        long long o_bstride, int row_stride, long long lse_bstride, int lse_hstride, int b_is_bf16,
+                        hipStream_t s) {
+    const long long threads = (long long)B * Tq * H * 32;
+    if (threads == 0) return hipSuccess;
+    if (b_is_bf16)
+        hipLaunchKernelGGL(merge_kernel<true>, dim3(grid_for(threads, 256)), dim3(256), 0, s, oa, la, ob, lb, B, H,
+                           Tq, d, o_bstride, row_stride, lse_bstride, lse_hstride);
+    else
+        hipLaunchKernelGGL(merge_kernel<false>, dim3(grid_for(threads, 256)), dim3(256), 0, s, oa, la, ob, lb, B, H,
+                           Tq, d, o_bstride, row_stride, lse_bstride, lse_hstride);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast(const float* src, void* dst, long long n, int to_bf16, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    if (to_bf16)
+        hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for((n + 3) / 4, 256)), dim3(256), 0, s, src,
+                           (uint16_t*)dst, n);
+    else
+        hipLaunchKernelGGL(copy_f32_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, src, (float*)dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_apply(void* x, const long long* pos, double log_base, int B, int T, int H, int d, int is_bf16,
+                             hipStream_t s) {
+    if ((long long)B * T == 0) return hipSuccess;
+    if (is_bf16)
+        hipLaunchKernelGGL(rope_apply_kernel<true>, dim3(T, B), dim3(256), 0, s, x, pos, T, H, d, log_base);
+    else
+        hipLaunchKernelGGL(rope_apply_kernel<false>, dim3(T, B), dim3(256), 0, s, x, pos, T, H, d, log_base);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_empty(void* out, int out_bf16, float* lse, int B, int H, int rows, int d, long long o_bstride,
+                             int row_stride, long long lse_bstride, int lse_hstride, hipStream_t s) {
+    const long long total = (long long)B * rows * H * d;
+    if (total == 0) return hipSuccess;
+    if (out_bf16)
+        hipLaunchKernelGGL(fill_empty_kernel<true>, dim3(grid_for(total, 256)), dim3(256), 0, s, out, lse, B, H, rows,
+                           d, o_bstride, row_stride, lse_bstride, lse_hstride);
+    else
+        hipLaunchKernelGGL(fill_empty_kernel<false>, dim3(grid_for(total, 256)), dim3(256), 0, s, out, lse, B, H, rows,
+                           d, o_bstride, row_stride, lse_bstride, lse_hstride);
+    return hipGetLastError();
+}
+
+}  // namespace bosa

@@ -1,0 +1,189 @@
+// Blockwise online-softmax attention forward, float32 inputs.
+//
+// True float32 products and accumulation (no bf16 or reduced-precision
+// operand rounding).  One wave of 64 lanes owns 32 query rows; the two lanes
+// of a pair (2i, 2i+1) share row i, each holding half of the (rotated) query
+// and of the output accumulator in registers, and add their partial dot
+// products with one lane exchange.  Key/value tiles of 32 rows are staged in
+// LDS and read by every pair at once (LDS broadcast); scores are folded into
+// the running max / denominator / weighted sum 8 keys at a time, the
+// safe-softmax accumulator rescale of the brunomaga.github.io
+// sequence-context-parallelism post ("Improving numerical stability").
+#include "common.h"
+
+namespace bosa {
+namespace {
+
+constexpr int BMF = 32;  // query rows per workgroup (one wave, two lanes per row)
+constexpr int BNF = 32;  // keys per LDS tile
+constexpr int SUB = 8;   // keys per online-softmax update
+
+template <int D>
+__global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(const FwdParams p) {
+    constexpr int HD = D / 2;
+    __shared__ float4 sK[BNF * D / 4];
+    __shared__ float4 sV[BNF * D / 4];
+    const int lane = threadIdx.x;
+    const int half = lane & 1;
+
+    int bid = blockIdx.x;
+    const int qt = p.n_qtiles - 1 - bid % p.n_qtiles;
+    bid /= p.n_qtiles;
+    const int h = bid % p.H;
+    const int b = bid / p.H;
+
+    const int rs = p.row_stride;
+    const float* qg = (const float*)p.q + b * p.q_bstride + (long long)h * D;
+    const float* kg = (const float*)p.k + b * p.kv_bstride + (long long)h * D;
+    const float* vg = (const float*)p.v + b * p.kv_bstride + (long long)h * D;
+    const bool noskip = (p.flags & ATTN_NO_TILE_SKIP) != 0;
+    const long long delta = p.q_off - p.kv_off;
+
+    const int q0 = qt * BMF;
+    const int qi = q0 + (lane >> 1);
+    const bool qvalid = qi < p.Tq;
+    const int c0 = half * HD;   // first dim this lane holds
+
+    float q[HD];
+    float o[HD];
+#pragma unroll
+    for (int c = 0; c < HD; c += 4) {
+        float4 x = qvalid ? *(const float4*)(qg + (long long)qi * rs + c0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (qvalid && p.rope_q) {
+            const float4 cs = *(const float4*)(p.rope_q + (long long)qi * (D / 2) + (c0 + c) / 2);
+            const float2 y0 = rot_pair(x.x, x.y, cs.x, cs.y);
+            const float2 y1 = rot_pair(x.z, x.w, cs.z, cs.w);
+            x = make_float4(y0.x, y0.y, y1.x, y1.y);
+        }
+        q[c] = x.x; q[c + 1] = x.y; q[c + 2] = x.z; q[c + 3] = x.w;
+        o[c] = o[c + 1] = o[c + 2] = o[c + 3] = 0.f;
+    }
+
+    const int qlast = min(q0 + BMF, p.Tq) - 1;
+    long long nk = p.Tkv;
+    if (p.causal && !noskip) {
+        long long lim = delta + qlast + 1;
+        nk = lim < 0 ? 0 : (lim < nk ? lim : nk);
+    }
+    const uint8_t* kpm_row = p.kpm ? p.kpm + b * p.kpm_bstride : nullptr;
+
+    float m_i = -INFINITY, l_i = 0.f;
+    for (int key0 = 0; key0 < nk; key0 += BNF) {
+        for (int idx = lane; idx < BNF * D / 4; idx += 64) {
+            const int row = idx / (D / 4), c4 = idx % (D / 4);
+            const int key = key0 + row;
+            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+            if (key < p.Tkv) {
+                kx = *(const float4*)(kg + (long long)key * rs + 4 * c4);
+                vx = *(const float4*)(vg + (long long)key * rs + 4 * c4);
+                if (p.rope_k) {
+                    const float4 cs = *(const float4*)(p.rope_k + (long long)key * (D / 2) + 2 * c4);
+                    const float2 y0 = rot_pair(kx.x, kx.y, cs.x, cs.y);
+                    const float2 y1 = rot_pair(kx.z, kx.w, cs.z, cs.w);
+                    kx = make_float4(y0.x, y0.y, y1.x, y1.y);
+                }
+            }
+            sK[idx] = kx;
+            sV[idx] = vx;
+        }
+        __syncthreads();
+
+        for (int j0 = 0; j0 < BNF; j0 += SUB) {
+            float s[SUB];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < SUB; ++j) {
+                const float4* kr = sK + (j0 + j) * (D / 4) + c0 / 4;
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < HD; c += 4) {
+                    const float4 kx = kr[c / 4];
+                    acc = fmaf(q[c], kx.x, acc);
+                    acc = fmaf(q[c + 1], kx.y, acc);
+                    acc = fmaf(q[c + 2], kx.z, acc);
+                    acc = fmaf(q[c + 3], kx.w, acc);
+                }
+                // lane pair: the lower half's partial is added first on both lanes
+                const float other = __shfl_xor(acc, 1);
+                acc = half ? (other + acc) : (acc + other);
+                const int key = key0 + j0 + j;
+                bool ok = key < p.Tkv;
+                if (ok && kpm_row) ok = kpm_row[key] == 0;
+                if (ok && p.causal) ok = (long long)key - qi <= delta;
+                if (ok && p.amask && qvalid) ok = p.amask[(long long)qi * p.amask_stride + key] == 0;
+                s[j] = ok ? acc : -INFINITY;
+                mx = fmaxf(mx, s[j]);
+            }
+            const float mnew = fmaxf(m_i, mx * p.scale_log2);
+            const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f(m_i - muse);
+            float rsum = 0.f;
+#pragma unroll
+            for (int j = 0; j < SUB; ++j) {
+                s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -muse));
+                rsum += s[j];
+            }
+            l_i = fmaf(l_i, alpha, rsum);
+            m_i = mnew;
+#pragma unroll
+            for (int c = 0; c < HD; ++c) o[c] *= alpha;
+#pragma unroll
+            for (int j = 0; j < SUB; ++j) {
+                const float4* vr = sV + (j0 + j) * (D / 4) + c0 / 4;
+#pragma unroll
+                for (int c = 0; c < HD; c += 4) {
+                    const float4 vx = vr[c / 4];
+                    o[c] = fmaf(s[j], vx.x, o[c]);
+                    o[c + 1] = fmaf(s[j], vx.y, o[c + 1]);
+                    o[c + 2] = fmaf(s[j], vx.z, o[c + 2]);
+                    o[c + 3] = fmaf(s[j], vx.w, o[c + 3]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if (!qvalid) return;
+    const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
+    const float lse_b = l_i > 0.f ? (m_i + log2f(l_i)) * kLn2 : -INFINITY;
+    float* lse_ptr = p.lse ? p.lse + b * p.lse_bstride + (long long)h * p.lse_hstride + qi : nullptr;
+    float* og = (float*)p.out + b * p.o_bstride + (long long)qi * rs + (long long)h * D + c0;
+    if (p.flags & ATTN_ACCUMULATE) {
+        const float la = *lse_ptr;   // both lanes of the pair read before the lower lane writes
+        float lse_n, wa, wb;
+        merge_weights(la, lse_b, lse_n, wa, wb);
+#pragma unroll
+        for (int c = 0; c < HD; c += 4) {
+            float4 oa = *(float4*)(og + c);
+            oa.x = merge_value(wa, oa.x, wb, o[c] * inv);
+            oa.y = merge_value(wa, oa.y, wb, o[c + 1] * inv);
+            oa.z = merge_value(wa, oa.z, wb, o[c + 2] * inv);
+            oa.w = merge_value(wa, oa.w, wb, o[c + 3] * inv);
+            *(float4*)(og + c) = oa;
+        }
+        if (!half) *lse_ptr = lse_n;
+        return;
+    }
+#pragma unroll
+    for (int c = 0; c < HD; c += 4)
+        *(float4*)(og + c) = make_float4(o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv);
+    if (lse_ptr && !half) *lse_ptr = lse_b;
+}
+
+template <int D>
+hipError_t launch(const FwdParams& p, hipStream_t s) {
+    FwdParams q = p;
+    q.n_qtiles = (p.Tq + BMF - 1) / BMF;
+    const long long grid = (long long)q.n_qtiles * p.H * p.B;
+    hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)grid), dim3(64), 0, s, q);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s) {
+    if (d == 128) return launch<128>(p, s);
+    return launch<64>(p, s);
+}
+
+}  // namespace bosa

@@ -1,0 +1,221 @@
+/*
+ * attn.h -- C ABI of the blockwise online-softmax attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Scaled dot-product attention forward,
+ *     out = softmax(Q K^T / sqrt(d) + mask) V,
+ * ("Transformers and Attention" digest, reference #22 Attention Is All You
+ * Need and #24 PyTorch scaled_dot_product_attention) one key/value tile at a
+ * time with online softmax: a running row max, a running denominator and a
+ * rescaled weighted sum per query row (brunomaga.github.io
+ * sequence-context-parallelism post, sections "Ring Attention" and "Improving
+ * numerical stability").  Partial results over disjoint key blocks are
+ * carried as (out, lse) and merged, which is the per-device work of Ring
+ * Attention ("CP: Split Long Contexts Across GPUs", section "Circulate K/V
+ * blocks with Ring").
+ *
+ * Conventions shared by every entry point.
+ *  - Layout: q and out are (B, Tq, H, d); k and v are (B, Tkv, H, d); all
+ *    contiguous, row-major, the layout the pages' ring code hands to its
+ *    attention kernel.  lse is (B, H, Tq) float32, natural log.
+ *  - Positions: query row i has absolute position q_off + i, key j has
+ *    kv_off + j.  They drive the causal test and the rotary embedding.
+ *  - Masks: nonzero = excluded.  kpm is (B, Tkv) uint8 (ignored source
+ *    entries per batch item), attn_mask is (Tq, Tkv) uint8 (forbidden
+ *    (query, key) pairs, shared over B and H).  Exclusions combine with each
+ *    other and with causal order ("Transformers and Attention" #2).
+ *  - A row with no allowed key yields out = 0 and lse = -inf, so that
+ *    (0, -inf) is the identity of attn_merge.
+ *  - Ownership: every pointer is caller-owned device memory (except where a
+ *    host pointer is stated).  The library keeps no device state between
+ *    calls; attn_fwd with a rotary embedding allocates a small stream-ordered
+ *    cos/sin table on `stream` and frees it on the same stream.
+ *  - Streams: every call only enqueues work on `stream` (NULL = the null
+ *    stream) and returns; there is no host synchronisation inside.
+ *  - Errors: arguments are validated on the host before any HIP call; a
+ *    failing call returns a nonzero attn_status, enqueues nothing, and
+ *    attn_last_error() describes the problem (thread-local string).  Launch
+ *    failures return ATTN_ERR_HIP.  Faults during execution surface at the
+ *    caller's next synchronisation.
+ */
+#ifndef BOSA_ATTN_H
+#define BOSA_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* attn_stream_t; /* the same type as hipStream_t */
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad flag combination */
+    ATTN_ERR_UNSUPPORTED = 2, /* head dim other than 64/128, unknown dtype */
+    ATTN_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+enum {
+    /* out/lse already hold a partial result (float32 out); merge this call's
+     * result into them in place instead of overwriting.  Requires OUT_F32. */
+    ATTN_ACCUMULATE = 1u,
+    /* out is float32 (a partial kept for merging) rather than the input dtype. */
+    ATTN_OUT_F32 = 2u,
+    /* debugging aid: visit every key tile, also the fully masked ones; the
+     * results are bit-identical to the default. */
+    ATTN_NO_TILE_SKIP = 4u
+};
+
+/*
+ * attn_fwd -- one attention forward call over one key/value block.
+ *
+ * Follows: "Transformers and Attention" #22/#24 (definition, 1/sqrt(d)
+ * scale, causal triangle with the diagonal), #2 (key-padding and attention
+ * masks, exclusions combined), #4 (rotary embedding of q and k);
+ * brunomaga.github.io post, "Improving numerical stability" (running max,
+ * rescale of both accumulators by exp of the max difference, LogSumExp) and
+ * "Implementation" (each ring step produces block_out and block_lse).
+ *
+ *  q, k, v    device, dtype `dtype`, layouts above.  k and v must not alias out.
+ *  out        device, (B, Tq, H, d): dtype `dtype`, or float32 with ATTN_OUT_F32.
+ *  lse        device float32 (B, H, Tq); may be NULL unless ATTN_ACCUMULATE.
+ *  B, H, Tq, Tkv  sizes >= 0 (B, H or Tq = 0: nothing to do; Tkv = 0: every
+ *             row is empty).  d: 64 or 128.
+ *  q_off, kv_off  absolute position of row 0 of q and of k/v.
+ *  causal     nonzero: key j is allowed for query i only if kv_off+j <= q_off+i.
+ *  kpm        device uint8 (B, Tkv) or NULL.  attn_mask: device uint8 (Tq, Tkv) or NULL.
+ *  rope_base  > 0: rotate adjacent coordinate pairs (2t, 2t+1) of q and k by
+ *             pos * rope_base^(-2t/d) (cos/sin accurate to float32 rounding),
+ *             in float32, and round the rotated values to `dtype` before the
+ *             dot product.  0: no rotary embedding.
+ *  dtype      ATTN_BF16 (bf16 MFMA, float32 accumulation and softmax) or
+ *             ATTN_F32 (float32 throughout).
+ *  flags      ATTN_ACCUMULATE | ATTN_OUT_F32 | ATTN_NO_TILE_SKIP.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int H, int Tq, int Tkv, int d,
+             long long q_off, long long kv_off, int causal,
+             const uint8_t* kpm, const uint8_t* attn_mask,
+             double rope_base, int dtype, unsigned flags, attn_stream_t stream);
+
+/*
+ * attn_merge -- (out_a, lse_a) <- (out_a, lse_a) (+) (out_b, lse_b), in place.
+ *
+ * The pages call an accumulate step after every ring step without defining
+ * it (brunomaga.github.io post, "Implementation"); this is the combination
+ * the fraction form and LogSumExp carry imply ("Ring Attention", "Improving
+ * numerical stability"): lse = logaddexp(lse_a, lse_b),
+ * out = e^(lse_a - lse) out_a + e^(lse_b - lse) out_b.  Never a plain sum or
+ * average ("CP: Split Long Contexts Across GPUs", "Circulate K/V blocks with
+ * Ring").  (0, -inf) is the identity; the operation is commutative bit for bit.
+ *
+ *  out_a      device float32 (B, Tq, H, d), read and written.
+ *  lse_a      device float32 (B, H, Tq), read and written.
+ *  out_b      device (B, Tq, H, d) of dtype b_dtype.  lse_b: device float32 (B, H, Tq).
+ *  d          any positive multiple of 4.
+ */
+int attn_merge(float* out_a, float* lse_a, const void* out_b, const float* lse_b,
+               int B, int H, int Tq, int d, int b_dtype, attn_stream_t stream);
+
+/*
+ * rope_apply -- rotary position embedding of x in place.
+ *
+ * "Transformers and Attention" #4 (RoFormer): an even-dimensional vector is
+ * split into coordinate pairs, each rotated by a positional angle, so that a
+ * rotated query and key interact through their position difference only.
+ * Pair (2t, 2t+1) of token i is rotated by pos[i] * base^(-2t/d):
+ * (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a), computed in float32
+ * from float64-accurate cos/sin and rounded to `dtype`.
+ *
+ *  x          device (B, T, H, d) of dtype `dtype`, rotated in place.
+ *  pos        device int64 [T]: absolute position of each token (shared over B and H).
+ *  base       > 0.  d: even, <= 256.
+ */
+int rope_apply(void* x, const long long* pos, double base, int B, int T, int H, int d,
+               int dtype, attn_stream_t stream);
+
+/*
+ * attn_cast -- dst[i] = (dst_dtype) src[i] for i < n, round-to-nearest-even.
+ * The last step of a ring share: the float32 accumulator becomes the
+ * output in the input dtype (brunomaga.github.io post, "Implementation":
+ * the accumulated output is cast to the dtype of q at the end).
+ */
+int attn_cast(const float* src, void* dst, long long n, int dst_dtype, attn_stream_t stream);
+
+/*
+ * Ring-attention share on one device.
+ *
+ * One rank of a P-rank ring keeps its query rows and meets every key/value
+ * block in ring order: its own block first, then the block of rank-1,
+ * rank-2, ... mod P ("CP: Split Long Contexts Across GPUs", "Circulate K/V
+ * blocks with Ring"; brunomaga.github.io post, "Distributed algorithm").
+ * Placement is contiguous (rank r owns tokens [r T/P, (r+1) T/P)) or zigzag
+ * (rank r owns chunks r and 2P-1-r of size T/(2P), "Balance the workload in
+ * causal attention").  Under zigzag, each (query chunk, key chunk) pair of a
+ * step is one attn_fwd sub-call; pairs that causal order masks completely
+ * are not issued.
+ *
+ * attn_ring_plan -- host-only bookkeeping (no HIP call).  Fills up to `cap`
+ * entries of `plan` (host memory) in issue order and returns the number of
+ * sub-calls, or a negative attn_status on bad arguments.
+ */
+typedef struct {
+    int step;          /* ring step 0..P-1 */
+    int block;         /* rank whose K/V block is used at this step */
+    int q_row0;        /* first local query row of the sub-call */
+    int q_rows;        /* number of local query rows */
+    long long q_pos0;  /* absolute position of local row q_row0 */
+    long long kv_pos0; /* absolute position (= row in the full K/V) of the first key */
+    int kv_rows;       /* number of keys */
+    int accumulate;    /* 1: merge into the partial already held for these rows */
+} attn_ring_call;
+
+int attn_ring_plan(int T, int P, int rank, int zigzag, int causal, attn_ring_call* plan, int cap);
+
+/*
+ * attn_ring_fwd -- execute a rank's ring share.
+ *
+ *  q          device (B, Tq_local, H, d) local query rows, Tq_local = T/P,
+ *             in local order (zigzag: chunk r then chunk 2P-1-r).
+ *  k, v       device (B, T, H, d): every block, at its absolute position (one
+ *             device emulates the arriving blocks; nothing is copied).
+ *  out        device (B, Tq_local, H, d) of `dtype`: the final output.
+ *  lse        device float32 (B, H, Tq_local): the final log-sum-exp.
+ *  acc        device float32 (B, Tq_local, H, d) scratch for the running partial
+ *             (may equal out when dtype is ATTN_F32).
+ *  kpm        device uint8 (B, T) or NULL, over absolute key positions.
+ *  Other arguments as attn_fwd.  The work is the sub-calls of attn_ring_plan,
+ *  issued in order on `stream`, then one attn_cast of acc into out.
+ */
+int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse, float* acc,
+                  int B, int H, int T, int d, int P, int rank, int zigzag, int causal,
+                  const uint8_t* kpm, double rope_base, int dtype, unsigned flags,
+                  attn_stream_t stream);
+
+/*
+ * Kernel timing for measurement tools.  Between attn_profile_start and
+ * attn_profile_stop, every attention-kernel launch made by attn_fwd or
+ * attn_ring_fwd on the calling thread is bracketed by a pair of HIP events
+ * recorded on the launch's own stream (at most max_launches launches; later
+ * ones are not timed).  attn_profile_stop waits for those events, writes the
+ * duration of each timed launch in milliseconds to ms[0 .. min(n, cap)) (host
+ * memory; may be NULL) and returns n, the number of timed launches, or a
+ * negative attn_status.  The events are created by start and destroyed by stop.
+ */
+int attn_profile_start(int max_launches);
+int attn_profile_stop(float* ms, int cap);
+
+/* Thread-local description of the last failure ("" if none). */
+const char* attn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BOSA_ATTN_H */
