@@ -93,7 +93,7 @@ Call plain_call(const void* q, const void* k, const void* v, void* out, float* l
 size_t kpm_list_bytes(const Call& c) {
     if (!c.kpm || c.dtype != ATTN_BF16 || (c.flags & ATTN_NO_TILE_SKIP)) return 0;
     const long long ntk = (c.Tkv + kTile - 1) / kTile;
-    return align_up((size_t)c.B * (size_t)(ntk + 1) * sizeof(int));
+    return align_up((size_t)c.B * (size_t)(ntk + 2) * sizeof(int));
 }
 
 // Enqueue one validated call.  `list` is scratch of kpm_list_bytes(c) bytes.
@@ -121,10 +121,10 @@ int enqueue(const Call& c, int* list, hipStream_t s) {
     if (c.dtype == ATTN_BF16) {
         if (list) {
             const int ntk = (c.Tkv + kTile - 1) / kTile;
-            e = launch_kpm_tiles(c.kpm, c.kpm_bstride, c.B, c.Tkv, kTile, list, ntk + 1, s);
+            e = launch_kpm_tiles(c.kpm, c.kpm_bstride, c.B, c.Tkv, kTile, list, ntk + 2, s);
             if (e != hipSuccess) return hip_fail(e, "key-padding tile list launch");
             p.kpm_list = list;
-            p.kpm_list_stride = ntk + 1;
+            p.kpm_list_stride = ntk + 2;
         }
     }
     const bool timed = g_prof.on && g_prof.n < g_prof.cap;
@@ -143,7 +143,7 @@ int check_sizes(int B, int H, int Tq, int Tkv, int d) {
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", d);
     const long long rs = (long long)H * d;
     if (rs > (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "H*d=%lld too large", rs);
-    if ((long long)B * H * (long long)((Tq + 127) / 128) >= (1LL << 31))
+    if ((long long)B * H * (long long)((Tq + 31) / 32) >= (1LL << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
     return ATTN_OK;
 }

@@ -95,7 +95,7 @@ struct FwdParams {
     const uint8_t* amask;      // [Tq][amask_stride]
     const float2* rope_q;      // [Tq][d/2] (cos, sin) or null
     const float2* rope_k;      // [Tkv][d/2] or null
-    const int* kpm_list;       // per batch: [count, entries...] of live key tiles, or null
+    const int* kpm_list;       // per batch: [count, leading clean tiles, entries...] of live key tiles, or null
     long long q_bstride, kv_bstride, o_bstride, kpm_bstride, lse_bstride;
     int row_stride;            // H * d
     int lse_hstride;

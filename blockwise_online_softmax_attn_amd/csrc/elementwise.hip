@@ -30,25 +30,31 @@ __device__ __forceinline__ void classify(const uint8_t* row, int k0, int k1, boo
 }
 
 // One workgroup per batch row: list[0] = number of tiles with at least one
-// allowed key, followed by those tile indices in increasing order (top bit set
-// when every key of the tile is allowed).  Fully masked tiles are skipped by
-// the attention kernel without being read.
+// allowed key, list[1] = number of leading tiles with no masked key, followed
+// by the live tile indices in increasing order (top bit set when every key of
+// the tile is allowed).  Fully masked tiles are skipped by the attention
+// kernel without being read.
 __global__ __launch_bounds__(256) void kpm_tiles_kernel(const uint8_t* __restrict__ kpm, long long bstride, int Tkv,
                                                         int tile, int* __restrict__ list, int list_stride) {
     __shared__ int counts[256];
+    __shared__ int first_unclean;
     const int b = blockIdx.x, tid = threadIdx.x;
     const uint8_t* row = kpm + b * bstride;
     int* out = list + (long long)b * list_stride;
     const int ntk = (Tkv + tile - 1) / tile;
     const int per = (ntk + 255) / 256;
     const int t0 = min(tid * per, ntk), t1 = min(t0 + per, ntk);
-    int cnt = 0;
+    if (tid == 0) first_unclean = ntk;
+    __syncthreads();
+    int cnt = 0, unclean = ntk;
     for (int t = t0; t < t1; ++t) {
         bool any_ok, all_ok;
         classify(row, t * tile, min((t + 1) * tile, Tkv), any_ok, all_ok);
         cnt += any_ok ? 1 : 0;
+        if (!all_ok && unclean == ntk) unclean = t;
     }
     counts[tid] = cnt;
+    if (unclean < ntk) atomicMin(&first_unclean, unclean);
     __syncthreads();
     if (tid == 0) {
         int run = 0;
@@ -58,13 +64,14 @@ __global__ __launch_bounds__(256) void kpm_tiles_kernel(const uint8_t* __restric
             run += c;
         }
         out[0] = run;
+        out[1] = first_unclean;
     }
     __syncthreads();
     int pos = counts[tid];
     for (int t = t0; t < t1; ++t) {
         bool any_ok, all_ok;
         classify(row, t * tile, min((t + 1) * tile, Tkv), any_ok, all_ok);
-        if (any_ok) out[1 + pos++] = (int)((uint32_t)t | (all_ok ? kTileClean : 0u));
+        if (any_ok) out[2 + pos++] = (int)((uint32_t)t | (all_ok ? kTileClean : 0u));
     }
 }
 

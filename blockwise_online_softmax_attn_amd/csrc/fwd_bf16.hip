@@ -6,7 +6,7 @@
 // post, section "Improving numerical stability"), then out = sum / denominator
 // and lse = max + ln(denominator).
 //
-// Mapping to CDNA4.  A workgroup of 4 waves owns 128 query rows of one
+// Mapping to CDNA4.  A workgroup of 8 waves owns 256 query rows of one
 // (batch, head); each wave owns 32 rows and keeps its Q operand in registers.
 // The scores are computed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_bf16: in the accumulator a lane then holds one query
@@ -16,17 +16,25 @@
 // of O^T += V^T P^T, whose A operand (V^T) is read from the row-major V tile
 // with ds_read_b64_tr_b16; O^T stays in registers with the same lane = query
 // layout, so the rescale by exp(m_old - m_new) is a per-lane scalar multiply.
-// K and V tiles (64 keys) are double-buffered in LDS with XOR-swizzled 16-byte
-// chunks (conflict-free MFMA operand reads), staged through registers so the
-// rotary embedding of K is applied on the way in.
+// K and V tiles (64 keys) are double-buffered in LDS with padded rows
+// (conflict-free MFMA operand reads at base + immediate offsets), staged
+// through registers so the rotary embedding of K is applied on the way in.
+// Tiles every row of the workgroup may see in full run without any masking
+// code; the causal band, padded tails and masks go through a masked copy.
 #include "common.h"
 
 namespace bosa {
 namespace {
 
-constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
-constexpr int NT = 256;   // threads per workgroup (4 waves)
+constexpr int NW = 8;     // waves per workgroup, 32 query rows each
+constexpr int BM = 32 * NW;
+constexpr int NT = 64 * NW;
+// Lazy rescale: the reference max of a row moves only when a tile's row max
+// exceeds it by more than this (log2 units), so probabilities stay <= 2^8
+// and the O/l rescale is almost never executed.  The result is the same up to
+// rounding for any reference.
+constexpr float kTau = 8.f;
 
 template <int D>
 struct Geo {
@@ -34,21 +42,16 @@ struct Geo {
     static constexpr int NDB = D / 32;          // 32-row d blocks of O^T
     static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
     static constexpr int CH = BN * CPR / NT;    // chunks per thread per tile
-    static constexpr int TILE = BN * D;         // elements of one K or V tile
-    static constexpr int LDS_BYTES = 4 * TILE * 2;
+    // Padded LDS rows: K rows step 16 bytes and V rows 64 bytes around the
+    // 256-byte bank window, so the 16-lane ds_read_b128 groups of the K
+    // operand and the 4-row groups of the transposed V reads hit distinct banks.
+    static constexpr int KS = D + 8;            // K row stride (elements)
+    static constexpr int VS = D + 32;           // V row stride (elements)
+    static constexpr int KTILE = BN * KS;
+    static constexpr int VTILE = BN * VS;
+    static constexpr int LDS_BYTES = 2 * (KTILE + VTILE) * 2;
+    static_assert(CH >= 1 && BN * CPR % NT == 0, "staging must divide evenly");
 };
-
-// Swizzled 16-byte chunk position of chunk c in row r.
-template <int D>
-__device__ __forceinline__ int ksw(int r, int c) {
-    if constexpr (D == 128) return c ^ (r & 15);
-    else return c ^ ((r >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int vsw(int r, int c) {
-    if constexpr (D == 128) return c ^ ((r & 3) << 2);
-    else return c ^ (((r >> 1) & 1) << 2);
-}
 
 // Partner exchange between lane l and lane l ^ 32: both outputs of the swap
 // hold {own value, partner value}.
@@ -62,83 +65,193 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 template <int D>
 struct Staging {
     uint4 k[Geo<D>::CH];
     uint4 v[Geo<D>::CH];
     float4 t[Geo<D>::CH][2];
+    int key0;   // first key of the staged tile
 };
 
-// Global -> registers for key tile starting at key0 (rows beyond Tkv are zero).
+// Global -> registers for the key tile starting at key0.  The loads are
+// unconditional (rows beyond Tkv read the last row instead), so that no wait
+// for them is needed before the registers are consumed by stage_store; rows
+// beyond Tkv are zeroed there.
 template <int D>
 __device__ __forceinline__ void stage_load(Staging<D>& st, const uint16_t* __restrict__ kg,
                                            const uint16_t* __restrict__ vg, const float2* __restrict__ tab,
                                            int key0, int Tkv, int rs, int tid) {
     using G = Geo<D>;
+    st.key0 = key0;
 #pragma unroll
     for (int i = 0; i < G::CH; ++i) {
         const int id = i * NT + tid;
         const int row = id / G::CPR, c = id % G::CPR;
-        const int key = key0 + row;
-        if (key < Tkv) {
-            st.k[i] = *(const uint4*)(kg + (long long)key * rs + c * 8);
-            st.v[i] = *(const uint4*)(vg + (long long)key * rs + c * 8);
-            if (tab) {
-                const float4* tp = (const float4*)(tab + (long long)key * (D / 2) + c * 4);
-                st.t[i][0] = tp[0];
-                st.t[i][1] = tp[1];
-            }
-        } else {
-            st.k[i] = make_uint4(0, 0, 0, 0);
-            st.v[i] = make_uint4(0, 0, 0, 0);
-            if (tab) {
-                st.t[i][0] = make_float4(1.f, 0.f, 1.f, 0.f);
-                st.t[i][1] = make_float4(1.f, 0.f, 1.f, 0.f);
-            }
+        const int key = min(key0 + row, Tkv - 1);
+        st.k[i] = *(const uint4*)(kg + (long long)key * rs + c * 8);
+        st.v[i] = *(const uint4*)(vg + (long long)key * rs + c * 8);
+        if (tab) {
+            const float4* tp = (const float4*)(tab + (long long)key * (D / 2) + c * 4);
+            st.t[i][0] = tp[0];
+            st.t[i][1] = tp[1];
         }
     }
 }
 
-// Registers -> LDS buffer (rotary embedding of K applied here).
+// Registers -> LDS buffer (rotary embedding of K applied here, rows beyond
+// Tkv written as zeros).
 template <int D>
-__device__ __forceinline__ void stage_store(const Staging<D>& st, uint16_t* sK, uint16_t* sV, bool rope, int tid) {
+__device__ __forceinline__ void stage_store(const Staging<D>& st, uint16_t* sK, uint16_t* sV, bool rope, int Tkv,
+                                            int tid) {
     using G = Geo<D>;
 #pragma unroll
     for (int i = 0; i < G::CH; ++i) {
         const int id = i * NT + tid;
         const int row = id / G::CPR, c = id % G::CPR;
         uint4 x = st.k[i];
+        uint4 y = st.v[i];
         if (rope) x = rope8_bf16(x, st.t[i][0], st.t[i][1]);
-        *(uint4*)(sK + row * D + ksw<D>(row, c) * 8) = x;
-        *(uint4*)(sV + row * D + vsw<D>(row, c) * 8) = st.v[i];
+        if (st.key0 + row >= Tkv) {
+            x = make_uint4(0, 0, 0, 0);
+            y = make_uint4(0, 0, 0, 0);
+        }
+        *(uint4*)(sK + row * G::KS + c * 8) = x;
+        *(uint4*)(sV + row * G::VS + c * 8) = y;
     }
 }
 
-// A operand of O^T += V^T P^T for d block db and key chunk (kb, cc): lane holds
-// d = 32 db + lane % 32 and the 8 keys the S^T accumulator assigned to its
-// half of the wave (see the P^T packing below).
+__device__ __forceinline__ s16x4 tr_read(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// Exclusions of a tile that is not entirely allowed.  The key behind
+// accumulator register r of the first (second) 32-key block has local index
+// 8 (r / 4) + 4 hh + r % 4 (+ 32).  thr4 = largest allowed local index minus
+// 4 hh (causal order and the key tail); kml = the tile's 64 key-padding
+// allowed bits shifted right by 4 hh; am = attention-mask row of this lane's
+// query at the tile's first key (shifted by 4 hh), or null.
+struct TileMask {
+    int thr4;
+    uint64_t kml;
+    const uint8_t* am;
+};
+
+// One key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 template <int D>
-__device__ __forceinline__ bf16x8 v_operand(const uint16_t* sVb, int kb, int cc, int db, int lane) {
-    const int jj = lane & 15, grp = lane >> 4;
-    const int row = kb * 32 + cc * 16 + 4 * (grp >> 1) + (jj >> 2);
-    const int col = db * 32 + 16 * (grp & 1) + 4 * (jj & 3);
-    const int c = col >> 3, e = col & 7;
-    const uint16_t* p0 = sVb + row * D + vsw<D>(row, c) * 8 + e;
-    const uint16_t* p1 = sVb + (row + 8) * D + vsw<D>(row + 8, c) * 8 + e;
-    s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
-    s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+__device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ Kl, const uint16_t* __restrict__ Vl,
+                                            const bf16x8 (&qreg)[Geo<D>::NC], f32x16 (&o)[Geo<D>::NDB],
+                                            float& m_i, float& l_i, float sl2, bool masked, const TileMask& mk) {
+    using G = Geo<D>;
+    // ---- S^T for keys [0, 32) and [32, 64) of the tile; K operand reads run
+    // two chunks ahead of the MFMAs that consume them
+    bf16x8 ka0[G::NC], ka1[G::NC];
+    ka0[0] = *(const bf16x8*)(Kl);
+    ka1[0] = *(const bf16x8*)(Kl + 32 * G::KS);
+    ka0[1] = *(const bf16x8*)(Kl + 16);
+    ka1[1] = *(const bf16x8*)(Kl + 32 * G::KS + 16);
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) {
+        if (c + 2 < G::NC) {
+            ka0[c + 2] = *(const bf16x8*)(Kl + 16 * (c + 2));
+            ka1[c + 2] = *(const bf16x8*)(Kl + 32 * G::KS + 16 * (c + 2));
+        }
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[c], qreg[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1[c], qreg[c], s1, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // ---- exclusions (only tiles that are not entirely allowed)
+    if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int b0 = 8 * (r >> 2) + (r & 3);
+            bool ok0 = b0 <= mk.thr4 && ((mk.kml >> b0) & 1);
+            bool ok1 = b0 + 32 <= mk.thr4 && ((mk.kml >> (b0 + 32)) & 1);
+            if (mk.am) {
+                ok0 = ok0 && mk.am[b0] == 0;
+                ok1 = ok1 && mk.am[b0 + 32] == 0;
+            }
+            s0[r] = ok0 ? s0[r] : -INFINITY;
+            s1[r] = ok1 ? s1[r] : -INFINITY;
+        }
+    }
+    // ---- online softmax with a lazily moved reference max
+    float mx = max3(s0[0], s1[0], s0[1]);
+    mx = max3(mx, s1[1], s0[2]);
+    mx = max3(mx, s1[2], s0[3]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) mx = max3(mx, fmaxf(s1[r], s0[r + 1]), fmaxf(s0[r], s1[r + 1]));
+    mx = max3(mx, s1[15], s0[15]);
+    mx = xhalf_max(mx) * sl2;
+    if (__ballot(mx > m_i + kTau)) {
+        const float mnew = fmaxf(m_i, mx);
+        const float a = (mnew == -INFINITY) ? 1.f : hw_exp2(m_i - mnew);
+        l_i *= a;
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) o[db] *= a;
+        m_i = mnew;
+    }
+    const float nm = (m_i == -INFINITY) ? 0.f : -m_i;
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        s0[r] = hw_exp2(fmaf(s0[r], sl2, nm));
+        s1[r] = hw_exp2(fmaf(s1[r], sl2, nm));
+        rs0 += s0[r];
+        rs1 += s1[r];
+    }
+    l_i += rs0 + rs1;
+    // ---- P^T operands: chunk (kb, cc) = accumulator registers 8cc .. 8cc+7
+    bf16x8 pb[4];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+        uint4 u0, u1;
+        u0.x = pack_bf16x2(s0[8 * cc + 0], s0[8 * cc + 1]);
+        u0.y = pack_bf16x2(s0[8 * cc + 2], s0[8 * cc + 3]);
+        u0.z = pack_bf16x2(s0[8 * cc + 4], s0[8 * cc + 5]);
+        u0.w = pack_bf16x2(s0[8 * cc + 6], s0[8 * cc + 7]);
+        u1.x = pack_bf16x2(s1[8 * cc + 0], s1[8 * cc + 1]);
+        u1.y = pack_bf16x2(s1[8 * cc + 2], s1[8 * cc + 3]);
+        u1.z = pack_bf16x2(s1[8 * cc + 4], s1[8 * cc + 5]);
+        u1.w = pack_bf16x2(s1[8 * cc + 6], s1[8 * cc + 7]);
+        pb[cc] = __builtin_bit_cast(bf16x8, u0);
+        pb[2 + cc] = __builtin_bit_cast(bf16x8, u1);
+    }
+    // ---- O^T += V^T P^T; transposed V reads run one d block ahead
     typedef short s16x8 __attribute__((ext_vector_type(8)));
-    s16x8 a = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-    return __builtin_bit_cast(bf16x8, a);
+    auto v_load = [&](int db, int kc) -> bf16x8 {
+        const uint16_t* p0 = Vl + (kc * 16) * G::VS + db * 32;
+        const s16x4 r0 = tr_read(p0);
+        const s16x4 r1 = tr_read(p0 + 8 * G::VS);
+        const s16x8 a = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        return __builtin_bit_cast(bf16x8, a);
+    };
+    bf16x8 va[2][4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) va[0][kc] = v_load(0, kc);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        if (db + 1 < G::NDB) {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) va[(db + 1) & 1][kc] = v_load(db + 1, kc);
+        }
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db & 1][kc], pb[kc], o[db], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p) {
     using G = Geo<D>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t* sK = (uint16_t*)smem;          // [2][TILE]
-    uint16_t* sV = sK + 2 * G::TILE;         // [2][TILE]
+    uint16_t* sK = (uint16_t*)smem;          // [2][KTILE]
+    uint16_t* sV = sK + 2 * G::KTILE;        // [2][VTILE]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -152,18 +265,21 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(const FwdParams p)
     const int b = bid / p.H;
 
     const int rs = p.row_stride;
+    const int Tq = p.Tq, Tkv = p.Tkv;
     const uint16_t* qg = (const uint16_t*)p.q + b * p.q_bstride + (long long)h * D;
     const uint16_t* kg = (const uint16_t*)p.k + b * p.kv_bstride + (long long)h * D;
     const uint16_t* vg = (const uint16_t*)p.v + b * p.kv_bstride + (long long)h * D;
     const bool noskip = (p.flags & ATTN_NO_TILE_SKIP) != 0;
     const bool rope = p.rope_q != nullptr;
+    const bool causal = p.causal != 0;
+    const float sl2 = p.scale_log2;
 
     const int q0 = qt * BM;
     const int qw0 = q0 + w * 32;
     const int qi = qw0 + l32;
-    const bool qvalid = qi < p.Tq;
-    const bool wvalid = qw0 < p.Tq;
-    const int qwlast = min(qw0 + 31, p.Tq - 1);
+    const bool qvalid = qi < Tq;
+    const bool wvalid = qw0 < Tq;
+    const int qwlast = min(qw0 + 31, Tq - 1);
     const long long delta = p.q_off - p.kv_off;   // key j allowed for query i iff j - i <= delta
 
     // ---- Q operand: lane holds query qi, d = 16c + 8hh + 0..7 for each chunk c.
@@ -180,147 +296,89 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(const FwdParams p)
         }
         qreg[c] = __builtin_bit_cast(bf16x8, x);
     }
+    // Finish the Q loads here, so no wait for them is left inside the tile loop.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-    // ---- key range of this workgroup
-    const int qlast = min(q0 + BM, p.Tq) - 1;
-    long long nk = p.Tkv;
-    if (p.causal && !noskip) {
-        long long lim = delta + qlast + 1;
+    // ---- key tiles of this workgroup
+    const int qlast = min(q0 + BM, Tq) - 1;
+    long long nk = Tkv;
+    if (causal && !noskip) {
+        const long long lim = delta + qlast + 1;
         nk = lim < 0 ? 0 : (lim < nk ? lim : nk);
     }
     const int nt = (int)((nk + BN - 1) / BN);
-
-    const int* klist = p.kpm_list ? p.kpm_list + (long long)b * p.kpm_list_stride : nullptr;
+    const int* klist = (p.kpm_list && !noskip) ? p.kpm_list + (long long)b * p.kpm_list_stride : nullptr;
     const int nlist = klist ? klist[0] : nt;
+    // Leading tiles with every key allowed for every row of the workgroup.
+    long long nfull = Tkv / BN;
+    if (causal) {
+        const long long lim = q0 + delta + 1;
+        const long long f = lim < 0 ? 0 : lim / BN;
+        nfull = f < nfull ? f : nfull;
+    }
+    if (klist) nfull = klist[1] < nfull ? klist[1] : nfull;
+    if (noskip || p.amask || (p.kpm && !klist)) nfull = 0;
+    const int n_full = (int)(nfull < nt ? nfull : nt);
+
+    auto tile_at = [&](int i) -> int { return klist ? (int)((uint32_t)klist[2 + i] & ~kTileClean) : i; };
+    auto clean_at = [&](int i) -> bool { return klist ? ((uint32_t)klist[2 + i] & kTileClean) != 0 : p.kpm == nullptr; };
+
+    // per-lane LDS operand offsets (elements)
+    const int k_off = l32 * G::KS + 8 * hh;
+    const int jj = lane & 15, grp = lane >> 4;
+    const int v_off = (4 * (grp >> 1) + (jj >> 2)) * G::VS + 16 * (grp & 1) + 4 * (jj & 3);
     const uint8_t* kpm_row = p.kpm ? p.kpm + b * p.kpm_bstride : nullptr;
+    const uint8_t* am_row = (p.amask && qvalid) ? p.amask + (long long)qi * p.amask_stride : nullptr;
 
-    // Tile cursor: i-th visited tile and whether no key in it is padding-masked.
-    auto fetch = [&](int i, int& t, bool& clean) -> bool {
-        if (noskip || !klist) {
-            t = i;
-            clean = (p.kpm == nullptr);
-            return i < nt;
-        }
-        if (i >= nlist) return false;
-        const uint32_t e = (uint32_t)klist[1 + i];
-        t = (int)(e & ~kTileClean);
-        clean = (e & kTileClean) != 0;
-        return t < nt;
-    };
-
-    float m_i = -INFINITY;   // running max of scaled scores (log2 units)
+    float m_i = -INFINITY;   // reference max of scaled scores (log2 units)
     float l_i = 0.f;         // running denominator (this half-wave's keys)
     f32x16 o[G::NDB];
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) o[db] = f32x16{};
 
     Staging<D> st;
-    int t;
-    bool tclean;
-    bool have = fetch(0, t, tclean);
-    if (have) {
-        stage_load<D>(st, kg, vg, p.rope_k, t * BN, p.Tkv, rs, tid);
-        stage_store<D>(st, sK, sV, rope, tid);
+    int ntiles = 0;
+    if (nt > 0 && nlist > 0 && tile_at(0) < nt) {
+        ntiles = 1;
+        stage_load<D>(st, kg, vg, p.rope_k, tile_at(0) * BN, Tkv, rs, tid);
+        stage_store<D>(st, sK, sV, rope, Tkv, tid);
     }
     __syncthreads();
 
     int buf = 0;
-    for (int it = 0; have; ++it) {
-        int tn;
-        bool tnclean;
-        const bool hn = fetch(it + 1, tn, tnclean);
-        if (hn) stage_load<D>(st, kg, vg, p.rope_k, tn * BN, p.Tkv, rs, tid);
-
-        const int key0 = t * BN;
-        const bool wave_dead = !wvalid || (p.causal && !noskip && (long long)key0 - qwlast > delta);
-        if (!wave_dead) {
-            const uint16_t* Kb = sK + buf * G::TILE;
-            const uint16_t* Vb = sV + buf * G::TILE;
-            // ---- S^T = K Q^T for keys [key0, key0+32) and [key0+32, key0+64)
-            f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-            for (int c = 0; c < G::NC; ++c) {
-                const int ch = 2 * c + hh;
-                const bf16x8 a0 = *(const bf16x8*)(Kb + l32 * D + ksw<D>(l32, ch) * 8);
-                const bf16x8 a1 = *(const bf16x8*)(Kb + (32 + l32) * D + ksw<D>(32 + l32, ch) * 8);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[c], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[c], s1, 0, 0, 0);
-            }
-            // ---- exclusions: causal order, key padding, attention mask, tile tail
-            const bool partial = noskip || !tclean || p.amask != nullptr || key0 + BN > p.Tkv ||
-                                 (p.causal && (long long)(key0 + BN - 1) - qw0 > delta);
-            if (partial) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        bool ok = key < p.Tkv;
-                        if (ok && kpm_row) ok = kpm_row[key] == 0;
-                        if (ok && p.causal) ok = (long long)key - qi <= delta;
-                        if (ok && p.amask && qvalid) ok = p.amask[(long long)qi * p.amask_stride + key] == 0;
-                        if (!ok) {
-                            if (kb == 0) s0[r] = -INFINITY;
-                            else s1[r] = -INFINITY;
-                        }
-                    }
-                }
-            }
-            // ---- online softmax update
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-            mx = xhalf_max(mx);
-            const float mnew = fmaxf(m_i, mx * p.scale_log2);
-            const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = hw_exp2(m_i - muse);
-            const float nm = -muse;
-            float rsum = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s0[r] = hw_exp2(fmaf(s0[r], p.scale_log2, nm));
-                s1[r] = hw_exp2(fmaf(s1[r], p.scale_log2, nm));
-                rsum += s0[r] + s1[r];
-            }
-            l_i = fmaf(l_i, alpha, rsum);
-            m_i = mnew;
-            if (__ballot(alpha != 1.f)) {
-#pragma unroll
-                for (int db = 0; db < G::NDB; ++db) o[db] *= alpha;
-            }
-            // ---- P^T operands: chunk (kb, cc) = accumulator registers 8cc .. 8cc+7
-            bf16x8 pb[4];
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                uint4 u0, u1;
-                u0.x = pack_bf16x2(s0[8 * cc + 0], s0[8 * cc + 1]);
-                u0.y = pack_bf16x2(s0[8 * cc + 2], s0[8 * cc + 3]);
-                u0.z = pack_bf16x2(s0[8 * cc + 4], s0[8 * cc + 5]);
-                u0.w = pack_bf16x2(s0[8 * cc + 6], s0[8 * cc + 7]);
-                u1.x = pack_bf16x2(s1[8 * cc + 0], s1[8 * cc + 1]);
-                u1.y = pack_bf16x2(s1[8 * cc + 2], s1[8 * cc + 3]);
-                u1.z = pack_bf16x2(s1[8 * cc + 4], s1[8 * cc + 5]);
-                u1.w = pack_bf16x2(s1[8 * cc + 6], s1[8 * cc + 7]);
-                pb[cc] = __builtin_bit_cast(bf16x8, u0);
-                pb[2 + cc] = __builtin_bit_cast(bf16x8, u1);
-            }
-            // ---- O^T += V^T P^T
-#pragma unroll
-            for (int db = 0; db < G::NDB; ++db) {
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-                    const bf16x8 a = v_operand<D>(Vb, kc >> 1, kc & 1, db, lane);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], o[db], 0, 0, 0);
-                }
-            }
+    for (int i = 0; i < ntiles; ++i) {
+        const int t = tile_at(i);
+        const bool more = (i + 1 < nlist) && tile_at(i + 1) < nt;
+        if (more) {
+            ntiles = i + 2;
+            stage_load<D>(st, kg, vg, p.rope_k, tile_at(i + 1) * BN, Tkv, rs, tid);
         }
-
-        if (hn) stage_store<D>(st, sK + (buf ^ 1) * G::TILE, sV + (buf ^ 1) * G::TILE, rope, tid);
+        const uint16_t* Kl = sK + buf * G::KTILE + k_off;
+        const uint16_t* Vl = sV + buf * G::VTILE + v_off;
+        const int key0 = t * BN;
+        const bool full = i < n_full;
+        if (full || (wvalid && !(causal && !noskip && (long long)key0 - qwlast > delta))) {
+            TileMask mk{63, ~0ull, nullptr};
+            if (!full) {
+                long long thr = (long long)Tkv - key0 - 1;
+                if (causal) {
+                    const long long c = (long long)qi + delta - key0;
+                    thr = c < thr ? c : thr;
+                }
+                mk.thr4 = (int)(thr < -1 ? -1 : (thr > 63 ? 63 : thr)) - 4 * hh;
+                uint64_t km = ~0ull;
+                if (kpm_row && !clean_at(i)) {
+                    const bool okk = key0 + lane < Tkv && kpm_row[key0 + lane] == 0;
+                    km = __ballot(okk);
+                }
+                mk.kml = km >> (4 * hh);
+                mk.am = am_row ? am_row + key0 + 4 * hh : nullptr;
+            }
+            attend_tile<D>(Kl, Vl, qreg, o, m_i, l_i, sl2, !full, mk);
+        }
+        if (more) stage_store<D>(st, sK + (buf ^ 1) * G::KTILE, sV + (buf ^ 1) * G::VTILE, rope, Tkv, tid);
         __syncthreads();
         buf ^= 1;
-        t = tn;
-        tclean = tnclean;
-        have = hn;
     }
 
     // ---- epilogue: out = O / l, lse = ln(sum exp(scores)); optional merge into a partial
