@@ -169,6 +169,50 @@ def cpu_baseline(w, host_inputs, rows: int, heads: int):
     }
 
 
+# ---------------------------------------------------------------- HBM traffic
+COPY_KERNEL_HINT = "copy_f32_kernel"   # the library's plain float32 copy (calibration of the byte counters)
+
+
+def pmc_per_dispatch(csv_path: str, counter: str):
+    """Mean value of `counter` per dispatch, for the attention kernel and for
+    the calibration copy kernel, from a rocprofv3 --pmc counter_collection.csv."""
+    import csv
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        kind = "attn" if "attn_fwd_bf16_kernel<128" in name else ("copy" if COPY_KERNEL_HINT in name else None)
+        if kind:
+            vals[kind][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: float(np.mean(list(v.values()))) for k, v in vals.items()}
+
+
+def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, workload: str) -> dict:
+    """Scale the attention kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
+    by what the same counters read for a copy of known size, and record the
+    kernel source hash they were taken with."""
+    f = pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    wv = pmc_per_dispatch(write_csv, "WRITE_SIZE")
+    nbytes = copy_mib * 2 ** 20
+    scale_f = nbytes / (f["copy"] * 1024.0)
+    scale_w = nbytes / (wv["copy"] * 1024.0)
+    out = {
+        "workload": workload,
+        "kernel_sources_sha256": kernel_sources_sha(),
+        "fetch_kib_per_dispatch": f["attn"], "write_kib_per_dispatch": wv["attn"],
+        "copy_bytes": nbytes, "copy_fetch_kib": f["copy"], "copy_write_kib": wv["copy"],
+        "scale_fetch": scale_f, "scale_write": scale_w,
+        "fetch_bytes_per_launch": f["attn"] * 1024.0 * scale_f,
+        "write_bytes_per_launch": wv["attn"] * 1024.0 * scale_w,
+    }
+    out["bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,9 +220,18 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-heads", type=int, default=3)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (byte-counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of a calibrated bench into "
+                         "the traffic record bench.py reports, then exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        w = workloads.WORKLOADS[args.workload]
+        print(json.dumps(write_traffic(*args.write_traffic, args.copy_calibration_mib or 1024, w.name)))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the ring on a single GPU (the ring itself is emulated "
               "on that GPU); runs on more than one GPU are not part of this build. Use --gpus 1.",
@@ -195,6 +248,14 @@ def main() -> int:
     pairs = step_pairs(w, plan, host[3])
     flops = 4.0 * w.d * pairs
     log(f"{pairs} allowed pairs/step = {flops:.4e} FLOPs; {launches} attention launches/step; warmup {args.warmup}")
+    if args.copy_calibration_mib:
+        # a plain copy of known size through the library's float32 copy kernel:
+        # reads and writes copy_calibration_mib MiB once each
+        src = torch.zeros(args.copy_calibration_mib * 2 ** 18, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        bosa.attn_cast(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
