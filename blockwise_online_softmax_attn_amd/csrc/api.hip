@@ -148,6 +148,14 @@ int check_sizes(int B, int H, int Tq, int Tkv, int d) {
     return ATTN_OK;
 }
 
+// The bf16 kernel addresses one 64-key tile of a head with 32-bit byte
+// offsets: 64 rows of H * d bf16 values must stay below 4 GiB.
+int check_bf16_rows(int dtype, int H, int d) {
+    if (dtype == ATTN_BF16 && (long long)H * d > (1LL << 25))
+        return fail(ATTN_ERR_UNSUPPORTED, "H*d=%lld too large for bf16 (max 2^25)", (long long)H * d);
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,14 +220,20 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     if (std::llabs(q_off) > (1LL << 52) || std::llabs(kv_off) > (1LL << 52))
         return fail(ATTN_ERR_INVALID_ARG, "positions out of range");
 
+    if (int rc = check_bf16_rows(dtype, H, d)) return rc;
+
     Call c = plain_call(q, k, v, out, lse, B, H, Tq, Tkv, d, q_off, kv_off, causal, kpm, attn_mask, dtype, flags);
     hipStream_t s = (hipStream_t)stream;
     const bool rope = rope_base > 0.0 && Tkv > 0;
+    // bf16: the keys are rotated once into a scratch copy that the attention
+    // kernel streams; float32: the kernel rotates keys on the fly.
+    const bool krot = rope && dtype == ATTN_BF16;
     const size_t tab_q = rope ? align_up((size_t)Tq * (d / 2) * sizeof(float2)) : 0;
     const size_t tab_k = rope ? align_up((size_t)Tkv * (d / 2) * sizeof(float2)) : 0;
+    const size_t kbuf = krot ? align_up((size_t)B * Tkv * H * d * 2) : 0;
     const size_t lst = kpm_list_bytes(c);
     Scratch ws;
-    hipError_t e = ws.alloc(tab_q + tab_k + lst, s);
+    hipError_t e = ws.alloc(tab_q + tab_k + kbuf + lst, s);
     if (e != hipSuccess) return hip_fail(e, "scratch allocation");
     char* wp = (char*)ws.ptr;
     if (rope) {
@@ -229,8 +243,15 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
         e = launch_rope_table((float2*)wp, q_off, Tq, d, lb, s);
         if (e == hipSuccess) e = launch_rope_table((float2*)(wp + tab_q), kv_off, Tkv, d, lb, s);
         if (e != hipSuccess) return hip_fail(e, "rotary table launch");
+        if (krot) {
+            void* kr = wp + tab_q + tab_k;
+            e = launch_rope_copy_bf16(k, kr, c.rope_k, B, Tkv, H, d, s);
+            if (e != hipSuccess) return hip_fail(e, "key rotation launch");
+            c.k = kr;
+            c.rope_k = nullptr;
+        }
     }
-    return enqueue(c, lst ? (int*)(wp + tab_q + tab_k) : nullptr, s);
+    return enqueue(c, lst ? (int*)(wp + tab_q + tab_k + kbuf) : nullptr, s);
 }
 
 int attn_merge(float* out_a, float* lse_a, const void* out_b, const float* lse_b, int B, int H, int Tq, int d,
@@ -327,15 +348,20 @@ int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float*
     if (!q || !k || !v || !out || !lse || !acc) return fail(ATTN_ERR_INVALID_ARG, "NULL pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(acc) || ((uintptr_t)out & 7))
         return fail(ATTN_ERR_INVALID_ARG, "q, k, v, acc must be 16-byte aligned, out 8-byte");
+    if (int rc = check_bf16_rows(dtype, H, d)) return rc;
     std::vector<attn_ring_call> plan(n);
     attn_ring_plan(T, P, rank, zigzag, causal, plan.data(), n);
 
     hipStream_t s = (hipStream_t)stream;
     const bool rope = rope_base > 0.0;
+    // bf16: every key block is rotated once (at its absolute positions) into
+    // a scratch copy, as the block's owner would before passing it on.
+    const bool krot = rope && dtype == ATTN_BF16;
     const size_t tab_q = rope ? align_up((size_t)Tl * (d / 2) * sizeof(float2)) : 0;
     const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(float2)) : 0;
+    const size_t kbuf = krot ? align_up((size_t)B * T * H * d * 2) : 0;
     std::vector<size_t> lst_off(n, 0);
-    size_t total = tab_q + tab_k;
+    size_t total = tab_q + tab_k + kbuf;
     std::vector<Call> calls(n);
     const int rs = H * d;
     const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
@@ -379,13 +405,18 @@ int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float*
         }
         if (err == hipSuccess) err = launch_rope_table((float2*)(wp + tab_q), 0, T, d, lb, s);
         if (err != hipSuccess) return hip_fail(err, "rotary table launch");
+        if (krot) {
+            err = launch_rope_copy_bf16(k, wp + tab_q + tab_k, (const float2*)(wp + tab_q), B, T, H, d, s);
+            if (err != hipSuccess) return hip_fail(err, "key rotation launch");
+        }
     }
     bool covered[2] = {false, false};
     for (int i = 0; i < n; ++i) {
         Call& c = calls[i];
         if (rope) {
             c.rope_q = (const float2*)wp + (size_t)plan[i].q_row0 * (d / 2);
-            c.rope_k = (const float2*)(wp + tab_q) + (size_t)plan[i].kv_pos0 * (d / 2);
+            if (krot) c.k = (const uint16_t*)(wp + tab_q + tab_k) + (size_t)plan[i].kv_pos0 * rs;
+            else c.rope_k = (const float2*)(wp + tab_q) + (size_t)plan[i].kv_pos0 * (d / 2);
         }
         const size_t lb = kpm_list_bytes(c);
         if (int rc = enqueue(c, lb ? (int*)(wp + lst_off[i]) : nullptr, s)) return rc;

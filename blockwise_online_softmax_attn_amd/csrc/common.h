@@ -94,7 +94,7 @@ struct FwdParams {
     const uint8_t* kpm;        // row b at kpm + b * kpm_bstride, indexed by local key
     const uint8_t* amask;      // [Tq][amask_stride]
     const float2* rope_q;      // [Tq][d/2] (cos, sin) or null
-    const float2* rope_k;      // [Tkv][d/2] or null
+    const float2* rope_k;      // [Tkv][d/2] or null (float32 kernel; the bf16 kernel takes rotated keys)
     const int* kpm_list;       // per batch: [count, leading clean tiles, entries...] of live key tiles, or null
     long long q_bstride, kv_bstride, o_bstride, kpm_bstride, lse_bstride;
     int row_stride;            // H * d
@@ -124,6 +124,8 @@ hipError_t launch_merge(float* oa, float* la, const void* ob, const float* lb, i
 hipError_t launch_cast(const float* src, void* dst, long long n, int to_bf16, hipStream_t s);
 hipError_t launch_rope_apply(void* x, const long long* pos, double log_base, int B, int T, int H, int d,
                              int is_bf16, hipStream_t s);
+hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
+                                 hipStream_t s);
 hipError_t launch_fill_empty(void* out, int out_bf16, float* lse, int B, int H, int rows, int d, long long o_bstride,
                              int row_stride, long long lse_bstride, int lse_hstride, hipStream_t s);
 

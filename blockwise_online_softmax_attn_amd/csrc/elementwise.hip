@@ -161,6 +161,23 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(void* __restrict__ x, c
     }
 }
 
+// dst = src with the rotary embedding of its position applied to every head
+// (bf16, [B][T][H][d] rows; tab[t] holds the (cos, sin) pairs of position t).
+// The attention kernel then streams already-rotated keys; the rotation is the
+// same float32 arithmetic as the fused query rotation, so results match it bit
+// for bit.  One thread per 16-byte granule (4 coordinate pairs).
+__global__ __launch_bounds__(256) void rope_copy_bf16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                             const float2* __restrict__ tab, long long n, int T,
+                                                             int H, int gpr) {
+    const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= n) return;
+    const long long row = g / gpr;   // (b * T + t) * H + h
+    const int c = (int)(g - row * gpr);
+    const int t = (int)((row / H) % T);
+    const float4* tp = (const float4*)(tab + (long long)t * (4 * gpr) + 4 * c);
+    dst[g] = rope8_bf16(src[g], tp[0], tp[1]);
+}
+
 // Rows [0, rows) become the merge identity: out = 0 (float32 or bf16), lse = -inf.
 template <bool BF16>
 __global__ __launch_bounds__(256) void fill_empty_kernel(void* __restrict__ out, float* __restrict__ lse, int B, int H,
@@ -229,6 +246,15 @@ hipError_t launch_rope_apply(void* x, const long long* pos, double log_base, int
         hipLaunchKernelGGL(rope_apply_kernel<true>, dim3(T, B), dim3(256), 0, s, x, pos, T, H, d, log_base);
     else
         hipLaunchKernelGGL(rope_apply_kernel<false>, dim3(T, B), dim3(256), 0, s, x, pos, T, H, d, log_base);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
+                                 hipStream_t s) {
+    const long long n = (long long)B * T * H * (d / 8);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(rope_copy_bf16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, (const uint4*)src, (uint4*)dst,
+                       tab, n, T, H, d / 8);
     return hipGetLastError();
 }
 

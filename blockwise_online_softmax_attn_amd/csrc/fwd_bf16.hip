@@ -16,20 +16,33 @@
 // of O^T += V^T P^T, whose A operand (V^T) is read from the row-major V tile
 // with ds_read_b64_tr_b16; O^T stays in registers with the same lane = query
 // layout, so the rescale by exp(m_old - m_new) is a per-lane scalar multiply.
-// K and V tiles (64 keys) are double-buffered in LDS with padded rows
-// (conflict-free MFMA operand reads at base + immediate offsets), staged
-// through registers so the rotary embedding of K is applied on the way in.
-// Tiles every row of the workgroup may see in full run without any masking
-// code; the causal band, padded tails and masks go through a masked copy.
+//
+// Data movement.  K (already rotated when the rotary embedding is on) and V
+// tiles of 64 keys go from HBM straight into LDS with buffer loads in LDS mode
+// (no registers, no LDS store instructions); keys past the end of the sequence
+// fall outside the buffer range and arrive as zeros.  Four LDS slots hold the
+// tiles in flight: while a wave works on tile i it already computes the scores
+// of tile i + 1, and the loads of tiles i + 2 and i + 3 are outstanding.  The
+// loads are issued from inline assembly with explicit vmcnt waits, so the
+// compiler does not serialise them against the LDS reads of the other slots.
+// Rows are stored in 16-byte granules permuted by an XOR of the row index, so
+// the MFMA operand reads are free of LDS bank conflicts without padding.
+//
+// Schedule per tile i: issue the loads of tile i + 3; mask (only tiles that
+// are not entirely allowed) and row max of S_i; rescale if the max moved;
+// then S_{i+1} = K_{i+1} Q^T on the matrix cores interleaved with the
+// exponentials of S_i on the vector ALU; then O += V_i P_i; wait for tile
+// i + 2 and synchronise the workgroup.
 #include "common.h"
 
 namespace bosa {
 namespace {
 
-constexpr int BN = 64;    // keys per tile
-constexpr int NW = 8;     // waves per workgroup, 32 query rows each
+constexpr int BN = 64;     // keys per tile
+constexpr int NW = 8;      // waves per workgroup, 32 query rows each
 constexpr int BM = 32 * NW;
 constexpr int NT = 64 * NW;
+constexpr int NSLOT = 4;   // LDS tile slots (tiles i .. i + 3)
 // Lazy rescale: the reference max of a row moves only when a tile's row max
 // exceeds it by more than this (log2 units), so probabilities stay <= 2^8
 // and the O/l rescale is almost never executed.  The result is the same up to
@@ -38,26 +51,32 @@ constexpr float kTau = 8.f;
 
 template <int D>
 struct Geo {
-    static constexpr int NC = D / 16;           // 16-wide d chunks of Q K^T
-    static constexpr int NDB = D / 32;          // 32-row d blocks of O^T
-    static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
-    static constexpr int CH = BN * CPR / NT;    // chunks per thread per tile
-    // Padded LDS rows: K rows step 16 bytes and V rows 64 bytes around the
-    // 256-byte bank window, so the 16-lane ds_read_b128 groups of the K
-    // operand and the 4-row groups of the transposed V reads hit distinct banks.
-    static constexpr int KS = D + 8;            // K row stride (elements)
-    static constexpr int VS = D + 32;           // V row stride (elements)
-    static constexpr int KTILE = BN * KS;
-    static constexpr int VTILE = BN * VS;
-    static constexpr int LDS_BYTES = 2 * (KTILE + VTILE) * 2;
-    static_assert(CH >= 1 && BN * CPR % NT == 0, "staging must divide evenly");
+    static constexpr int NC = D / 16;                // 16-wide d chunks of Q K^T
+    static constexpr int NDB = D / 32;               // 32-row d blocks of O^T
+    static constexpr int GPR = D / 8;                // 16-byte granules per K/V row
+    static constexpr int ROW = 2 * D;                // bytes per K/V row in LDS
+    static constexpr int RP = 256 / ROW;             // rows per 256-byte bank window
+    static constexpr int TILE = BN * ROW;            // bytes per K or V tile
+    static constexpr int SLOT = 2 * TILE;            // K tile, then V tile
+    static constexpr int LDS_BYTES = NSLOT * SLOT;
+    static constexpr int NBLK = TILE / 1024;         // 1 KB load blocks per tile and tensor
+    static constexpr int NI = NBLK / NW;             // load blocks per wave per tile and tensor
+    static constexpr int RPB = 1024 / ROW;           // rows per load block
+    static_assert(NI >= 1 && NBLK % NW == 0, "load blocks must divide evenly over the waves");
+    static_assert(2 * NI <= 15, "vmcnt immediates");
+    // Granule permutations (involutions): stored position = granule ^ h(row).
+    // K: the 16 rows read by one 16-lane group land in 16 distinct bank
+    // windows.  V: the 4 rows x 32 bytes of a transposed-read group and the two
+    // column halves of a 32-lane pass land in distinct banks.
+    static __device__ __forceinline__ int hk(int r) { return (r / RP) % GPR; }
+    static __device__ __forceinline__ int hv(int r) { return 4 * ((r / RP) % (GPR / 4)); }
 };
 
 // Partner exchange between lane l and lane l ^ 32: both outputs of the swap
 // hold {own value, partner value}.
 __device__ __forceinline__ float xhalf_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -65,64 +84,37 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+// NaN-propagating maximum (v_maximum3_f32): unlike fmaxf it needs no operand
+// canonicalisation.  Scores are finite or -inf (excluded keys), where the two agree.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return vmax(a, vmax(b, c)); }
 
-template <int D>
-struct Staging {
-    uint4 k[Geo<D>::CH];
-    uint4 v[Geo<D>::CH];
-    float4 t[Geo<D>::CH][2];
-    int key0;   // first key of the staged tile
-};
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Global -> registers for the key tile starting at key0.  The loads are
-// unconditional (rows beyond Tkv read the last row instead), so that no wait
-// for them is needed before the registers are consumed by stage_store; rows
-// beyond Tkv are zeroed there.
-template <int D>
-__device__ __forceinline__ void stage_load(Staging<D>& st, const uint16_t* __restrict__ kg,
-                                           const uint16_t* __restrict__ vg, const float2* __restrict__ tab,
-                                           int key0, int Tkv, int rs, int tid) {
-    using G = Geo<D>;
-    st.key0 = key0;
-#pragma unroll
-    for (int i = 0; i < G::CH; ++i) {
-        const int id = i * NT + tid;
-        const int row = id / G::CPR, c = id % G::CPR;
-        const int key = min(key0 + row, Tkv - 1);
-        st.k[i] = *(const uint4*)(kg + (long long)key * rs + c * 8);
-        st.v[i] = *(const uint4*)(vg + (long long)key * rs + c * 8);
-        if (tab) {
-            const float4* tp = (const float4*)(tab + (long long)key * (D / 2) + c * 4);
-            st.t[i][0] = tp[0];
-            st.t[i][1] = tp[1];
-        }
-    }
+// Buffer resource for raw byte addressing of `bytes` bytes from `base`;
+// loads at or beyond `bytes` return zeros.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
-// Registers -> LDS buffer (rotary embedding of K applied here, rows beyond
-// Tkv written as zeros).
-template <int D>
-__device__ __forceinline__ void stage_store(const Staging<D>& st, uint16_t* sK, uint16_t* sV, bool rope, int Tkv,
-                                            int tid) {
-    using G = Geo<D>;
-#pragma unroll
-    for (int i = 0; i < G::CH; ++i) {
-        const int id = i * NT + tid;
-        const int row = id / G::CPR, c = id % G::CPR;
-        uint4 x = st.k[i];
-        uint4 y = st.v[i];
-        if (rope) x = rope8_bf16(x, st.t[i][0], st.t[i][1]);
-        if (st.key0 + row >= Tkv) {
-            x = make_uint4(0, 0, 0, 0);
-            y = make_uint4(0, 0, 0, 0);
-        }
-        *(uint4*)(sK + row * G::KS + c * 8) = x;
-        *(uint4*)(sV + row * G::VS + c * 8) = y;
-    }
+// 16 bytes per lane from rsrc + voff into LDS at m0 + 16 * lane.  Issued from
+// inline assembly: the compiler neither waits for it before unrelated LDS
+// reads nor counts it; the kernel waits with explicit vmcnt values.
+__device__ __forceinline__ void load_lds16(uint32_t voff, const u32x4& rsrc, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
+                 : "memory");
 }
 
-__device__ __forceinline__ s16x4 tr_read(const uint16_t* p) {
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and every LDS read it issued has returned, then synchronise the
+// workgroup.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+
+__device__ __forceinline__ s16x4 tr_read(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
@@ -138,74 +130,109 @@ struct TileMask {
     const uint8_t* am;
 };
 
-// One key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+__device__ __forceinline__ void apply_mask(f32x16& s0, f32x16& s1, const TileMask& mk) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int b0 = 8 * (r >> 2) + (r & 3);
+        bool ok0 = b0 <= mk.thr4 && ((mk.kml >> b0) & 1);
+        bool ok1 = b0 + 32 <= mk.thr4 && ((mk.kml >> (b0 + 32)) & 1);
+        if (mk.am) {
+            ok0 = ok0 && mk.am[b0] == 0;
+            ok1 = ok1 && mk.am[b0 + 32] == 0;
+        }
+        s0[r] = ok0 ? s0[r] : -INFINITY;
+        s1[r] = ok1 ? s1[r] : -INFINITY;
+    }
+}
+
+// Row max of the tile (scaled, log2 units) and the lazy move of the reference
+// max m_i with the matching rescale of O and l.
 template <int D>
-__device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ Kl, const uint16_t* __restrict__ Vl,
-                                            const bf16x8 (&qreg)[Geo<D>::NC], f32x16 (&o)[Geo<D>::NDB],
-                                            float& m_i, float& l_i, float sl2, bool masked, const TileMask& mk) {
-    using G = Geo<D>;
-    // ---- S^T for keys [0, 32) and [32, 64) of the tile; K operand reads run
-    // two chunks ahead of the MFMAs that consume them
-    bf16x8 ka0[G::NC], ka1[G::NC];
-    ka0[0] = *(const bf16x8*)(Kl);
-    ka1[0] = *(const bf16x8*)(Kl + 32 * G::KS);
-    ka0[1] = *(const bf16x8*)(Kl + 16);
-    ka1[1] = *(const bf16x8*)(Kl + 32 * G::KS + 16);
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-    __builtin_amdgcn_s_setprio(1);
+__device__ __forceinline__ void update_max(const f32x16& s0, const f32x16& s1, f32x16 (&o)[Geo<D>::NDB], float& m_i,
+                                           float& l_i, float sl2) {
+    // two independent chains of v_maximum3_f32
+    float ma = max3(s0[0], s0[1], s0[2]), mb = max3(s1[0], s1[1], s1[2]);
 #pragma unroll
-    for (int c = 0; c < G::NC; ++c) {
-        if (c + 2 < G::NC) {
-            ka0[c + 2] = *(const bf16x8*)(Kl + 16 * (c + 2));
-            ka1[c + 2] = *(const bf16x8*)(Kl + 32 * G::KS + 16 * (c + 2));
-        }
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[c], qreg[c], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1[c], qreg[c], s1, 0, 0, 0);
+    for (int r = 3; r < 15; r += 2) {
+        ma = max3(ma, s0[r], s0[r + 1]);
+        mb = max3(mb, s1[r], s1[r + 1]);
     }
-    __builtin_amdgcn_s_setprio(0);
-    // ---- exclusions (only tiles that are not entirely allowed)
-    if (masked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int b0 = 8 * (r >> 2) + (r & 3);
-            bool ok0 = b0 <= mk.thr4 && ((mk.kml >> b0) & 1);
-            bool ok1 = b0 + 32 <= mk.thr4 && ((mk.kml >> (b0 + 32)) & 1);
-            if (mk.am) {
-                ok0 = ok0 && mk.am[b0] == 0;
-                ok1 = ok1 && mk.am[b0 + 32] == 0;
-            }
-            s0[r] = ok0 ? s0[r] : -INFINITY;
-            s1[r] = ok1 ? s1[r] : -INFINITY;
-        }
-    }
-    // ---- online softmax with a lazily moved reference max
-    float mx = max3(s0[0], s1[0], s0[1]);
-    mx = max3(mx, s1[1], s0[2]);
-    mx = max3(mx, s1[2], s0[3]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) mx = max3(mx, fmaxf(s1[r], s0[r + 1]), fmaxf(s0[r], s1[r + 1]));
-    mx = max3(mx, s1[15], s0[15]);
+    float mx = max3(ma, mb, vmax(s0[15], s1[15]));
     mx = xhalf_max(mx) * sl2;
     if (__ballot(mx > m_i + kTau)) {
         const float mnew = fmaxf(m_i, mx);
         const float a = (mnew == -INFINITY) ? 1.f : hw_exp2(m_i - mnew);
         l_i *= a;
 #pragma unroll
-        for (int db = 0; db < G::NDB; ++db) o[db] *= a;
+        for (int db = 0; db < Geo<D>::NDB; ++db) o[db] *= a;
         m_i = mnew;
     }
-    const float nm = (m_i == -INFINITY) ? 0.f : -m_i;
+}
+
+// S^T of one tile: keys [0, 32) into s0 and [32, 64) into s1.  Kt = K tile
+// in LDS; koff = per-lane operand offsets (granule c of this lane's key row).
+template <int D>
+__device__ __forceinline__ void scores(const char* Kt, const uint32_t (&koff)[Geo<D>::NC],
+                                       const bf16x8 (&qreg)[Geo<D>::NC], f32x16& s0, f32x16& s1) {
+    using G = Geo<D>;
+    bf16x8 ka0[G::NC], ka1[G::NC];
+    ka0[0] = *(const bf16x8*)(Kt + koff[0]);
+    ka1[0] = *(const bf16x8*)(Kt + koff[0] + 32 * G::ROW);
+    ka0[1] = *(const bf16x8*)(Kt + koff[1]);
+    ka1[1] = *(const bf16x8*)(Kt + koff[1] + 32 * G::ROW);
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) {
+        if (c + 2 < G::NC) {
+            ka0[c + 2] = *(const bf16x8*)(Kt + koff[c + 2]);
+            ka1[c + 2] = *(const bf16x8*)(Kt + koff[c + 2] + 32 * G::ROW);
+        }
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[c], qreg[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1[c], qreg[c], s1, 0, 0, 0);
+    }
+}
+
+// Probabilities of the current tile (in place, then packed to the bf16 P^T
+// operands) interleaved with the scores of the next tile.
+template <int D>
+__device__ __forceinline__ void exp_and_next(f32x16& s0, f32x16& s1, float nm, float sl2, float& l_i, bf16x8 (&pb)[4],
+                                             const char* Kn, const uint32_t (&koff)[Geo<D>::NC],
+                                             const bf16x8 (&qreg)[Geo<D>::NC], f32x16& n0, f32x16& n1) {
+    using G = Geo<D>;
+    constexpr int PER = 16 / G::NC;   // registers of s0 (and of s1) per chunk of the next tile
+    bf16x8 ka0[G::NC], ka1[G::NC];
+    ka0[0] = *(const bf16x8*)(Kn + koff[0]);
+    ka1[0] = *(const bf16x8*)(Kn + koff[0] + 32 * G::ROW);
+    ka0[1] = *(const bf16x8*)(Kn + koff[1]);
+    ka1[1] = *(const bf16x8*)(Kn + koff[1] + 32 * G::ROW);
+    n0 = f32x16{};
+    n1 = f32x16{};
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        s0[r] = hw_exp2(fmaf(s0[r], sl2, nm));
-        s1[r] = hw_exp2(fmaf(s1[r], sl2, nm));
-        rs0 += s0[r];
-        rs1 += s1[r];
+    for (int c = 0; c < G::NC; ++c) {
+        if (c + 2 < G::NC) {
+            ka0[c + 2] = *(const bf16x8*)(Kn + koff[c + 2]);
+            ka1[c + 2] = *(const bf16x8*)(Kn + koff[c + 2] + 32 * G::ROW);
+        }
+        n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[c], qreg[c], n0, 0, 0, 0);
+#pragma unroll
+        for (int r = c * PER; r < c * PER + PER; ++r) {
+            s0[r] = hw_exp2(fmaf(s0[r], sl2, nm));
+            rs0 += s0[r];
+        }
+        n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1[c], qreg[c], n1, 0, 0, 0);
+#pragma unroll
+        for (int r = c * PER; r < c * PER + PER; ++r) {
+            s1[r] = hw_exp2(fmaf(s1[r], sl2, nm));
+            rs1 += s1[r];
+        }
+        // keep the chunks in program order: the exponentials stay interleaved
+        // with the matrix instructions instead of being hoisted ahead of them
+        __builtin_amdgcn_sched_barrier(0);
     }
     l_i += rs0 + rs1;
-    // ---- P^T operands: chunk (kb, cc) = accumulator registers 8cc .. 8cc+7
-    bf16x8 pb[4];
+    // P^T operands: chunk (kb, cc) = accumulator registers 8cc .. 8cc+7
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
         uint4 u0, u1;
@@ -220,41 +247,42 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ Kl, con
         pb[cc] = __builtin_bit_cast(bf16x8, u0);
         pb[2 + cc] = __builtin_bit_cast(bf16x8, u1);
     }
-    // ---- O^T += V^T P^T; transposed V reads run one d block ahead
+}
+
+// O^T += V^T P^T for one tile; Vt = V tile in LDS, voff = per-lane offsets of
+// the transposed reads for each 32-row d block.
+template <int D>
+__device__ __forceinline__ void accumulate_pv(const char* Vt, const uint32_t (&voff)[Geo<D>::NDB], const bf16x8 (&pb)[4],
+                                              f32x16 (&o)[Geo<D>::NDB]) {
+    using G = Geo<D>;
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     auto v_load = [&](int db, int kc) -> bf16x8 {
-        const uint16_t* p0 = Vl + (kc * 16) * G::VS + db * 32;
+        const char* p0 = Vt + voff[db] + (16 * kc) * G::ROW;
         const s16x4 r0 = tr_read(p0);
-        const s16x4 r1 = tr_read(p0 + 8 * G::VS);
+        const s16x4 r1 = tr_read(p0 + 8 * G::ROW);
         const s16x8 a = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
         return __builtin_bit_cast(bf16x8, a);
     };
-    bf16x8 va[2][4];
+    // 4 NDB MFMAs in (db, kc) order; operand reads run PF MFMAs ahead
+    constexpr int NM = 4 * G::NDB, PF = 3;
+    bf16x8 va[PF + 1];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) va[0][kc] = v_load(0, kc);
-    __builtin_amdgcn_s_setprio(1);
+    for (int j = 0; j < PF; ++j) va[j] = v_load(j / 4, j % 4);
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
-        if (db + 1 < G::NDB) {
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) va[(db + 1) & 1][kc] = v_load(db + 1, kc);
-        }
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db & 1][kc], pb[kc], o[db], 0, 0, 0);
+    for (int j = 0; j < NM; ++j) {
+        if (j + PF < NM) va[(j + PF) % (PF + 1)] = v_load((j + PF) / 4, (j + PF) % 4);
+        o[j / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j % (PF + 1)], pb[j % 4], o[j / 4], 0, 0, 0);
     }
-    __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p) {
     using G = Geo<D>;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t* sK = (uint16_t*)smem;          // [2][KTILE]
-    uint16_t* sV = sK + 2 * G::KTILE;        // [2][VTILE]
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
     const int l32 = lane & 31, hh = lane >> 5;
 
     // Heaviest query tiles (most keys under causal order) are dispatched first.
@@ -265,12 +293,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     const int b = bid / p.H;
 
     const int rs = p.row_stride;
+    const uint32_t rs2 = 2u * (uint32_t)rs;   // bytes between consecutive keys
     const int Tq = p.Tq, Tkv = p.Tkv;
     const uint16_t* qg = (const uint16_t*)p.q + b * p.q_bstride + (long long)h * D;
-    const uint16_t* kg = (const uint16_t*)p.k + b * p.kv_bstride + (long long)h * D;
-    const uint16_t* vg = (const uint16_t*)p.v + b * p.kv_bstride + (long long)h * D;
+    const char* kg = (const char*)((const uint16_t*)p.k + b * p.kv_bstride + (long long)h * D);
+    const char* vg = (const char*)((const uint16_t*)p.v + b * p.kv_bstride + (long long)h * D);
     const bool noskip = (p.flags & ATTN_NO_TILE_SKIP) != 0;
-    const bool rope = p.rope_q != nullptr;
     const bool causal = p.causal != 0;
     const float sl2 = p.scale_log2;
 
@@ -289,14 +317,15 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
         uint4 x = make_uint4(0, 0, 0, 0);
         if (qvalid) {
             x = *(const uint4*)(qg + (long long)qi * rs + 16 * c + 8 * hh);
-            if (rope) {
+            if (p.rope_q) {
                 const float4* tp = (const float4*)(p.rope_q + (long long)qi * (D / 2) + 8 * c + 4 * hh);
                 x = rope8_bf16(x, tp[0], tp[1]);
             }
         }
         qreg[c] = __builtin_bit_cast(bf16x8, x);
     }
-    // Finish the Q loads here, so no wait for them is left inside the tile loop.
+    // Finish the Q loads here: the vmcnt bookkeeping of the loop below counts
+    // only tile loads.
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // ---- key tiles of this workgroup
@@ -307,8 +336,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
         nk = lim < 0 ? 0 : (lim < nk ? lim : nk);
     }
     const int nt = (int)((nk + BN - 1) / BN);
-    const int* klist = (p.kpm_list && !noskip) ? p.kpm_list + (long long)b * p.kpm_list_stride : nullptr;
-    const int nlist = klist ? klist[0] : nt;
+    // The live-tile list is read-only for this kernel: constant address space,
+    // so its entries come in through scalar loads (a vector load would need a
+    // vmcnt wait, which would also wait for the tile loads in flight).
+    typedef const __attribute__((address_space(4))) int* cint_ptr;
+    const cint_ptr klist =
+        (p.kpm_list && !noskip) ? (cint_ptr)(p.kpm_list + (long long)b * p.kpm_list_stride) : nullptr;
     // Leading tiles with every key allowed for every row of the workgroup.
     long long nfull = Tkv / BN;
     if (causal) {
@@ -322,63 +355,142 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
 
     auto tile_at = [&](int i) -> int { return klist ? (int)((uint32_t)klist[2 + i] & ~kTileClean) : i; };
     auto clean_at = [&](int i) -> bool { return klist ? ((uint32_t)klist[2 + i] & kTileClean) != 0 : p.kpm == nullptr; };
+    // Number of tiles to visit: the live list is increasing, so cut it at nt.
+    int ntiles = nt;
+    if (klist) {
+        int lo = 0, hi = klist[0];   // first list entry >= nt
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (tile_at(mid) < nt) lo = mid + 1;
+            else hi = mid;
+        }
+        ntiles = lo;
+    }
+    // Tiles [0, n_act) hold allowed keys for some row of this wave (the
+    // leading full tiles, then up to the last tile the wave's causal limit
+    // reaches); the rest are skipped by this wave.
+    int n_act = ntiles;
+    if (!wvalid) {
+        n_act = n_full;
+    } else if (causal && !noskip) {
+        const long long lim = (long long)qwlast + delta;   // last allowed key of the wave
+        int lo = n_full, hi = ntiles;                        // first tile with key0 > lim
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((long long)tile_at(mid) * BN <= lim) lo = mid + 1;
+            else hi = mid;
+        }
+        n_act = lo;
+    }
 
-    // per-lane LDS operand offsets (elements)
-    const int k_off = l32 * G::KS + 8 * hh;
-    const int jj = lane & 15, grp = lane >> 4;
-    const int v_off = (4 * (grp >> 1) + (jj >> 2)) * G::VS + 16 * (grp & 1) + 4 * (jj & 3);
+    // ---- per-lane constants
+    // LDS operand offsets (bytes within a tile)
+    uint32_t koff[G::NC];
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) koff[c] = l32 * G::ROW + 16 * ((2 * c + hh) ^ G::hk(l32));
+    uint32_t voff[G::NDB];
+    {
+        const int jj = lane & 15, grp = lane >> 4;
+        const int r0 = 4 * (grp >> 1) + (jj >> 2);
+        const int hv = G::hv(r0);
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+            const int g = 4 * db + 2 * (grp & 1) + ((jj & 3) >> 1);
+            voff[db] = r0 * G::ROW + 16 * (g ^ hv) + 8 * (jj & 1);
+        }
+    }
+    // Tile loads: this wave moves load blocks w*NI .. w*NI+NI-1 of the K and V
+    // tiles; lane -> (row, stored position) -> source granule.
+    uint32_t dk[G::NI], dv[G::NI];
+#pragma unroll
+    for (int n = 0; n < G::NI; ++n) {
+        const int m = w * G::NI + n;
+        const int row = m * G::RPB + lane / G::GPR;
+        const int pos = lane % G::GPR;
+        dk[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ G::hk(row));
+        dv[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ G::hv(row));
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+    auto issue = [&](int i) {
+        const int key0 = tile_at(i) * BN;
+        // bytes up to the end of the tile's last key row; keys >= Tkv read as zeros
+        const uint32_t nb = (uint32_t)min(Tkv - 1 - key0, BN - 1) * rs2 + 2u * D;
+        const u32x4 rk = buffer_rsrc(kg + (long long)key0 * rs2, nb);
+        const u32x4 rv = buffer_rsrc(vg + (long long)key0 * rs2, nb);
+        const uint32_t base = lds0 + (uint32_t)(i % NSLOT) * G::SLOT + (uint32_t)(w * G::NI) * 1024u;
+#pragma unroll
+        for (int n = 0; n < G::NI; ++n) load_lds16(dk[n], rk, base + 1024u * n);
+#pragma unroll
+        for (int n = 0; n < G::NI; ++n) load_lds16(dv[n], rv, base + G::TILE + 1024u * n);
+    };
     const uint8_t* kpm_row = p.kpm ? p.kpm + b * p.kpm_bstride : nullptr;
     const uint8_t* am_row = (p.amask && qvalid) ? p.amask + (long long)qi * p.amask_stride : nullptr;
+    auto tile_mask = [&](int i) -> TileMask {
+        TileMask mk{63, ~0ull, nullptr};
+        const int key0 = tile_at(i) * BN;
+        long long thr = (long long)Tkv - key0 - 1;
+        if (causal) {
+            const long long c = (long long)qi + delta - key0;
+            thr = c < thr ? c : thr;
+        }
+        mk.thr4 = (int)(thr < -1 ? -1 : (thr > 63 ? 63 : thr)) - 4 * hh;
+        uint64_t km = ~0ull;
+        if (kpm_row && !clean_at(i)) {
+            const bool okk = key0 + lane < Tkv && kpm_row[key0 + lane] == 0;
+            km = __ballot(okk);
+        }
+        mk.kml = km >> (4 * hh);
+        mk.am = am_row ? am_row + key0 + 4 * hh : nullptr;
+        return mk;
+    };
 
     float m_i = -INFINITY;   // reference max of scaled scores (log2 units)
     float l_i = 0.f;         // running denominator (this half-wave's keys)
     f32x16 o[G::NDB];
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) o[db] = f32x16{};
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
 
-    Staging<D> st;
-    int ntiles = 0;
-    if (nt > 0 && nlist > 0 && tile_at(0) < nt) {
-        ntiles = 1;
-        stage_load<D>(st, kg, vg, p.rope_k, tile_at(0) * BN, Tkv, rs, tid);
-        stage_store<D>(st, sK, sV, rope, Tkv, tid);
+    // ---- prologue: tiles 0..2 in flight, tiles 0 and 1 resident, S_0
+    constexpr int PT = 2 * G::NI;   // tile loads per wave per tile
+    if (ntiles > 0) issue(0);
+    if (ntiles > 1) issue(1);
+    if (ntiles > 2) {
+        issue(2);
+        wait_barrier<PT>();
+    } else {
+        wait_barrier<0>();
     }
-    __syncthreads();
+    if (n_act > 0) scores<D>(smem, koff, qreg, s0, s1);
 
-    int buf = 0;
-    for (int i = 0; i < ntiles; ++i) {
-        const int t = tile_at(i);
-        const bool more = (i + 1 < nlist) && tile_at(i + 1) < nt;
-        if (more) {
-            ntiles = i + 2;
-            stage_load<D>(st, kg, vg, p.rope_k, tile_at(i + 1) * BN, Tkv, rs, tid);
+    // One tile: softmax of the scores in (c0, c1), scores of the next tile
+    // into (x0, x1), O += V P.  Called with the two register sets swapped on
+    // alternate tiles, so no copy of the scores is needed.
+    auto step = [&](int i, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1) {
+        const bool more = i + 3 < ntiles;
+        if (more) issue(i + 3);
+        if (i < n_act) {
+            if (i >= n_full) apply_mask(c0, c1, tile_mask(i));
+            update_max<D>(c0, c1, o, m_i, l_i, sl2);
+            const float nm = (m_i == -INFINITY) ? 0.f : -m_i;
+            bf16x8 pb[4];
+            __builtin_amdgcn_s_setprio(1);
+            // The scores of tile i + 1 are computed even when this wave will
+            // not use them (last tile, or no allowed key for its rows): the
+            // slot is always readable, and one code path keeps the registers
+            // in budget.
+            exp_and_next<D>(c0, c1, nm, sl2, l_i, pb, smem + ((i + 1) % NSLOT) * G::SLOT, koff, qreg, x0, x1);
+            accumulate_pv<D>(smem + (i % NSLOT) * G::SLOT + G::TILE, voff, pb, o);
+            __builtin_amdgcn_s_setprio(0);
         }
-        const uint16_t* Kl = sK + buf * G::KTILE + k_off;
-        const uint16_t* Vl = sV + buf * G::VTILE + v_off;
-        const int key0 = t * BN;
-        const bool full = i < n_full;
-        if (full || (wvalid && !(causal && !noskip && (long long)key0 - qwlast > delta))) {
-            TileMask mk{63, ~0ull, nullptr};
-            if (!full) {
-                long long thr = (long long)Tkv - key0 - 1;
-                if (causal) {
-                    const long long c = (long long)qi + delta - key0;
-                    thr = c < thr ? c : thr;
-                }
-                mk.thr4 = (int)(thr < -1 ? -1 : (thr > 63 ? 63 : thr)) - 4 * hh;
-                uint64_t km = ~0ull;
-                if (kpm_row && !clean_at(i)) {
-                    const bool okk = key0 + lane < Tkv && kpm_row[key0 + lane] == 0;
-                    km = __ballot(okk);
-                }
-                mk.kml = km >> (4 * hh);
-                mk.am = am_row ? am_row + key0 + 4 * hh : nullptr;
-            }
-            attend_tile<D>(Kl, Vl, qreg, o, m_i, l_i, sl2, !full, mk);
-        }
-        if (more) stage_store<D>(st, sK + (buf ^ 1) * G::KTILE, sV + (buf ^ 1) * G::VTILE, rope, Tkv, tid);
-        __syncthreads();
-        buf ^= 1;
+        // tile i + 2 resident for every wave; tile i + 3 may stay in flight
+        if (more) wait_barrier<PT>();
+        else wait_barrier<0>();
+    };
+    f32x16 n0, n1;
+    for (int i = 0; i < ntiles; i += 2) {
+        step(i, s0, s1, n0, n1);
+        if (i + 1 < ntiles) step(i + 1, n0, n1, s0, s1);
     }
 
     // ---- epilogue: out = O / l, lse = ln(sum exp(scores)); optional merge into a partial
@@ -458,6 +570,7 @@ hipError_t launch(const FwdParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s) {
+    if (p.rope_k) return hipErrorInvalidValue;   // keys must arrive rotated
     if (d == 128) return launch<128>(p, s);
     return launch<64>(p, s);
 }
