@@ -285,8 +285,16 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // Heaviest query tiles (most keys under causal order) are dispatched first.
+    // Workgroup b is dispatched to XCD b % 8 (each XCD has its own L2).  The
+    // logical order is renumbered so that every XCD receives a contiguous range
+    // of it: the query tiles of one head then share that XCD's L2 for K and V.
+    // Within the logical order the heaviest query tiles (most keys under causal
+    // order) come first.
     int bid = blockIdx.x;
+    {
+        const int full = (int)gridDim.x & ~7;
+        if (bid < full) bid = (bid & 7) * (full >> 3) + (bid >> 3);
+    }
     const int qt = p.n_qtiles - 1 - bid % p.n_qtiles;
     bid /= p.n_qtiles;
     const int h = bid % p.H;
