@@ -221,7 +221,7 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
-    ap.add_argument("--cpu-heads", type=int, default=3)
+    ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (byte-counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
