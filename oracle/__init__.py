@@ -15,7 +15,8 @@ Every function states the passage of the source pages it follows:
   blocks with Ring", "Balance the workload in causal attention";
 * the sequence/context-parallelism post on brunomaga.github.io: section "Ring
   Attention" (fraction form), "Improving numerical stability" (safe softmax,
-  accumulator rescale, LogSumExp), "Distributed algorithm" and "Implementation".
+  accumulator rescale, LogSumExp), "Distributed algorithm" and "Implementation"
+  (forward and backward pass of the ring).
 
 Pins: every function here is checked by ``tests/test_oracle_pins.py`` against
 facts the pages or mathematics fix (printed worked example, closed forms,
@@ -30,7 +31,9 @@ from .reference import (  # noqa: F401
     rope_rotate_f32,
     rope_frequencies,
     sdpa,
+    sdpa_backward,
     attention,
+    attention_backward,
     merge,
     ring_order,
     zigzag_chunks,

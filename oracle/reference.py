@@ -30,6 +30,8 @@ def round_to_dtype(x, dtype: str) -> np.ndarray:
     before the dot product (RoPE applied to stored bf16 tensors).
     """
     x = np.asarray(x, dtype=np.float64)
+    if dtype == "f64":
+        return x
     if dtype == "f32":
         return x.astype(np.float32).astype(np.float64)
     if dtype != "bf16":
@@ -118,6 +120,29 @@ def rope_rotate_f32(x, pos, base: float) -> np.ndarray:
 # --------------------------------------------------------------------------
 # scaled dot-product attention, plain definition
 # --------------------------------------------------------------------------
+def _rotated(x, pos, base: float, dtype: str) -> np.ndarray:
+    """Rotated operand as the attention sees it: the float32 rotation rounded
+    to the input dtype, or (dtype "f64") the exact float64 rotation with no
+    rounding at all, for derivative checks."""
+    if dtype == "f64":
+        return rope_rotate(x, pos, base)
+    return round_to_dtype(rope_rotate_f32(x, pos, base), dtype)
+
+
+def _allowed(B, Tq, Tkv, q_pos, kv_pos, causal, kpm, attn_mask) -> np.ndarray:
+    """allowed[b, i, j]: key-padding and attention-mask exclusions combined
+    ("Transformers and Attention" #2) and, if causal, key position <= query
+    position (#24)."""
+    allowed = np.ones((B, Tq, Tkv), dtype=bool)
+    if kpm is not None:
+        allowed &= ~(np.asarray(kpm) != 0)[:, None, :]
+    if attn_mask is not None:
+        allowed &= ~(np.asarray(attn_mask) != 0)[None, :, :]
+    if causal:
+        allowed &= (np.asarray(kv_pos)[None, None, :] <= np.asarray(q_pos)[None, :, None])
+    return allowed
+
+
 def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=None,
          rope_base: float = 0.0, dtype: str = "bf16") -> Tuple[np.ndarray, np.ndarray]:
     """out, lse of softmax(q k^T / sqrt(d) + mask) v for every (batch, head).
@@ -150,16 +175,9 @@ def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=No
     q_pos = np.asarray(q_pos, dtype=np.int64)
     kv_pos = np.asarray(kv_pos, dtype=np.int64)
     if rope_base > 0:
-        q = round_to_dtype(rope_rotate_f32(q, q_pos, rope_base), dtype)
-        k = round_to_dtype(rope_rotate_f32(k, kv_pos, rope_base), dtype)
-
-    allowed = np.ones((B, Tq, Tkv), dtype=bool)
-    if kpm is not None:
-        allowed &= ~(np.asarray(kpm) != 0)[:, None, :]
-    if attn_mask is not None:
-        allowed &= ~(np.asarray(attn_mask) != 0)[None, :, :]
-    if causal:
-        allowed &= (kv_pos[None, None, :] <= q_pos[None, :, None])
+        q = _rotated(q, q_pos, rope_base, dtype)
+        k = _rotated(k, kv_pos, rope_base, dtype)
+    allowed = _allowed(B, Tq, Tkv, q_pos, kv_pos, causal, kpm, attn_mask)
 
     scale = 1.0 / math.sqrt(d)
     dv = v.shape[-1]
@@ -181,6 +199,77 @@ def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=No
             out[b, :, h, :] = p @ v[b, :, h, :]
             lse[b, h, :] = np.where(has, m_safe + np.log(l_safe), NEG_INF)
     return out, lse
+
+
+def sdpa_backward(q, k, v, dout, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=None,
+                  rope_base: float = 0.0, dtype: str = "bf16") -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients dq, dk, dv of L = sum_i dout_i . out_i for the ``sdpa``
+    forward with the same arguments.
+
+    The brunomaga.github.io post ("Ring Attention", item 3; "Implementation",
+    the backward pass) states that the backward pass is computed blockwise
+    from dout, q, k, v, the final out and the saved log-sum-exp, with dq
+    accumulated locally and dk, dv accumulated alongside their K/V block.  The
+    block gradients are those of the whole attention, so the plain definition
+    is the chain rule through the forward definition, written out here with
+    the full probability matrix:
+        P = softmax of the allowed scores (exactly 0 elsewhere),
+        dv_j  = sum_i P_ij dout_i,
+        dP_ij = dout_i . v_j,
+        dS_ij = P_ij (dP_ij - sum_l P_il dP_il),
+        dq'_i = (1/sqrt(d)) sum_j dS_ij k'_j,   dk'_j = (1/sqrt(d)) sum_i dS_ij q'_i,
+    and with RoPE dq = R(pos)^T dq', dk = R(pos)^T dk' (the rotation is
+    orthogonal).  The rounding of the rotated operands to the input dtype is
+    passed through unchanged (its derivative is taken as the identity).
+    A row with no allowed key contributes nothing.
+
+    Shapes as in ``sdpa``; dout is (B, Tq, H, d_v).  Returns float64 dq
+    (B, Tq, H, d), dk (B, Tkv, H, d), dv (B, Tkv, H, d_v).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, Tq, H, d = q.shape
+    Tkv = k.shape[1]
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    kv_pos = np.asarray(kv_pos, dtype=np.int64)
+    qr, kr = q, k
+    if rope_base > 0:
+        qr = _rotated(q, q_pos, rope_base, dtype)
+        kr = _rotated(k, kv_pos, rope_base, dtype)
+    allowed = _allowed(B, Tq, Tkv, q_pos, kv_pos, causal, kpm, attn_mask)
+    scale = 1.0 / math.sqrt(d)
+    dq = np.zeros_like(qr)
+    dk = np.zeros_like(kr)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        ok = allowed[b]
+        has = ok.any(axis=1)
+        for h in range(H):
+            s = scale * (qr[b, :, h, :] @ kr[b, :, h, :].T)
+            m = np.where(has, np.max(np.where(ok, s, NEG_INF), axis=1) if Tkv else 0.0, 0.0)
+            with np.errstate(over="ignore"):
+                e = np.where(ok, np.exp(s - m[:, None]), 0.0)
+            l = np.where(has, e.sum(axis=1), 1.0)
+            p = e / l[:, None]                                        # (Tq, Tkv)
+            g = dout[b, :, h, :]
+            dp = g @ v[b, :, h, :].T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dv[b, :, h, :] = p.T @ g
+            dq[b, :, h, :] = scale * (ds @ kr[b, :, h, :])
+            dk[b, :, h, :] = scale * (ds.T @ qr[b, :, h, :])
+    if rope_base > 0:
+        dq = rope_rotate(dq, -q_pos, rope_base)
+        dk = rope_rotate(dk, -kv_pos, rope_base)
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, dout, *, q_off: int = 0, kv_off: int = 0, **kw):
+    """``sdpa_backward`` with contiguous positions q_off + i and kv_off + j."""
+    Tq = np.asarray(q).shape[1]
+    Tkv = np.asarray(k).shape[1]
+    return sdpa_backward(q, k, v, dout, q_off + np.arange(Tq), kv_off + np.arange(Tkv), **kw)
 
 
 def attention(q, k, v, *, q_off: int = 0, kv_off: int = 0, **kw) -> Tuple[np.ndarray, np.ndarray]:
