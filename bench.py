@@ -42,6 +42,7 @@ PEAK_BF16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json")
 KERNEL_SOURCES = ["blockwise_online_softmax_attn_amd/csrc/fwd_bf16.hip",
+                  "blockwise_online_softmax_attn_amd/csrc/tile_io.h",
                   "blockwise_online_softmax_attn_amd/csrc/common.h"]
 
 

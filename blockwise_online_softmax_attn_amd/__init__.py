@@ -1,4 +1,5 @@
-"""Blockwise online-softmax attention forward for AMD Instinct MI355X (gfx950).
+"""Blockwise online-softmax attention (forward and backward) for AMD Instinct
+MI355X (gfx950).
 
 Python binding of libattn.so (C ABI in include/attn.h).  These functions only
 marshal arguments: they check tensor placement, shapes and dtypes, allocate
@@ -163,6 +164,74 @@ def attn_ring_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, P: int, 
                               int(flags), _stream(stream))
     check(rc)
     return out, lse
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+             lse: torch.Tensor, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None, *, q_off: int = 0, kv_off: int = 0, causal: bool = False,
+             kpm: Optional[torch.Tensor] = None, attn_mask: Optional[torch.Tensor] = None, rope_base: float = 0.0,
+             flags: int = 0, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dq, dk, dv of sum(dout * out) for the attn_fwd call with the same
+    arguments (see attn_bwd in attn.h).  bf16 inputs; gradients bf16, or
+    float32 with ATTN_OUT_F32 (ATTN_ACCUMULATE adds into dq, dk, dv)."""
+    load()
+    B, Tq, H, d = q.shape
+    Tkv = k.shape[1]
+    if k.shape != (B, Tkv, H, d) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if lse.shape != (B, H, Tq):
+        raise ValueError("lse must be (B, H, Tq)")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    gdt = torch.float32 if (flags & ATTN_OUT_F32) else torch.bfloat16
+    if flags & ATTN_ACCUMULATE and (dq is None or dk is None or dv is None):
+        raise ValueError("ATTN_ACCUMULATE needs dq, dk and dv to add into")
+    dq = torch.empty(q.shape, dtype=gdt, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=gdt, device=q.device) if dk is None else dk
+    dv = torch.empty(k.shape, dtype=gdt, device=q.device) if dv is None else dv
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape:
+        raise ValueError("gradient shape mismatch")
+    if kpm is not None and (kpm.shape != (B, Tkv) or kpm.dtype != torch.uint8):
+        raise ValueError("kpm must be uint8 (B, Tkv)")
+    if attn_mask is not None and (attn_mask.shape != (Tq, Tkv) or attn_mask.dtype != torch.uint8):
+        raise ValueError("attn_mask must be uint8 (Tq, Tkv)")
+    rc = load().attn_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"),
+                         _dev(lse, "lse", torch.float32), _dev(dq, "dq", gdt), _dev(dk, "dk", gdt),
+                         _dev(dv, "dv", gdt), B, H, Tq, Tkv, d, int(q_off), int(kv_off), 1 if causal else 0,
+                         _dev(kpm, "kpm"), _dev(attn_mask, "attn_mask"), float(rope_base), ATTN_BF16, int(flags),
+                         _stream(stream))
+    check(rc)
+    return dq, dk, dv
+
+
+def attn_ring_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                  lse: torch.Tensor, *, P: int, rank: int, zigzag: bool, causal: bool = True,
+                  kpm: Optional[torch.Tensor] = None, rope_base: float = 0.0, flags: int = 0,
+                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                  dv: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of one rank's ring share: local q, out, dout (B, T/P, H, d),
+    full k, v (B, T, H, d), lse from attn_ring_fwd.  Returns dq (local) and
+    this rank's contributions dk, dv (full length)."""
+    load()
+    B, T, H, d = k.shape
+    Tl = q.shape[1]
+    if q.shape != (B, T // P, H, d) or Tl * P != T or v.shape != k.shape:
+        raise ValueError("ring shapes: q (B, T/P, H, d), k = v (B, T, H, d)")
+    if out.shape != q.shape or dout.shape != q.shape or lse.shape != (B, H, Tl):
+        raise ValueError("out, dout (B, T/P, H, d) and lse (B, H, T/P) expected")
+    gdt = torch.float32 if (flags & ATTN_OUT_F32) else torch.bfloat16
+    dq = torch.empty(q.shape, dtype=gdt, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=gdt, device=q.device) if dk is None else dk
+    dv = torch.empty(k.shape, dtype=gdt, device=q.device) if dv is None else dv
+    rc = load().attn_ring_bwd(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
+                              _dev(v, "v", torch.bfloat16), _dev(out, "out", torch.bfloat16),
+                              _dev(dout, "dout", torch.bfloat16), _dev(lse, "lse", torch.float32),
+                              _dev(dq, "dq", gdt), _dev(dk, "dk", gdt), _dev(dv, "dv", gdt), B, H, T, d, P, rank,
+                              int(zigzag), int(causal), _dev(kpm, "kpm"), float(rope_base), ATTN_BF16, int(flags),
+                              _stream(stream))
+    check(rc)
+    return dq, dk, dv
 
 
 class KernelTimer:

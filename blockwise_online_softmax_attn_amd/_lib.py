@@ -15,7 +15,8 @@ ATTN_ACCUMULATE, ATTN_OUT_F32, ATTN_NO_TILE_SKIP = 1, 2, 4
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan", "attn_ring_fwd",
-           "attn_profile_start", "attn_profile_stop", "attn_last_error", "attn_version")
+           "attn_bwd", "attn_ring_bwd", "attn_profile_start", "attn_profile_stop", "attn_last_error",
+           "attn_version")
 
 
 class RingCall(ctypes.Structure):
@@ -55,10 +56,12 @@ def load() -> ctypes.CDLL:
     lib.attn_cast.argtypes = [vp, vp, ll, i, vp]
     lib.attn_ring_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(RingCall), i]
     lib.attn_ring_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, d, i, u, vp]
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, ll, ll, i, vp, vp, d, i, u, vp]
+    lib.attn_ring_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, d, i, u, vp]
     lib.attn_profile_start.argtypes = [i]
     lib.attn_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_float), i]
     for name in ("attn_fwd", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan", "attn_ring_fwd",
-                 "attn_profile_start", "attn_profile_stop", "attn_version"):
+                 "attn_bwd", "attn_ring_bwd", "attn_profile_start", "attn_profile_stop", "attn_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p

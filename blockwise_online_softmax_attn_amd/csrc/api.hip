@@ -90,6 +90,12 @@ Call plain_call(const void* q, const void* k, const void* v, void* out, float* l
     return c;
 }
 
+size_t kpm_list_bytes(const uint8_t* kpm, int dtype, unsigned flags, int B, int Tkv) {
+    if (!kpm || dtype != ATTN_BF16 || (flags & ATTN_NO_TILE_SKIP)) return 0;
+    const long long ntk = (Tkv + kTile - 1) / kTile;
+    return align_up((size_t)B * (size_t)(ntk + 2) * sizeof(int));
+}
+
 size_t kpm_list_bytes(const Call& c) {
     if (!c.kpm || c.dtype != ATTN_BF16 || (c.flags & ATTN_NO_TILE_SKIP)) return 0;
     const long long ntk = (c.Tkv + kTile - 1) / kTile;
@@ -136,6 +142,62 @@ int enqueue(const Call& c, int* list, hipStream_t s) {
         ++g_prof.n;
     }
     return ATTN_OK;
+}
+
+// Run one kernel launch, bracketed by profiling events when profiling is on.
+template <typename F>
+int timed_launch(F&& launch, const char* what, hipStream_t s) {
+    hipError_t e;
+    const bool timed = g_prof.on && g_prof.n < g_prof.cap;
+    if (timed && (e = hipEventRecord(g_prof.ev[2 * g_prof.n], s)) != hipSuccess) return hip_fail(e, "event record");
+    e = launch();
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (timed) {
+        if ((e = hipEventRecord(g_prof.ev[2 * g_prof.n + 1], s)) != hipSuccess) return hip_fail(e, "event record");
+        ++g_prof.n;
+    }
+    return ATTN_OK;
+}
+
+// One backward sub-call: q, k (rotated when RoPE is on), v, dout, ld2 and the
+// float32 gradients in place, with element strides.
+struct BwdCall {
+    const void* q; const void* k; const void* v; const void* dout; const float2* ld2;
+    float* dq; float* dk; float* dv;
+    int B, H, Tq, Tkv, d;
+    long long q_off, kv_off;
+    int causal;
+    const uint8_t* kpm; const uint8_t* amask;
+    unsigned flags;
+    long long q_bstride, kv_bstride, kpm_bstride, lse_bstride;
+    int lse_hstride, amask_stride;
+};
+
+// Enqueue the dQ and dK/dV kernels of one sub-call; `list` is scratch of
+// kpm_list_bytes bytes for the live key tiles of the dQ kernel (or null).
+int enqueue_bwd(const BwdCall& c, int* list, hipStream_t s) {
+    BwdParams p{};
+    p.q = c.q; p.k = c.k; p.v = c.v; p.dout = c.dout; p.ld2 = c.ld2;
+    p.dq = c.dq; p.dk = c.dk; p.dv = c.dv;
+    p.kpm = c.kpm; p.amask = c.amask; p.kpm_list = nullptr;
+    p.q_bstride = c.q_bstride; p.kv_bstride = c.kv_bstride; p.kpm_bstride = c.kpm_bstride;
+    p.lse_bstride = c.lse_bstride; p.lse_hstride = c.lse_hstride; p.amask_stride = c.amask_stride;
+    p.row_stride = c.H * c.d;
+    p.B = c.B; p.H = c.H; p.Tq = c.Tq; p.Tkv = c.Tkv;
+    p.q_off = c.q_off; p.kv_off = c.kv_off; p.causal = c.causal ? 1 : 0;
+    p.flags = c.flags;
+    p.scale = (float)(1.0 / std::sqrt((double)c.d));
+    p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.d));
+    hipError_t e;
+    if (list) {
+        const int ntk = (c.Tkv + kTile - 1) / kTile;
+        e = launch_kpm_tiles(c.kpm, c.kpm_bstride, c.B, c.Tkv, kTile, list, ntk + 2, s);
+        if (e != hipSuccess) return hip_fail(e, "key-padding tile list launch");
+        p.kpm_list = list;
+        p.kpm_list_stride = ntk + 2;
+    }
+    if (int rc = timed_launch([&] { return launch_bwd_dq(p, c.d, s); }, "backward dQ kernel launch", s)) return rc;
+    return timed_launch([&] { return launch_bwd_dkdv(p, c.d, s); }, "backward dK/dV kernel launch", s);
 }
 
 int check_sizes(int B, int H, int Tq, int Tkv, int d) {
@@ -435,6 +497,218 @@ int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float*
     if (dtype == ATTN_F32 && (void*)acc == out) return ATTN_OK;
     err = launch_cast(acc, out, nel, dtype == ATTN_BF16, s);
     return err == hipSuccess ? ATTN_OK : hip_fail(err, "cast launch");
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int B, int H, int Tq, int Tkv, int d, long long q_off, long long kv_off,
+             int causal, const uint8_t* kpm, const uint8_t* attn_mask, double rope_base, int dtype, unsigned flags,
+             attn_stream_t stream) {
+    g_err.clear();
+    if (int rc = check_sizes(B, H, Tq, Tkv, d)) return rc;
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass supports bf16 inputs only");
+    if (int rc = check_bf16_rows(dtype, H, d)) return rc;
+    if (flags & ~(unsigned)(ATTN_ACCUMULATE | ATTN_OUT_F32 | ATTN_NO_TILE_SKIP))
+        return fail(ATTN_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+    if ((flags & ATTN_ACCUMULATE) && !(flags & ATTN_OUT_F32))
+        return fail(ATTN_ERR_INVALID_ARG, "ATTN_ACCUMULATE needs float32 gradients (ATTN_OUT_F32)");
+    if (!(rope_base >= 0.0) || std::isinf(rope_base)) return fail(ATTN_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
+    if (B == 0 || H == 0 || (Tq == 0 && Tkv == 0)) return ATTN_OK;
+    if (Tq > 0 && (!q || !out || !dout || !lse || !dq)) return fail(ATTN_ERR_INVALID_ARG, "q, out, dout, lse and dq must not be NULL");
+    if (Tkv > 0 && (!k || !v || !dk || !dv)) return fail(ATTN_ERR_INVALID_ARG, "k, v, dk and dv must not be NULL");
+    for (const void* ptr : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+        if (ptr && !aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (std::llabs(q_off) > (1LL << 52) || std::llabs(kv_off) > (1LL << 52))
+        return fail(ATTN_ERR_INVALID_ARG, "positions out of range");
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool f32 = (flags & ATTN_OUT_F32) != 0;
+    const bool accum = (flags & ATTN_ACCUMULATE) != 0;
+    const long long rs = (long long)H * d;
+    const size_t nq = (size_t)B * Tq * rs, nk = (size_t)B * Tkv * rs;
+    if (Tq == 0 || Tkv == 0) {
+        // nothing reaches the empty side; the other side's gradients are zero
+        if (accum) return ATTN_OK;
+        hipError_t e = hipSuccess;
+        void* z = Tq == 0 ? dk : dq;
+        const size_t n = Tq == 0 ? nk : nq;
+        if (f32) {
+            e = launch_zero_f32((float*)z, (long long)n, s);
+            if (e == hipSuccess && Tq == 0) e = launch_zero_f32((float*)dv, (long long)n, s);
+        } else {
+            e = launch_fill_empty(z, 1, nullptr, B, H, Tq == 0 ? Tkv : Tq, d, (long long)(Tq == 0 ? Tkv : Tq) * rs,
+                                  (int)rs, 0, 0, s);
+            if (e == hipSuccess && Tq == 0)
+                e = launch_fill_empty(dv, 1, nullptr, B, H, Tkv, d, (long long)Tkv * rs, (int)rs, 0, 0, s);
+        }
+        return e == hipSuccess ? ATTN_OK : hip_fail(e, "zero fill");
+    }
+    const bool rope = rope_base > 0.0;
+    // float32 results go straight to the caller's buffers unless they must
+    // still be rotated back (dq, dk with RoPE) or cast (bf16 outputs)
+    const bool dq_direct = f32 && !rope, dk_direct = dq_direct, dv_direct = dq_direct;
+    const size_t ld_b = align_up((size_t)B * H * Tq * sizeof(float2));
+    const size_t tab_q = rope ? align_up((size_t)Tq * (d / 2) * sizeof(float2)) : 0;
+    const size_t tab_k = rope ? align_up((size_t)Tkv * (d / 2) * sizeof(float2)) : 0;
+    const size_t qr_b = rope ? align_up(nq * 2) : 0, kr_b = rope ? align_up(nk * 2) : 0;
+    const size_t dq_b = dq_direct ? 0 : align_up(nq * 4), dk_b = dk_direct ? 0 : align_up(nk * 4);
+    const size_t dv_b = dv_direct ? 0 : align_up(nk * 4);
+    const size_t lst = kpm_list_bytes(kpm, dtype, flags, B, Tkv);
+    Scratch ws;
+    hipError_t e = ws.alloc(ld_b + tab_q + tab_k + qr_b + kr_b + dq_b + dk_b + dv_b + lst, s);
+    if (e != hipSuccess) return hip_fail(e, "scratch allocation");
+    char* wp = (char*)ws.ptr;
+    float2* ld2 = (float2*)wp;
+    wp += ld_b;
+    float2* tq = (float2*)wp;
+    wp += tab_q;
+    float2* tk = (float2*)wp;
+    wp += tab_k;
+    void* qr = wp;
+    wp += qr_b;
+    void* kr = wp;
+    wp += kr_b;
+    float* gq = dq_direct ? (float*)dq : (float*)wp;
+    wp += dq_b;
+    float* gk = dk_direct ? (float*)dk : (float*)wp;
+    wp += dk_b;
+    float* gv = dv_direct ? (float*)dv : (float*)wp;
+    wp += dv_b;
+    int* list = lst ? (int*)wp : nullptr;
+
+    e = launch_bwd_delta(dout, out, lse, ld2, B, H, Tq, d, (long long)Tq * rs, (int)rs, (long long)H * Tq, Tq, s);
+    if (e != hipSuccess) return hip_fail(e, "delta launch");
+    if (rope) {
+        const double lb = std::log(rope_base);
+        e = launch_rope_table(tq, q_off, Tq, d, lb, s);
+        if (e == hipSuccess) e = launch_rope_table(tk, kv_off, Tkv, d, lb, s);
+        if (e == hipSuccess) e = launch_rope_copy_bf16(q, qr, tq, B, Tq, H, d, s);
+        if (e == hipSuccess) e = launch_rope_copy_bf16(k, kr, tk, B, Tkv, H, d, s);
+        if (e != hipSuccess) return hip_fail(e, "rotary launch");
+    }
+    BwdCall c{};
+    c.q = rope ? qr : q; c.k = rope ? kr : k; c.v = v; c.dout = dout; c.ld2 = ld2;
+    c.dq = gq; c.dk = gk; c.dv = gv;
+    c.B = B; c.H = H; c.Tq = Tq; c.Tkv = Tkv; c.d = d; c.q_off = q_off; c.kv_off = kv_off; c.causal = causal;
+    c.kpm = kpm; c.amask = attn_mask;
+    // accumulate in the kernels only where they write the caller's buffers
+    c.flags = (flags & ATTN_NO_TILE_SKIP) | (accum && dq_direct ? ATTN_ACCUMULATE : 0u);
+    c.q_bstride = (long long)Tq * rs; c.kv_bstride = (long long)Tkv * rs; c.kpm_bstride = Tkv;
+    c.lse_bstride = (long long)H * Tq; c.lse_hstride = Tq; c.amask_stride = Tkv;
+    if (int rc = enqueue_bwd(c, list, s)) return rc;
+    // finalize: rotate back, cast, accumulate
+    const int tobf = f32 ? 0 : 1;
+    const int acc = accum ? 1 : 0;
+    if (!dq_direct) {
+        e = launch_bwd_finalize(gq, dq, rope ? tq : nullptr, B, Tq, H, d, (long long)Tq * rs, (long long)Tq * rs, tobf, acc, s);
+        if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    }
+    if (!dk_direct) {
+        e = launch_bwd_finalize(gk, dk, rope ? tk : nullptr, B, Tkv, H, d, (long long)Tkv * rs, (long long)Tkv * rs, tobf, acc, s);
+        if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    }
+    if (!dv_direct) {
+        e = launch_bwd_finalize(gv, dv, nullptr, B, Tkv, H, d, (long long)Tkv * rs, (long long)Tkv * rs, tobf, acc, s);
+        if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    }
+    return ATTN_OK;
+}
+
+int attn_ring_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int H, int T, int d, int P, int rank, int zigzag, int causal,
+                  const uint8_t* kpm, double rope_base, int dtype, unsigned flags, attn_stream_t stream) {
+    g_err.clear();
+    const int n = attn_ring_plan(T, P, rank, zigzag, causal, nullptr, 0);
+    if (n < 0) return -n;
+    const int Tl = T / P;
+    if (int rc = check_sizes(B, H, Tl, T, d)) return rc;
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass supports bf16 inputs only");
+    if (int rc = check_bf16_rows(dtype, H, d)) return rc;
+    if (flags & ~(unsigned)(ATTN_NO_TILE_SKIP | ATTN_OUT_F32))
+        return fail(ATTN_ERR_INVALID_ARG, "only ATTN_NO_TILE_SKIP and ATTN_OUT_F32 may be passed");
+    if (!(rope_base >= 0.0) || std::isinf(rope_base)) return fail(ATTN_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
+    if (B == 0 || H == 0) return ATTN_OK;
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return fail(ATTN_ERR_INVALID_ARG, "NULL pointer");
+    for (const void* ptr : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+        if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    std::vector<attn_ring_call> plan(n);
+    attn_ring_plan(T, P, rank, zigzag, causal, plan.data(), n);
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool rope = rope_base > 0.0;
+    const long long rs = (long long)H * d;
+    const size_t nq = (size_t)B * Tl * rs, nk = (size_t)B * T * rs;
+    const size_t ld_b = align_up((size_t)B * H * Tl * sizeof(float2));
+    const size_t tab_q = rope ? align_up((size_t)Tl * (d / 2) * sizeof(float2)) : 0;
+    const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(float2)) : 0;
+    const size_t qr_b = rope ? align_up(nq * 2) : 0, kr_b = rope ? align_up(nk * 2) : 0;
+    const size_t g_b = align_up(nq * 4) + 2 * align_up(nk * 4);
+    std::vector<size_t> lst_off(n, 0);
+    size_t total = ld_b + tab_q + tab_k + qr_b + kr_b + g_b;
+    for (int i = 0; i < n; ++i) {
+        lst_off[i] = total;
+        total += kpm_list_bytes(kpm ? kpm + plan[i].kv_pos0 : nullptr, dtype, flags, B, plan[i].kv_rows);
+    }
+    Scratch ws;
+    hipError_t e = ws.alloc(total, s);
+    if (e != hipSuccess) return hip_fail(e, "scratch allocation");
+    char* base = (char*)ws.ptr;
+    char* wp = base;
+    float2* ld2 = (float2*)wp; wp += ld_b;
+    float2* tq = (float2*)wp; wp += tab_q;
+    float2* tk = (float2*)wp; wp += tab_k;
+    char* qr = wp; wp += qr_b;
+    char* kr = wp; wp += kr_b;
+    float* gq = (float*)wp; wp += align_up(nq * 4);
+    float* gk = (float*)wp; wp += align_up(nk * 4);
+    float* gv = (float*)wp;
+
+    e = launch_bwd_delta(dout, out, lse, ld2, B, H, Tl, d, (long long)Tl * rs, (int)rs, (long long)H * Tl, Tl, s);
+    if (e == hipSuccess) e = launch_zero_f32(gq, (long long)nq, s);
+    if (e == hipSuccess) e = launch_zero_f32(gk, (long long)nk, s);
+    if (e == hipSuccess) e = launch_zero_f32(gv, (long long)nk, s);
+    if (e != hipSuccess) return hip_fail(e, "setup launch");
+    if (rope) {
+        const double lb = std::log(rope_base);
+        const int parts = zigzag ? 2 : 1;
+        const int c = Tl / parts;
+        for (int ph = 0; ph < parts && e == hipSuccess; ++ph) {
+            const long long pos0 = (long long)(ph == 0 ? rank : 2 * P - 1 - rank) * c;
+            e = launch_rope_table(tq + (size_t)ph * c * (d / 2), pos0, c, d, lb, s);
+        }
+        if (e == hipSuccess) e = launch_rope_table(tk, 0, T, d, lb, s);
+        if (e == hipSuccess) e = launch_rope_copy_bf16(q, qr, tq, B, Tl, H, d, s);
+        if (e == hipSuccess) e = launch_rope_copy_bf16(k, kr, tk, B, T, H, d, s);
+        if (e != hipSuccess) return hip_fail(e, "rotary launch");
+    }
+    const size_t esz = 2;
+    for (int i = 0; i < n; ++i) {
+        const attn_ring_call& pc = plan[i];
+        BwdCall c{};
+        c.q = (rope ? (const char*)qr : (const char*)q) + (size_t)pc.q_row0 * rs * esz;
+        c.k = (rope ? (const char*)kr : (const char*)k) + (size_t)pc.kv_pos0 * rs * esz;
+        c.v = (const char*)v + (size_t)pc.kv_pos0 * rs * esz;
+        c.dout = (const char*)dout + (size_t)pc.q_row0 * rs * esz;
+        c.ld2 = ld2 + pc.q_row0;
+        c.dq = gq + (size_t)pc.q_row0 * rs;
+        c.dk = gk + (size_t)pc.kv_pos0 * rs;
+        c.dv = gv + (size_t)pc.kv_pos0 * rs;
+        c.B = B; c.H = H; c.Tq = pc.q_rows; c.Tkv = pc.kv_rows; c.d = d;
+        c.q_off = pc.q_pos0; c.kv_off = pc.kv_pos0; c.causal = causal;
+        c.kpm = kpm ? kpm + pc.kv_pos0 : nullptr;
+        c.amask = nullptr;
+        c.flags = (flags & ATTN_NO_TILE_SKIP) | ATTN_ACCUMULATE;
+        c.q_bstride = (long long)Tl * rs; c.kv_bstride = (long long)T * rs; c.kpm_bstride = T;
+        c.lse_bstride = (long long)H * Tl; c.lse_hstride = Tl; c.amask_stride = 0;
+        const size_t lb = kpm_list_bytes(c.kpm, dtype, flags, B, c.Tkv);
+        if (int rc = enqueue_bwd(c, lb ? (int*)(base + lst_off[i]) : nullptr, s)) return rc;
+    }
+    const int tobf = (flags & ATTN_OUT_F32) ? 0 : 1;
+    e = launch_bwd_finalize(gq, dq, rope ? tq : nullptr, B, Tl, H, d, (long long)Tl * rs, (long long)Tl * rs, tobf, 0, s);
+    if (e == hipSuccess)
+        e = launch_bwd_finalize(gk, dk, rope ? tk : nullptr, B, T, H, d, (long long)T * rs, (long long)T * rs, tobf, 0, s);
+    if (e == hipSuccess)
+        e = launch_bwd_finalize(gv, dv, nullptr, B, T, H, d, (long long)T * rs, (long long)T * rs, tobf, 0, s);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "finalize launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,682 @@
+// Blockwise attention backward, bf16 inputs, gfx950 MFMA.
+//
+// Method (brunomaga.github.io sequence-context-parallelism post, section
+// "Ring Attention", item 3, and the backward pass of its "Implementation"):
+// gradients are computed block by block from dout, the operands, the final
+// out and the saved log-sum-exp, without the attention matrix.  With
+// P = exp(s - lse) on allowed pairs and delta_i = sum_c dout_ic out_ic:
+//   dv_j  = sum_i P_ij dout_i
+//   dS_ij = P_ij (dout_i . v_j - delta_i)
+//   dq_i  = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i
+// (q, k rotated when RoPE is on; the caller rotates dq, dk back).
+//
+// Two kernels, so that every output element has one writer and the result is
+// deterministic:
+// * dQ: 8 waves x 32 query rows per workgroup, as in the forward kernel.
+//   K tiles are read row-wise for S^T = K Q^T and transposed for
+//   dQ^T += K^T dS^T, so each K tile is loaded twice, once per LDS swizzle;
+//   the V tile serves dP^T = V dO^T.  Q and dO stay in registers.
+// * dK/dV: 4 waves x 32 keys per workgroup; K and V stay in registers as the
+//   B operands of S = Q K^T and dP = dO V^T; 32-query tiles of Q and dO
+//   (each twice, row-read and transposed swizzles) and their (lse, delta)
+//   stream through LDS.  The accumulators dK^T and dV^T keep lane = key.
+// Tiles move HBM -> LDS with buffer loads in LDS mode (out-of-range rows
+// arrive as zeros), as in the forward kernel.
+#include "tile_io.h"
+
+namespace bosa {
+namespace {
+
+template <int D>
+struct BG {
+    static constexpr int NC = D / 16;     // 16-wide d chunks (contraction over d)
+    static constexpr int NDB = D / 32;    // 32-row d blocks of a transposed accumulator
+    static constexpr int GPR = D / 8;     // 16-byte granules per row
+    static constexpr int ROW = 2 * D;     // bytes per bf16 row in LDS
+    static constexpr int RP = 256 / ROW;  // rows per 256-byte bank window
+    static constexpr int RPB = 1024 / ROW;
+    // Stored granule position = granule ^ h(row).  hk: conflict-free 16-lane
+    // row reads (ds_read_b128); hv: conflict-free transposed reads.
+    static __device__ __forceinline__ int hk(int r) { return (r / RP) % GPR; }
+    static __device__ __forceinline__ int hv(int r) { return 4 * ((r / RP) % (GPR / 4)); }
+};
+
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// A operand of a 32x32x16 MFMA holding the transpose of 16 rows x 32 columns
+// of a row-major LDS tile (rows 16 kc .. 16 kc + 15, columns 32 db ..).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const char* tile, uint32_t voff_db, int kc) {
+    const char* p0 = tile + voff_db + (16 * kc) * BG<D>::ROW;
+    const s16x4 r0 = tr_read(p0);
+    const s16x4 r1 = tr_read(p0 + 8 * BG<D>::ROW);
+    const s16x8 a = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    return __builtin_bit_cast(bf16x8, a);
+}
+
+// Per-lane byte offsets of the transposed reads for each 32-column block
+// (stored with the hv swizzle), and of the row reads of granule 2c + hh of
+// row lane % 32 (stored with the hk swizzle).
+template <int D>
+__device__ __forceinline__ void lane_offsets(int lane, uint32_t (&roff)[BG<D>::NC], uint32_t (&toff)[BG<D>::NDB]) {
+    using G = BG<D>;
+    const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) roff[c] = l32 * G::ROW + 16 * ((2 * c + hh) ^ G::hk(l32));
+    const int jj = lane & 15, grp = lane >> 4;
+    const int r0 = 4 * (grp >> 1) + (jj >> 2);
+    const int hv = G::hv(r0);
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        const int g = 4 * db + 2 * (grp & 1) + ((jj & 3) >> 1);
+        toff[db] = r0 * G::ROW + 16 * (g ^ hv) + 8 * (jj & 1);
+    }
+}
+
+// Source offset (bytes, relative to the tile's first row) of the granule a
+// lane moves into 1 KB block m of a tile stored with swizzle h.
+template <int D, bool TR>
+__device__ __forceinline__ uint32_t dma_offset(int m, int lane, uint32_t rs2) {
+    using G = BG<D>;
+    const int row = m * G::RPB + lane / G::GPR;
+    const int pos = lane % G::GPR;
+    const int h = TR ? G::hv(row) : G::hk(row);
+    return (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ h);
+}
+
+// Packed bf16 operand from accumulator registers 8 cc .. 8 cc + 7.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int cc) {
+    uint4 u;
+    u.x = pack_bf16x2(x[8 * cc + 0], x[8 * cc + 1]);
+    u.y = pack_bf16x2(x[8 * cc + 2], x[8 * cc + 3]);
+    u.z = pack_bf16x2(x[8 * cc + 4], x[8 * cc + 5]);
+    u.w = pack_bf16x2(x[8 * cc + 6], x[8 * cc + 7]);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// Workgroup renumbering for the eight XCDs (each receives a contiguous range).
+__device__ __forceinline__ int xcd_order(int bid) {
+    const int full = (int)gridDim.x & ~7;
+    return bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
+}
+
+// ============================================================== dQ
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
+    using G = BG<D>;
+    constexpr int BN = 64, NW = 8, BM = 32 * NW, NSL = 3;
+    constexpr int TILE = BN * G::ROW;        // bytes of one 64-row tile
+    constexpr int SLOT = 3 * TILE;           // K (row swizzle) | K (transposed swizzle) | V
+    constexpr int NI = TILE / 1024 / NW;     // 1 KB blocks per wave per tile copy
+    constexpr int PT = 3 * NI;               // loads per wave per tile
+    static_assert(NI >= 1 && (TILE / 1024) % NW == 0, "blocks must divide over the waves");
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    int bid = xcd_order(blockIdx.x);
+    const int qt = p.n_tiles - 1 - bid % p.n_tiles;   // heaviest causal query tiles first
+    bid /= p.n_tiles;
+    const int h = bid % p.H, b = bid / p.H;
+
+    const int rs = p.row_stride;
+    const uint32_t rs2 = 2u * (uint32_t)rs;
+    const int Tq = p.Tq, Tkv = p.Tkv;
+    const long long qrow0 = b * p.q_bstride + (long long)h * D;
+    const char* kg = (const char*)((const uint16_t*)p.k + b * p.kv_bstride + (long long)h * D);
+    const char* vg = (const char*)((const uint16_t*)p.v + b * p.kv_bstride + (long long)h * D);
+    const bool noskip = (p.flags & ATTN_NO_TILE_SKIP) != 0;
+    const bool causal = p.causal != 0;
+    const float sl2 = p.scale_log2;
+    const int q0 = qt * BM, qw0 = q0 + w * 32, qi = qw0 + l32;
+    const bool qvalid = qi < Tq, wvalid = qw0 < Tq;
+    const int qwlast = min(qw0 + 31, Tq - 1);
+    const long long delta = p.q_off - p.kv_off;
+
+    // Q and dO operands (B of S^T = K Q^T and dP^T = V dO^T): lane = query.
+    bf16x8 qreg[G::NC], oreg[G::NC];
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) {
+        uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+        if (qvalid) {
+            const long long o = qrow0 + (long long)qi * rs + 16 * c + 8 * hh;
+            x = *(const uint4*)((const uint16_t*)p.q + o);
+            y = *(const uint4*)((const uint16_t*)p.dout + o);
+        }
+        qreg[c] = __builtin_bit_cast(bf16x8, x);
+        oreg[c] = __builtin_bit_cast(bf16x8, y);
+    }
+    float2 ld = make_float2(INFINITY, 0.f);
+    if (qvalid) ld = p.ld2[b * p.lse_bstride + (long long)h * p.lse_hstride + qi];
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): only tile loads are counted below
+
+    // key tiles (as in the forward kernel)
+    const int qlast = min(q0 + BM, Tq) - 1;
+    long long nk = Tkv;
+    if (causal && !noskip) {
+        const long long lim = delta + qlast + 1;
+        nk = lim < 0 ? 0 : (lim < nk ? lim : nk);
+    }
+    const int nt = (int)((nk + BN - 1) / BN);
+    typedef const __attribute__((address_space(4))) int* cint_ptr;
+    const cint_ptr klist =
+        (p.kpm_list && !noskip) ? (cint_ptr)(p.kpm_list + (long long)b * p.kpm_list_stride) : nullptr;
+    long long nfull = Tkv / BN;
+    if (causal) {
+        const long long lim = q0 + delta + 1;
+        const long long f = lim < 0 ? 0 : lim / BN;
+        nfull = f < nfull ? f : nfull;
+    }
+    if (klist) nfull = klist[1] < nfull ? klist[1] : nfull;
+    if (noskip || p.amask || (p.kpm && !klist)) nfull = 0;
+    const int n_full = (int)(nfull < nt ? nfull : nt);
+    auto tile_at = [&](int i) -> int { return klist ? (int)((uint32_t)klist[2 + i] & ~kTileClean) : i; };
+    auto clean_at = [&](int i) -> bool { return klist ? ((uint32_t)klist[2 + i] & kTileClean) != 0 : p.kpm == nullptr; };
+    int ntiles = nt;
+    if (klist) {
+        int lo = 0, hi = klist[0];
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (tile_at(mid) < nt) lo = mid + 1;
+            else hi = mid;
+        }
+        ntiles = lo;
+    }
+    int n_act = ntiles;
+    if (!wvalid) {
+        n_act = n_full;
+    } else if (causal && !noskip) {
+        const long long lim = (long long)qwlast + delta;
+        int lo = n_full, hi = ntiles;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((long long)tile_at(mid) * BN <= lim) lo = mid + 1;
+            else hi = mid;
+        }
+        n_act = lo;
+    }
+
+    uint32_t roff[G::NC], toff[G::NDB];
+    lane_offsets<D>(lane, roff, toff);
+    uint32_t dr[NI], dt[NI];
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+        dr[n] = dma_offset<D, false>(w * NI + n, lane, rs2);
+        dt[n] = dma_offset<D, true>(w * NI + n, lane, rs2);
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+    auto slot_of = [&](int i) -> int { return __builtin_amdgcn_readfirstlane(i % NSL); };
+    auto issue = [&](int i) {
+        const int key0 = tile_at(i) * BN;
+        const uint32_t nb = (uint32_t)min(Tkv - 1 - key0, BN - 1) * rs2 + 2u * D;
+        const u32x4 rk = buffer_rsrc(kg + (long long)key0 * rs2, nb);
+        const u32x4 rv = buffer_rsrc(vg + (long long)key0 * rs2, nb);
+        const uint32_t base = lds0 + (uint32_t)slot_of(i) * SLOT + (uint32_t)(w * NI) * 1024u;
+#pragma unroll
+        for (int n = 0; n < NI; ++n) load_lds16(dr[n], rk, base + 1024u * n);
+#pragma unroll
+        for (int n = 0; n < NI; ++n) load_lds16(dt[n], rk, base + TILE + 1024u * n);
+#pragma unroll
+        for (int n = 0; n < NI; ++n) load_lds16(dr[n], rv, base + 2 * TILE + 1024u * n);
+    };
+    const uint8_t* kpm_row = p.kpm ? p.kpm + b * p.kpm_bstride : nullptr;
+    const uint8_t* am_row = (p.amask && qvalid) ? p.amask + (long long)qi * p.amask_stride : nullptr;
+    auto tile_mask = [&](int i) -> TileMask {
+        TileMask mk{63, ~0ull, nullptr};
+        const int key0 = tile_at(i) * BN;
+        long long thr = (long long)Tkv - key0 - 1;
+        if (causal) {
+            const long long c = (long long)qi + delta - key0;
+            thr = c < thr ? c : thr;
+        }
+        mk.thr4 = (int)(thr < -1 ? -1 : (thr > 63 ? 63 : thr)) - 4 * hh;
+        uint64_t km = ~0ull;
+        if (kpm_row && !clean_at(i)) {
+            const bool okk = key0 + lane < Tkv && kpm_row[key0 + lane] == 0;
+            km = __ballot(okk);
+        }
+        mk.kml = km >> (4 * hh);
+        mk.am = am_row ? am_row + key0 + 4 * hh : nullptr;
+        return mk;
+    };
+
+    f32x16 acc[G::NDB];
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) acc[db] = f32x16{};
+
+    if (ntiles > 0) issue(0);
+    if (ntiles > 1) {
+        issue(1);
+        wait_barrier<PT>();
+    } else {
+        wait_barrier<0>();
+    }
+    for (int i = 0; i < ntiles; ++i) {
+        const bool more = i + 2 < ntiles;
+        if (more) issue(i + 2);
+        if (i < n_act) {
+            const char* St = smem + slot_of(i) * SLOT;
+            f32x16 s0 = f32x16{}, s1 = f32x16{}, d0 = f32x16{}, d1 = f32x16{};
+#pragma unroll
+            for (int c = 0; c < G::NC; ++c) {
+                const bf16x8 k0 = *(const bf16x8*)(St + roff[c]);
+                const bf16x8 k1 = *(const bf16x8*)(St + roff[c] + 32 * G::ROW);
+                const bf16x8 v0 = *(const bf16x8*)(St + 2 * TILE + roff[c]);
+                const bf16x8 v1 = *(const bf16x8*)(St + 2 * TILE + roff[c] + 32 * G::ROW);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[c], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[c], s1, 0, 0, 0);
+                d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, oreg[c], d0, 0, 0, 0);
+                d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, oreg[c], d1, 0, 0, 0);
+            }
+            if (i >= n_full) apply_mask(s0, s1, tile_mask(i));
+            // dS^T = P^T (dP^T - delta), P^T = exp2(s sl2 - lse2); lane = query
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p0 = hw_exp2(fmaf(s0[r], sl2, -ld.x));
+                const float p1 = hw_exp2(fmaf(s1[r], sl2, -ld.x));
+                s0[r] = p0 * (d0[r] - ld.y);
+                s1[r] = p1 * (d1[r] - ld.y);
+            }
+            bf16x8 ds[4];
+            ds[0] = pack8(s0, 0);
+            ds[1] = pack8(s0, 1);
+            ds[2] = pack8(s1, 0);
+            ds[3] = pack8(s1, 1);
+            // dQ^T += K^T dS^T: A = K^T from the transposed-swizzle copy
+#pragma unroll
+            for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(St + TILE, toff[db], kc), ds[kc],
+                                                                      acc[db], 0, 0, 0);
+        }
+        if (more) wait_barrier<PT>();
+        else wait_barrier<0>();
+    }
+
+    if (!qvalid) return;
+    float* og = p.dq + b * p.q_bstride + (long long)qi * rs + (long long)h * D;
+    const bool accum = (p.flags & ATTN_ACCUMULATE) != 0;
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float4* dst = (float4*)(og + db * 32 + 8 * g + 4 * hh);
+            float4 r = make_float4(acc[db][4 * g + 0] * p.scale, acc[db][4 * g + 1] * p.scale,
+                                   acc[db][4 * g + 2] * p.scale, acc[db][4 * g + 3] * p.scale);
+            if (accum) {
+                const float4 a = *dst;
+                r.x += a.x;
+                r.y += a.y;
+                r.z += a.z;
+                r.w += a.w;
+            }
+            *dst = r;
+        }
+    }
+}
+
+// ============================================================== dK, dV
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
+    using G = BG<D>;
+    constexpr int NW = 4, BK = 32 * NW, BQ = 32, NSL = 4;
+    constexpr int QTILE = BQ * G::ROW;           // bytes of one 32-row tile
+    constexpr int LDO = 4 * QTILE;               // (lse2, delta) of the tile after the four copies
+    constexpr int SLOT = 4 * QTILE + 256;        // Q | Q^T | dO | dO^T | 32 x float2
+    constexpr int NI = QTILE / 1024 / NW;
+    constexpr int PT = 4 * NI + 1;
+    static_assert(NI >= 1 && (QTILE / 1024) % NW == 0, "blocks must divide over the waves");
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    int bid = xcd_order(blockIdx.x);
+    const int kt = bid % p.n_tiles;   // low key tiles see the most queries under causal order
+    bid /= p.n_tiles;
+    const int h = bid % p.H, b = bid / p.H;
+
+    const int rs = p.row_stride;
+    const uint32_t rs2 = 2u * (uint32_t)rs;
+    const int Tq = p.Tq, Tkv = p.Tkv;
+    const bool causal = p.causal != 0;
+    const bool noskip = (p.flags & ATTN_NO_TILE_SKIP) != 0;
+    const float sl2 = p.scale_log2;
+    const long long delta = p.q_off - p.kv_off;   // key j allowed for query i iff j - i <= delta
+    const int k0 = kt * BK, kw0 = k0 + 32 * w, kj = kw0 + l32;
+    const bool kvalid = kj < Tkv;
+    const bool kmasked = p.kpm && kvalid && p.kpm[b * p.kpm_bstride + kj] != 0;
+
+    // K and V operands (B of S = Q K^T and dP = dO V^T): lane = key.
+    bf16x8 kreg[G::NC], vreg[G::NC];
+    const long long krow = b * p.kv_bstride + (long long)kj * rs + (long long)h * D;
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) {
+        uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+        if (kvalid) {
+            x = *(const uint4*)((const uint16_t*)p.k + krow + 16 * c + 8 * hh);
+            y = *(const uint4*)((const uint16_t*)p.v + krow + 16 * c + 8 * hh);
+        }
+        kreg[c] = __builtin_bit_cast(bf16x8, x);
+        vreg[c] = __builtin_bit_cast(bf16x8, y);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    // Query tiles: from the first that can see key k0 to the end.
+    const int nqt = (Tq + BQ - 1) / BQ;
+    int t0 = 0;
+    if (causal && !noskip) {
+        const long long first = (long long)k0 - delta;   // first query that sees key k0
+        t0 = first <= 0 ? 0 : (first >= Tq ? nqt : (int)(first / BQ));
+    }
+    // This wave: tiles before tw0 cannot see its keys; from tf on every pair is allowed.
+    int tw0 = t0, tf = 0;
+    {
+        const long long first = (long long)kw0 - delta;
+        if (causal && !noskip) tw0 = first <= 0 ? 0 : (first >= Tq ? nqt : (int)(first / BQ));
+        const long long full = (long long)kw0 + 31 - delta;   // first query seeing all 32 keys
+        tf = !causal ? 0 : (full <= 0 ? 0 : (int)((full + BQ - 1) / BQ));
+        if (p.amask || noskip) tf = nqt;
+    }
+    const bool wactive = kw0 < Tkv;
+    const int tail = Tq % BQ ? nqt - 1 : nqt;   // a partial last tile needs the row test
+
+    uint32_t roff[G::NC], toff[G::NDB];
+    lane_offsets<D>(lane, roff, toff);
+    uint32_t dr[NI], dt[NI];
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+        dr[n] = dma_offset<D, false>(w * NI + n, lane, rs2);
+        dt[n] = dma_offset<D, true>(w * NI + n, lane, rs2);
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+    const char* qg = (const char*)((const uint16_t*)p.q + b * p.q_bstride + (long long)h * D);
+    const char* og = (const char*)((const uint16_t*)p.dout + b * p.q_bstride + (long long)h * D);
+    const float2* ldg = p.ld2 + b * p.lse_bstride + (long long)h * p.lse_hstride;
+    auto slot_of = [&](int t) -> int { return __builtin_amdgcn_readfirstlane(t % NSL); };
+    auto issue = [&](int t) {
+        const int qa = t * BQ;
+        const uint32_t nb = (uint32_t)min(Tq - 1 - qa, BQ - 1) * rs2 + 2u * D;
+        const u32x4 rq = buffer_rsrc(qg + (long long)qa * rs2, nb);
+        const u32x4 ro = buffer_rsrc(og + (long long)qa * rs2, nb);
+        const uint32_t slot = lds0 + (uint32_t)slot_of(t) * SLOT;
+        const uint32_t base = slot + (uint32_t)(w * NI) * 1024u;
+#pragma unroll
+        for (int n = 0; n < NI; ++n) load_lds16(dr[n], rq, base + 1024u * n);
+#pragma unroll
+        for (int n = 0; n < NI; ++n) load_lds16(dt[n], rq, base + QTILE + 1024u * n);
+#pragma unroll
+        for (int n = 0; n < NI; ++n) load_lds16(dr[n], ro, base + 2 * QTILE + 1024u * n);
+#pragma unroll
+        for (int n = 0; n < NI; ++n) load_lds16(dt[n], ro, base + 3 * QTILE + 1024u * n);
+        // (lse2, delta) of the 32 rows: 64 floats, 16 per wave
+        const u32x4 rl = buffer_rsrc(ldg + qa, (uint32_t)min(Tq - qa, BQ) * 8u);
+        if (lane < 16) load_lds4((uint32_t)(16 * w + lane) * 4u, rl, slot + LDO + 64u * w);
+    };
+
+    f32x16 dk[G::NDB], dv[G::NDB];
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+
+    const int ntl = nqt - t0;   // tiles this workgroup visits
+    if (ntl > 0) issue(t0);
+    if (ntl > 1) issue(t0 + 1);
+    if (ntl > 2) {
+        issue(t0 + 2);
+        wait_barrier<2 * PT>();
+    } else if (ntl > 1) {
+        wait_barrier<PT>();
+    } else {
+        wait_barrier<0>();
+    }
+    for (int t = t0; t < nqt; ++t) {
+        const bool more = t + 3 < nqt;
+        if (more) issue(t + 3);
+        if (wactive && t >= tw0) {
+            const char* St = smem + slot_of(t) * SLOT;
+            // S = Q K^T and dP = dO V^T: lane = key, register r = query 8 (r/4) + 4 hh + r%4
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int c = 0; c < G::NC; ++c) {
+                const bf16x8 a = *(const bf16x8*)(St + roff[c]);
+                const bf16x8 o = *(const bf16x8*)(St + 2 * QTILE + roff[c]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[c], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, vreg[c], dp, 0, 0, 0);
+            }
+            if (t < tf || t >= tail) {
+                // causal order, rows past Tq, attention mask
+                const int qa = t * BQ;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qi = qa + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    bool ok = qi < Tq && (!causal || (long long)kj - qi <= delta);
+                    if (p.amask && ok && kvalid) ok = p.amask[(long long)qi * p.amask_stride + kj] == 0;
+                    s[r] = ok ? s[r] : -INFINITY;
+                }
+            }
+            // (lse2, delta) of rows 8 j + 4 hh + 0..3: two 16-byte reads per j
+            const float4* lp = (const float4*)(St + LDO);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 a = lp[4 * j + 2 * hh];       // rows 8j+4hh, +1
+                const float4 c = lp[4 * j + 2 * hh + 1];   // rows 8j+4hh+2, +3
+                const float l2[4] = {a.x, a.z, c.x, c.z};
+                const float dl[4] = {a.y, a.w, c.y, c.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * j + e;
+                    const float pr = hw_exp2(fmaf(s[r], sl2, -l2[e]));
+                    s[r] = pr;
+                    dp[r] = pr * (dp[r] - dl[e]);
+                }
+            }
+            const bf16x8 pp[2] = {pack8(s, 0), pack8(s, 1)};
+            const bf16x8 ps[2] = {pack8(dp, 0), pack8(dp, 1)};
+            // dV^T += dO^T P and dK^T += Q^T dS (A operands transposed from LDS)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int db = 0; db < G::NDB; ++db) {
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(St + 3 * QTILE, toff[db], kc),
+                                                                     pp[kc], dv[db], 0, 0, 0);
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(St + QTILE, toff[db], kc),
+                                                                     ps[kc], dk[db], 0, 0, 0);
+                }
+        }
+        if (t + 3 < nqt) wait_barrier<2 * PT>();
+        else if (t + 2 < nqt) wait_barrier<PT>();
+        else wait_barrier<0>();
+    }
+
+    if (!kvalid) return;
+    const long long orow = b * p.kv_bstride + (long long)kj * rs + (long long)h * D;
+    const bool accum = (p.flags & ATTN_ACCUMULATE) != 0;
+    // A key excluded by the key-padding mask gets exactly zero (its lane may
+    // hold anything: its scores were not masked, since they reach no other key).
+    const float ks = p.scale;
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float4* pk = (float4*)(p.dk + orow + db * 32 + 8 * g + 4 * hh);
+            float4* pv = (float4*)(p.dv + orow + db * 32 + 8 * g + 4 * hh);
+            float4 rk = make_float4(dk[db][4 * g] * ks, dk[db][4 * g + 1] * ks, dk[db][4 * g + 2] * ks,
+                                    dk[db][4 * g + 3] * ks);
+            float4 rv = make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+            if (kmasked) {
+                rk = make_float4(0.f, 0.f, 0.f, 0.f);
+                rv = rk;
+            }
+            if (accum) {
+                const float4 a = *pk, c = *pv;
+                rk.x += a.x; rk.y += a.y; rk.z += a.z; rk.w += a.w;
+                rv.x += c.x; rv.y += c.y; rv.z += c.z; rv.w += c.w;
+            }
+            *pk = rk;
+            *pv = rv;
+        }
+    }
+}
+
+// ============================================================== helpers
+// ld2 = (lse log2 e, or +inf for an empty row; delta = sum_c dout out): one
+// 16-lane group per (row, head).
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ out,
+                                                        const float* __restrict__ lse, float2* __restrict__ ld2, int B,
+                                                        int H, int Tq, int d, long long bstride, int row_stride,
+                                                        long long lse_bstride, int lse_hstride) {
+    const long long gid = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 4;   // (b, t, h)
+    const int sub = threadIdx.x & 15;
+    const long long rows = (long long)B * Tq * H;
+    if (gid >= rows) return;
+    const int h = (int)(gid % H);
+    const long long bt = gid / H;
+    const int t = (int)(bt % Tq), b = (int)(bt / Tq);
+    const long long base = b * bstride + (long long)t * row_stride + (long long)h * d;
+    float acc = 0.f;
+    for (int c = sub * 8; c < d; c += 128) {
+        const uint4 x = *(const uint4*)(dout + base + c);
+        const uint4 y = *(const uint4*)(out + base + c);
+        acc = fmaf(bf16_lo(x.x), bf16_lo(y.x), acc);
+        acc = fmaf(bf16_hi(x.x), bf16_hi(y.x), acc);
+        acc = fmaf(bf16_lo(x.y), bf16_lo(y.y), acc);
+        acc = fmaf(bf16_hi(x.y), bf16_hi(y.y), acc);
+        acc = fmaf(bf16_lo(x.z), bf16_lo(y.z), acc);
+        acc = fmaf(bf16_hi(x.z), bf16_hi(y.z), acc);
+        acc = fmaf(bf16_lo(x.w), bf16_lo(y.w), acc);
+        acc = fmaf(bf16_hi(x.w), bf16_hi(y.w), acc);
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 16);
+    if (sub == 0) {
+        const long long li = b * lse_bstride + (long long)h * lse_hstride + t;
+        const float l = lse[li];
+        ld2[li] = make_float2(l == -INFINITY ? INFINITY : l * kLog2e, acc);
+    }
+}
+
+// dst = (accumulate ? dst : 0) + R(-pos) src per coordinate pair, pos from
+// the table row of the token (tab[t][pair] = cos, sin of +pos); tab == null:
+// no rotation.  One thread per pair.
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restrict__ src, void* __restrict__ dst,
+                                                           const float2* __restrict__ tab, int B, int T, int H, int d,
+                                                           long long src_bstride, long long dst_bstride, int accumulate) {
+    const long long pid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int half = d / 2;
+    const long long npairs = (long long)B * T * H * half;
+    if (pid >= npairs) return;
+    const int pr = (int)(pid % half);
+    long long r = pid / half;
+    const int h = (int)(r % H);
+    r /= H;
+    const int t = (int)(r % T), b = (int)(r / T);
+    const long long rowoff = (long long)t * H * d + (long long)h * d + 2 * pr;
+    const float2 x = *(const float2*)(src + b * src_bstride + rowoff);
+    float2 y = x;
+    if (tab) {
+        const float2 cs = tab[(long long)t * half + pr];
+        y = rot_pair(x.x, x.y, cs.x, -cs.y);
+    }
+    if (BF16) {
+        uint32_t* o = (uint32_t*)((uint16_t*)dst + b * dst_bstride + rowoff);
+        *o = pack_bf16x2(y.x, y.y);
+    } else {
+        float2* o = (float2*)((float*)dst + b * dst_bstride + rowoff);
+        if (accumulate) {
+            const float2 a = *o;
+            y.x += a.x;
+            y.y += a.y;
+        }
+        *o = y;
+    }
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float4* __restrict__ x, long long n4) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n4) x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+inline unsigned grid_for(long long n, int block) { return (unsigned)((n + block - 1) / block); }
+
+template <int D>
+hipError_t launch_dq(const BwdParams& p, hipStream_t s) {
+    constexpr int BM = 256, LDS = 3 * 3 * 64 * 2 * D;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    BwdParams q = p;
+    q.n_tiles = (p.Tq + BM - 1) / BM;
+    const long long grid = (long long)q.n_tiles * p.H * p.B;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)grid), dim3(512), LDS, s, q);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dkdv(const BwdParams& p, hipStream_t s) {
+    constexpr int BK = 128, LDS = 4 * (4 * 32 * 2 * D + 256);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    BwdParams q = p;
+    q.n_tiles = (p.Tkv + BK - 1) / BK;
+    const long long grid = (long long)q.n_tiles * p.H * p.B;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(256), LDS, s, q);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t s) {
+    return d == 128 ? launch_dq<128>(p, s) : launch_dq<64>(p, s);
+}
+
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t s) {
+    return d == 128 ? launch_dkdv<128>(p, s) : launch_dkdv<64>(p, s);
+}
+
+hipError_t launch_bwd_delta(const void* dout, const void* out, const float* lse, float2* ld2, int B, int H, int Tq,
+                            int d, long long bstride, int row_stride, long long lse_bstride, int lse_hstride,
+                            hipStream_t s) {
+    const long long threads = (long long)B * Tq * H * 16;
+    if (threads == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3(grid_for(threads, 256)), dim3(256), 0, s, (const uint16_t*)dout,
+                       (const uint16_t*)out, lse, ld2, B, H, Tq, d, bstride, row_stride, lse_bstride, lse_hstride);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_finalize(const float* src, void* dst, const float2* tab, int B, int T, int H, int d,
+                               long long src_bstride, long long dst_bstride, int dst_bf16, int accumulate,
+                               hipStream_t s) {
+    const long long n = (long long)B * T * H * (d / 2);
+    if (n == 0) return hipSuccess;
+    if (dst_bf16)
+        hipLaunchKernelGGL(bwd_finalize_kernel<true>, dim3(grid_for(n, 256)), dim3(256), 0, s, src, dst, tab, B, T, H,
+                           d, src_bstride, dst_bstride, 0);
+    else
+        hipLaunchKernelGGL(bwd_finalize_kernel<false>, dim3(grid_for(n, 256)), dim3(256), 0, s, src, dst, tab, B, T,
+                           H, d, src_bstride, dst_bstride, accumulate);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float* x, long long n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const long long n4 = n / 4;   // callers pass multiples of 4 (d is 64 or 128)
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, s, (float4*)x, n4);
+    return hipGetLastError();
+}
+
+}  // namespace bosa

@@ -109,6 +109,35 @@ struct FwdParams {
     int n_qtiles;
 };
 
+// One attention backward launch (bf16 inputs, float32 outputs).  q and k are
+// the operands as the forward multiplied them (rotated when RoPE is on); the
+// gradients dq and dk come out in that rotated frame.  Strides in elements.
+struct BwdParams {
+    const void* q;             // (B, Tq, H, d)
+    const void* k;             // (B, Tkv, H, d)
+    const void* v;
+    const void* dout;          // (B, Tq, H, d)
+    const float2* ld2;         // (B, H, Tq): (lse * log2 e, or +inf for a row with no allowed key; delta)
+    float* dq;                 // (B, Tq, H, d) float32
+    float* dk;                 // (B, Tkv, H, d) float32
+    float* dv;
+    const uint8_t* kpm;
+    const uint8_t* amask;
+    const int* kpm_list;       // live key tiles (dq kernel), as for the forward, or null
+    long long q_bstride, kv_bstride, kpm_bstride, lse_bstride;
+    int row_stride;            // H * d
+    int lse_hstride;
+    int amask_stride;
+    int kpm_list_stride;
+    int B, H, Tq, Tkv;
+    long long q_off, kv_off;
+    int causal;
+    unsigned flags;            // ATTN_ACCUMULATE: add into dq / dk / dv; ATTN_NO_TILE_SKIP
+    float scale_log2;          // log2(e) / sqrt(d)
+    float scale;               // 1 / sqrt(d)
+    int n_tiles;               // query tiles (dq kernel) or key tiles (dk/dv kernel) per (b, h)
+};
+
 // Entry of a live-tile list: tile index, top bit set when no key of the tile is masked.
 constexpr uint32_t kTileClean = 0x80000000u;
 
@@ -126,6 +155,18 @@ hipError_t launch_rope_apply(void* x, const long long* pos, double log_base, int
                              int is_bf16, hipStream_t s);
 hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
                                  hipStream_t s);
+hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t s);
+// ld2[b][h][i] = (lse * log2 e or +inf when lse = -inf, sum_c dout * out) for bf16 dout, out.
+hipError_t launch_bwd_delta(const void* dout, const void* out, const float* lse, float2* ld2, int B, int H, int Tq,
+                            int d, long long bstride, int row_stride, long long lse_bstride, int lse_hstride,
+                            hipStream_t s);
+// dst (float32 or bf16, optionally += ) = src rotated back by -pos (tab: cos/sin of +pos, or null for no
+// rotation); src, dst (B, T, H, d) with batch strides in elements.
+hipError_t launch_bwd_finalize(const float* src, void* dst, const float2* tab, int B, int T, int H, int d,
+                               long long src_bstride, long long dst_bstride, int dst_bf16, int accumulate,
+                               hipStream_t s);
+hipError_t launch_zero_f32(float* x, long long n, hipStream_t s);
 hipError_t launch_fill_empty(void* out, int out_bf16, float* lse, int B, int H, int rows, int d, long long o_bstride,
                              int row_stride, long long lse_bstride, int lse_hstride, hipStream_t s);
 

@@ -196,9 +196,70 @@ int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float*
                   attn_stream_t stream);
 
 /*
+ * attn_bwd -- attention backward: gradients of L = sum(dout * out) for the
+ * attn_fwd call with the same q, k, v, positions, masks and rotary base.
+ *
+ * Follows the backward pass of the brunomaga.github.io post ("Ring Attention",
+ * item 3: gradients computed blockwise, never storing the attention matrix;
+ * "Implementation": each ring step computes the block gradients of the local
+ * queries against the current K/V block from dout, q, k, v, the final out and
+ * the saved log-sum-exp; dq accumulates locally, dk and dv accumulate with
+ * their block).  With P = exp(s - lse) on allowed pairs and
+ * delta_i = sum_c dout_ic out_ic:  dv_j = sum_i P_ij dout_i,
+ * dS_ij = P_ij (dout_i . v_j - delta_i),  dq_i = sum_j dS_ij k_j / sqrt(d),
+ * dk_j = sum_i dS_ij q_i / sqrt(d), with q, k rotated when rope_base > 0 and
+ * dq, dk rotated back (the rotation is orthogonal).
+ *
+ *  q, dout, out  device (B, Tq, H, d) bf16; out is the final forward output.
+ *  k, v          device (B, Tkv, H, d) bf16.
+ *  lse           device float32 (B, H, Tq): the forward's log-sum-exp over
+ *                every key the rows see (not a block partial).
+ *  dq            device (B, Tq, H, d); dk, dv device (B, Tkv, H, d): bf16,
+ *                or float32 with ATTN_OUT_F32.  ATTN_ACCUMULATE (needs
+ *                ATTN_OUT_F32) adds the gradients into dq, dk and dv instead
+ *                of overwriting them, as a ring step does with its
+ *                accumulators.
+ *  dtype         ATTN_BF16 only (ATTN_ERR_UNSUPPORTED otherwise).
+ *  flags         ATTN_ACCUMULATE | ATTN_OUT_F32 | ATTN_NO_TILE_SKIP.
+ *  Rows with no allowed key contribute nothing; keys with kpm set get zero
+ *  gradients.  Results are deterministic (every output element is written by
+ *  one workgroup).  Scratch (rotated q and k, float32 gradients, the
+ *  per-row (lse, delta)) is allocated and freed on `stream`.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv,
+             int B, int H, int Tq, int Tkv, int d, long long q_off, long long kv_off, int causal,
+             const uint8_t* kpm, const uint8_t* attn_mask, double rope_base, int dtype, unsigned flags,
+             attn_stream_t stream);
+
+/*
+ * attn_ring_bwd -- backward of a rank's ring share (the inverse of
+ * attn_ring_fwd): the sub-calls of attn_ring_plan, each computing the block
+ * gradients of the local rows against one K/V block, with dq accumulated over
+ * the blocks and dk, dv accumulated at the block's absolute positions (the
+ * pages rotate these accumulators with their block; one device holds them in
+ * place).  The rotation back and the cast happen once at the end.
+ *
+ *  q, out, dout  device (B, T/P, H, d) bf16, local rows in local order.
+ *  lse           device float32 (B, H, T/P) from attn_ring_fwd.
+ *  k, v          device (B, T, H, d) bf16, every block at its position.
+ *  dq            device (B, T/P, H, d); dk, dv device (B, T, H, d): bf16, or
+ *                float32 with ATTN_OUT_F32.  dk and dv receive this rank's
+ *                contributions only (keys no local row sees get 0).
+ *  flags         ATTN_OUT_F32 | ATTN_NO_TILE_SKIP.  Other arguments as
+ *                attn_ring_fwd.
+ */
+int attn_ring_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv,
+                  int B, int H, int T, int d, int P, int rank, int zigzag, int causal,
+                  const uint8_t* kpm, double rope_base, int dtype, unsigned flags,
+                  attn_stream_t stream);
+
+/*
  * Kernel timing for measurement tools.  Between attn_profile_start and
- * attn_profile_stop, every attention-kernel launch made by attn_fwd or
- * attn_ring_fwd on the calling thread is bracketed by a pair of HIP events
+ * attn_profile_stop, every attention-kernel launch made by attn_fwd,
+ * attn_ring_fwd, attn_bwd or attn_ring_bwd on the calling thread (for the
+ * backward: the dQ and the dK/dV kernel) is bracketed by a pair of HIP events
  * recorded on the launch's own stream (at most max_launches launches; later
  * ones are not timed).  attn_profile_stop waits for those events, writes the
  * duration of each timed launch in milliseconds to ms[0 .. min(n, cap)) (host
