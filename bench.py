@@ -38,6 +38,7 @@ import blockwise_online_softmax_attn_amd as bosa  # noqa: E402
 import workloads  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s and % of MFMA bf16 peak (causal, d=128) on 1 MI355X"
+METRIC_BWD = "attention bwd TFLOP/s and % of MFMA bf16 peak (causal, d=128) on 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json")
@@ -132,10 +133,40 @@ def make_step(w, plan, dev_inputs):
     return step, 1
 
 
+def make_bwd_step(w, plan, dev_inputs):
+    """The backward of the same share: forward once (untimed) for out and lse,
+    then each step runs attn_ring_bwd (or attn_bwd) on a fixed dout."""
+    dq, dk, dv, dkpm = dev_inputs
+    chunks = None
+    if plan is not None:
+        firsts = {}
+        for c in plan:
+            firsts.setdefault(c.q_row0, c.q_pos0)
+        chunks = [firsts[r] // w.chunk for r in sorted(firsts)]
+    dout = workloads.draw_tokens(w, 4, chunks if chunks is not None else range(w.n_chunks)).to(dq.device)
+    if plan is not None:
+        out, lse = bosa.attn_ring_fwd(dq, dk, dv, P=w.ring_P, rank=w.ring_rank, zigzag=w.zigzag, causal=w.causal,
+                                      kpm=dkpm, rope_base=w.rope_base)
+        g = [torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)]
+
+        def step():
+            bosa.attn_ring_bwd(dq, dk, dv, out, dout, lse, P=w.ring_P, rank=w.ring_rank, zigzag=w.zigzag,
+                               causal=w.causal, kpm=dkpm, rope_base=w.rope_base, dq=g[0], dk=g[1], dv=g[2])
+        return step, 2 * len(plan), dout.cpu()
+    out, lse = bosa.attn_fwd(dq, dk, dv, causal=w.causal, kpm=dkpm, rope_base=w.rope_base)
+    g = [torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)]
+
+    def step():
+        bosa.attn_bwd(dq, dk, dv, out, dout, lse, g[0], g[1], g[2], causal=w.causal, kpm=dkpm,
+                      rope_base=w.rope_base)
+    return step, 2, dout.cpu()
+
+
 # ---------------------------------------------------------------- CPU baseline
-def cpu_baseline(w, host_inputs, rows: int, heads: int):
+def cpu_baseline(w, host_inputs, rows: int, heads: int, dout=None):
     """The fp64 oracle, as it stands, on the heaviest `rows` local query rows
-    of the first `heads` heads against every key (bounded sample)."""
+    of the first `heads` heads against every key (bounded sample); the
+    backward oracle instead when dout is given."""
     import threadpoolctl
 
     import oracle
@@ -147,8 +178,13 @@ def cpu_baseline(w, host_inputs, rows: int, heads: int):
     info = threadpoolctl.threadpool_info()
     blas_threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     t0 = time.perf_counter()
-    oracle.sdpa(qs, ks, vs, qpos[sel], np.arange(w.T), causal=w.causal,
-                kpm=None if kpm is None else kpm.numpy(), rope_base=w.rope_base, dtype=w.dtype)
+    if dout is None:
+        oracle.sdpa(qs, ks, vs, qpos[sel], np.arange(w.T), causal=w.causal,
+                    kpm=None if kpm is None else kpm.numpy(), rope_base=w.rope_base, dtype=w.dtype)
+    else:
+        oracle.sdpa_backward(qs, ks, vs, dout[:, sel, :heads].double().numpy(), qpos[sel], np.arange(w.T),
+                             causal=w.causal, kpm=None if kpm is None else kpm.numpy(), rope_base=w.rope_base,
+                             dtype=w.dtype)
     dt = time.perf_counter() - t0
     pairs = 0
     for b in range(w.B):
@@ -156,7 +192,7 @@ def cpu_baseline(w, host_inputs, rows: int, heads: int):
         for p in qpos[sel]:
             lim = min(int(p) + 1, w.T) if w.causal else w.T
             pairs += lim if valid is None else int(valid[:lim].sum())
-    flops = 4.0 * w.d * pairs * heads
+    flops = (8.0 if dout is not None else 4.0) * w.d * pairs * heads
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -164,7 +200,8 @@ def cpu_baseline(w, host_inputs, rows: int, heads: int):
         "kind": "oracle",
         "sample": (f"{rows} query rows (local rows {sel[0]}..{sel[-1]}, positions {int(qpos[sel[0]])}.."
                    f"{int(qpos[sel[-1]])}) x {heads} of {w.H} heads x B={w.B} against all {w.T} keys, "
-                   f"{'causal' if w.causal else 'non-causal'}{', RoPE' if w.rope_base else ''}: "
+                   f"{'causal' if w.causal else 'non-causal'}{', RoPE' if w.rope_base else ''}"
+                   f"{' (backward: dq, dk, dv)' if dout is not None else ''}: "
                    f"{flops:.3e} algorithmic FLOPs in {dt:.2f} s (float64 numpy, BLAS threads={blas_threads}, "
                    f"host cpus={os.cpu_count()})"),
     }
@@ -220,6 +257,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward share (default, the headline metric) or its backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--cpu-heads", type=int, default=4)
@@ -245,9 +284,20 @@ def main() -> int:
     w = workloads.WORKLOADS[args.workload]
     log(f"workload {w.name}: drawing inputs")
     plan, host, dev = build_inputs(w)
-    step, launches = make_step(w, plan, dev)
+    bwd = args.which == "bwd"
+    if bwd and w.dtype != "bf16":
+        print("the backward pass takes bf16 inputs", file=sys.stderr)
+        return 2
+    dout_host = None
+    if bwd:
+        step, launches, dout_host = make_bwd_step(w, plan, dev)
+    else:
+        step, launches = make_step(w, plan, dev)
     pairs = step_pairs(w, plan, host[3])
-    flops = 4.0 * w.d * pairs
+    # algorithmic FLOPs: forward S = Q K^T and P V, 2 d each per allowed pair;
+    # backward dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q (the scores
+    # the kernels recompute are not counted)
+    flops = (8.0 if bwd else 4.0) * w.d * pairs
     log(f"{pairs} allowed pairs/step = {flops:.4e} FLOPs; {launches} attention launches/step; warmup {args.warmup}")
     if args.copy_calibration_mib:
         # a plain copy of known size through the library's float32 copy kernel:
@@ -280,7 +330,7 @@ def main() -> int:
         f"{achieved:.1f} TFLOP/s over {n_launch} launches (avg {kern_ms / max(n_launch, 1):.4f} ms)")
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if not bwd and os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_sources_sha256") == kernel_sources_sha() and tr.get("workload") == w.name:
@@ -292,8 +342,9 @@ def main() -> int:
         "unit": "TFLOP/s",
         "frac": (achieved / peak) if achieved else None,
         "traffic": traffic,
-        "kernel": "attn_fwd_bf16_kernel<128>" if (w.dtype == "bf16" and w.d == 128) else
-                  ("attn_fwd_bf16_kernel<64>" if w.dtype == "bf16" else f"attn_fwd_f32_kernel<{w.d}>"),
+        "kernel": (f"bwd_dq_kernel<{w.d}> + bwd_dkdv_kernel<{w.d}>" if bwd else
+                   "attn_fwd_bf16_kernel<128>" if (w.dtype == "bf16" and w.d == 128) else
+                   ("attn_fwd_bf16_kernel<64>" if w.dtype == "bf16" else f"attn_fwd_f32_kernel<{w.d}>")),
         "launches": n_launch,
         "avg_launch_ms": kern_ms / max(n_launch, 1),
         "flops_per_launch": flops * args.steps / max(n_launch, 1),
@@ -301,10 +352,10 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows x {args.cpu_heads} heads")
-        cpu = cpu_baseline(w, host, args.cpu_rows, args.cpu_heads)
+        cpu = cpu_baseline(w, host, args.cpu_rows // 2 if bwd else args.cpu_rows, args.cpu_heads, dout_host)
         log(f"cpu baseline {cpu['value']:.3e} TFLOP/s")
     line = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -322,6 +373,7 @@ def main() -> int:
             "causal": w.causal, "rope_base": w.rope_base, "kpm_len_range": w.kpm_len_range,
             "ring_P": w.ring_P, "ring_rank": w.ring_rank, "zigzag": w.zigzag,
             "attention_launches_per_step": launches, "algorithmic_flops_per_step": flops,
+            "pass": args.which,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -16,10 +16,12 @@
 //   K tiles are read row-wise for S^T = K Q^T and transposed for
 //   dQ^T += K^T dS^T, so each K tile is loaded twice, once per LDS swizzle;
 //   the V tile serves dP^T = V dO^T.  Q and dO stay in registers.
-// * dK/dV: 4 waves x 32 keys per workgroup; K and V stay in registers as the
-//   B operands of S = Q K^T and dP = dO V^T; 32-query tiles of Q and dO
-//   (each twice, row-read and transposed swizzles) and their (lse, delta)
-//   stream through LDS.  The accumulators dK^T and dV^T keep lane = key.
+// * dK/dV: 128 keys per workgroup, each 32-key block shared by two waves (one
+//   computes P and dV, the other dP, dS and dK, with P passed through LDS);
+//   K and V stay in registers as the B operands of S = Q K^T and dP = dO V^T;
+//   32-query tiles of Q and dO (each twice, row-read and transposed
+//   swizzles) and their (lse, delta) stream through LDS.  The accumulators
+//   dK^T and dV^T keep lane = key.
 // Tiles move HBM -> LDS with buffer loads in LDS mode (out-of-range rows
 // arrive as zeros), as in the forward kernel.
 #include "tile_io.h"
@@ -318,21 +320,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ============================================================== dK, dV
+// 8 waves, 128 keys per workgroup.  The 32-key block kb = w % 4 is shared by
+// two waves: wave A (w < 4) computes S = Q K^T, P and dV^T += dO^T P; wave B
+// (w >= 4) computes dP = dO V^T, dS = P (dP - delta) and dK^T += Q^T dS,
+// taking P (float32) from wave A through LDS.  Each wave holds one operand
+// (K or V) and one accumulator (dV^T or dK^T), so two waves fit per SIMD;
+// waves w and w + 4 share a SIMD, one of each role.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     using G = BG<D>;
-    constexpr int NW = 4, BK = 32 * NW, BQ = 32, NSL = 4;
+    constexpr int NW = 8, BK = 128, BQ = 32, NSL = 4;
     constexpr int QTILE = BQ * G::ROW;           // bytes of one 32-row tile
     constexpr int LDO = 4 * QTILE;               // (lse2, delta) of the tile after the four copies
     constexpr int SLOT = 4 * QTILE + 256;        // Q | Q^T | dO | dO^T | 32 x float2
-    constexpr int NI = QTILE / 1024 / NW;
-    constexpr int PT = 4 * NI + 1;
-    static_assert(NI >= 1 && (QTILE / 1024) % NW == 0, "blocks must divide over the waves");
+    constexpr int XCH = NSL * SLOT;              // P exchange: 4 blocks x 4 KB
+    constexpr int NBLK = QTILE / 1024;           // 1 KB blocks per copy
+    constexpr int PW = 4 * NBLK / NW;            // blocks per wave per tile (all in one copy)
+    constexpr int PT = PW + 1;                   // loads per wave per tile
+    static_assert(PW >= 1 && NBLK % PW == 0, "a wave's blocks must lie in one copy");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
+    const bool roleA = w < 4;
+    const int kb = w & 3;
     int bid = xcd_order(blockIdx.x);
     const int kt = bid % p.n_tiles;   // low key tiles see the most queries under causal order
     bid /= p.n_tiles;
@@ -345,22 +357,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const bool noskip = (p.flags & ATTN_NO_TILE_SKIP) != 0;
     const float sl2 = p.scale_log2;
     const long long delta = p.q_off - p.kv_off;   // key j allowed for query i iff j - i <= delta
-    const int k0 = kt * BK, kw0 = k0 + 32 * w, kj = kw0 + l32;
+    const int k0 = kt * BK, kw0 = k0 + 32 * kb, kj = kw0 + l32;
     const bool kvalid = kj < Tkv;
     const bool kmasked = p.kpm && kvalid && p.kpm[b * p.kpm_bstride + kj] != 0;
 
-    // K and V operands (B of S = Q K^T and dP = dO V^T): lane = key.
-    bf16x8 kreg[G::NC], vreg[G::NC];
-    const long long krow = b * p.kv_bstride + (long long)kj * rs + (long long)h * D;
+    // K (wave A) or V (wave B) operand, B of S = Q K^T or dP = dO V^T: lane = key.
+    bf16x8 kv[G::NC];
+    {
+        const uint16_t* src = roleA ? (const uint16_t*)p.k : (const uint16_t*)p.v;
+        const long long krow = b * p.kv_bstride + (long long)kj * rs + (long long)h * D;
 #pragma unroll
-    for (int c = 0; c < G::NC; ++c) {
-        uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
-        if (kvalid) {
-            x = *(const uint4*)((const uint16_t*)p.k + krow + 16 * c + 8 * hh);
-            y = *(const uint4*)((const uint16_t*)p.v + krow + 16 * c + 8 * hh);
+        for (int c = 0; c < G::NC; ++c) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (kvalid) x = *(const uint4*)(src + krow + 16 * c + 8 * hh);
+            kv[c] = __builtin_bit_cast(bf16x8, x);
         }
-        kreg[c] = __builtin_bit_cast(bf16x8, x);
-        vreg[c] = __builtin_bit_cast(bf16x8, y);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
@@ -368,62 +379,56 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const int nqt = (Tq + BQ - 1) / BQ;
     int t0 = 0;
     if (causal && !noskip) {
-        const long long first = (long long)k0 - delta;   // first query that sees key k0
+        const long long first = (long long)k0 - delta;
         t0 = first <= 0 ? 0 : (first >= Tq ? nqt : (int)(first / BQ));
     }
-    // This wave: tiles before tw0 cannot see its keys; from tf on every pair is allowed.
     int tw0 = t0, tf = 0;
     {
         const long long first = (long long)kw0 - delta;
         if (causal && !noskip) tw0 = first <= 0 ? 0 : (first >= Tq ? nqt : (int)(first / BQ));
-        const long long full = (long long)kw0 + 31 - delta;   // first query seeing all 32 keys
+        const long long full = (long long)kw0 + 31 - delta;
         tf = !causal ? 0 : (full <= 0 ? 0 : (int)((full + BQ - 1) / BQ));
         if (p.amask || noskip) tf = nqt;
     }
     const bool wactive = kw0 < Tkv;
-    const int tail = Tq % BQ ? nqt - 1 : nqt;   // a partial last tile needs the row test
+    const int tail = Tq % BQ ? nqt - 1 : nqt;
 
     uint32_t roff[G::NC], toff[G::NDB];
     lane_offsets<D>(lane, roff, toff);
-    uint32_t dr[NI], dt[NI];
+    // tile loads: this wave moves blocks PW*w .. PW*w+PW-1 of the 4 NBLK blocks
+    // (copies: Q row swizzle, Q transposed, dO row, dO transposed)
+    const int copy = (PW * w) / NBLK;
+    const bool from_q = copy < 2, tr_sw = copy & 1;
+    uint32_t dofs[PW];
 #pragma unroll
-    for (int n = 0; n < NI; ++n) {
-        dr[n] = dma_offset<D, false>(w * NI + n, lane, rs2);
-        dt[n] = dma_offset<D, true>(w * NI + n, lane, rs2);
+    for (int n = 0; n < PW; ++n) {
+        const int m = (PW * w + n) % NBLK;
+        dofs[n] = tr_sw ? dma_offset<D, true>(m, lane, rs2) : dma_offset<D, false>(m, lane, rs2);
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
-    const char* qg = (const char*)((const uint16_t*)p.q + b * p.q_bstride + (long long)h * D);
-    const char* og = (const char*)((const uint16_t*)p.dout + b * p.q_bstride + (long long)h * D);
+    const char* srcg = (const char*)((const uint16_t*)(from_q ? p.q : p.dout) + b * p.q_bstride + (long long)h * D);
     const float2* ldg = p.ld2 + b * p.lse_bstride + (long long)h * p.lse_hstride;
     auto slot_of = [&](int t) -> int { return __builtin_amdgcn_readfirstlane(t % NSL); };
     auto issue = [&](int t) {
         const int qa = t * BQ;
         const uint32_t nb = (uint32_t)min(Tq - 1 - qa, BQ - 1) * rs2 + 2u * D;
-        const u32x4 rq = buffer_rsrc(qg + (long long)qa * rs2, nb);
-        const u32x4 ro = buffer_rsrc(og + (long long)qa * rs2, nb);
+        const u32x4 r = buffer_rsrc(srcg + (long long)qa * rs2, nb);
         const uint32_t slot = lds0 + (uint32_t)slot_of(t) * SLOT;
-        const uint32_t base = slot + (uint32_t)(w * NI) * 1024u;
+        const uint32_t base = slot + (uint32_t)copy * QTILE + (uint32_t)((PW * w) % NBLK) * 1024u;
 #pragma unroll
-        for (int n = 0; n < NI; ++n) load_lds16(dr[n], rq, base + 1024u * n);
-#pragma unroll
-        for (int n = 0; n < NI; ++n) load_lds16(dt[n], rq, base + QTILE + 1024u * n);
-#pragma unroll
-        for (int n = 0; n < NI; ++n) load_lds16(dr[n], ro, base + 2 * QTILE + 1024u * n);
-#pragma unroll
-        for (int n = 0; n < NI; ++n) load_lds16(dt[n], ro, base + 3 * QTILE + 1024u * n);
-        // (lse2, delta) of the 32 rows: 64 floats, 16 per wave
+        for (int n = 0; n < PW; ++n) load_lds16(dofs[n], r, base + 1024u * n);
+        // (lse2, delta) of the 32 rows: 64 floats, 8 per wave
         const u32x4 rl = buffer_rsrc(ldg + qa, (uint32_t)min(Tq - qa, BQ) * 8u);
-        if (lane < 16) load_lds4((uint32_t)(16 * w + lane) * 4u, rl, slot + LDO + 64u * w);
+        if (lane < 8) load_lds4((uint32_t)(8 * w + lane) * 4u, rl, slot + LDO + 32u * w);
     };
+    // P exchange block of this key block: [register group j][lane][4 floats]
+    float4* xch = (float4*)(smem + XCH + 4096 * kb) + lane;
 
-    f32x16 dk[G::NDB], dv[G::NDB];
+    f32x16 acc[G::NDB];   // dV^T (wave A) or dK^T (wave B); lane = key
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
-        dk[db] = f32x16{};
-        dv[db] = f32x16{};
-    }
+    for (int db = 0; db < G::NDB; ++db) acc[db] = f32x16{};
 
-    const int ntl = nqt - t0;   // tiles this workgroup visits
+    const int ntl = nqt - t0;
     if (ntl > 0) issue(t0);
     if (ntl > 1) issue(t0 + 1);
     if (ntl > 2) {
@@ -437,56 +442,70 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     for (int t = t0; t < nqt; ++t) {
         const bool more = t + 3 < nqt;
         if (more) issue(t + 3);
-        if (wactive && t >= tw0) {
-            const char* St = smem + slot_of(t) * SLOT;
-            // S = Q K^T and dP = dO V^T: lane = key, register r = query 8 (r/4) + 4 hh + r%4
-            f32x16 s = f32x16{}, dp = f32x16{};
+        const bool act = wactive && t >= tw0;   // the same for both waves of a key block
+        const char* St = smem + slot_of(t) * SLOT;
+        const float4* lp = (const float4*)(St + LDO);
+        f32x16 x = f32x16{};   // S (wave A) or dP (wave B): lane = key, register r = query 8 (r/4) + 4 hh + r%4
+        if (act) {
+            const char* rows = St + (roleA ? 0 : 2 * QTILE);   // Q or dO, row swizzle
+            bf16x8 ra[2];
+            ra[0] = *(const bf16x8*)(rows + roff[0]);
 #pragma unroll
             for (int c = 0; c < G::NC; ++c) {
-                const bf16x8 a = *(const bf16x8*)(St + roff[c]);
-                const bf16x8 o = *(const bf16x8*)(St + 2 * QTILE + roff[c]);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[c], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, vreg[c], dp, 0, 0, 0);
+                if (c + 1 < G::NC) ra[(c + 1) & 1] = *(const bf16x8*)(rows + roff[c + 1]);
+                x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[c & 1], kv[c], x, 0, 0, 0);
             }
-            if (t < tf || t >= tail) {
-                // causal order, rows past Tq, attention mask
-                const int qa = t * BQ;
+            if (roleA) {
+                if (t < tf || t >= tail) {
+                    const int qa = t * BQ;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qi = qa + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    bool ok = qi < Tq && (!causal || (long long)kj - qi <= delta);
-                    if (p.amask && ok && kvalid) ok = p.amask[(long long)qi * p.amask_stride + kj] == 0;
-                    s[r] = ok ? s[r] : -INFINITY;
+                    for (int r = 0; r < 16; ++r) {
+                        const int qi = qa + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        bool ok = qi < Tq && (!causal || (long long)kj - qi <= delta);
+                        if (p.amask && ok && kvalid) ok = p.amask[(long long)qi * p.amask_stride + kj] == 0;
+                        x[r] = ok ? x[r] : -INFINITY;
+                    }
+                }
+                // P = exp2(s sl2 - lse2) with the row's lse2 from LDS
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float4 a = lp[4 * j + 2 * hh];
+                    const float4 c = lp[4 * j + 2 * hh + 1];
+                    x[4 * j + 0] = hw_exp2(fmaf(x[4 * j + 0], sl2, -a.x));
+                    x[4 * j + 1] = hw_exp2(fmaf(x[4 * j + 1], sl2, -a.z));
+                    x[4 * j + 2] = hw_exp2(fmaf(x[4 * j + 2], sl2, -c.x));
+                    x[4 * j + 3] = hw_exp2(fmaf(x[4 * j + 3], sl2, -c.z));
+                    xch[64 * j] = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
                 }
             }
-            // (lse2, delta) of rows 8 j + 4 hh + 0..3: two 16-byte reads per j
-            const float4* lp = (const float4*)(St + LDO);
+        }
+        lds_barrier();   // P of every key block is in LDS
+        if (act) {
+            if (!roleA) {
+                // dS = P (dP - delta)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float4 a = lp[4 * j + 2 * hh];       // rows 8j+4hh, +1
-                const float4 c = lp[4 * j + 2 * hh + 1];   // rows 8j+4hh+2, +3
-                const float l2[4] = {a.x, a.z, c.x, c.z};
-                const float dl[4] = {a.y, a.w, c.y, c.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * j + e;
-                    const float pr = hw_exp2(fmaf(s[r], sl2, -l2[e]));
-                    s[r] = pr;
-                    dp[r] = pr * (dp[r] - dl[e]);
+                for (int j = 0; j < 4; ++j) {
+                    const float4 a = lp[4 * j + 2 * hh];
+                    const float4 c = lp[4 * j + 2 * hh + 1];
+                    const float4 pr = xch[64 * j];
+                    x[4 * j + 0] = pr.x * (x[4 * j + 0] - a.y);
+                    x[4 * j + 1] = pr.y * (x[4 * j + 1] - a.w);
+                    x[4 * j + 2] = pr.z * (x[4 * j + 2] - c.y);
+                    x[4 * j + 3] = pr.w * (x[4 * j + 3] - c.w);
                 }
             }
-            const bf16x8 pp[2] = {pack8(s, 0), pack8(s, 1)};
-            const bf16x8 ps[2] = {pack8(dp, 0), pack8(dp, 1)};
-            // dV^T += dO^T P and dK^T += Q^T dS (A operands transposed from LDS)
+            // dV^T += dO^T P (wave A) or dK^T += Q^T dS (wave B)
+            const bf16x8 xb[2] = {pack8(x, 0), pack8(x, 1)};
+            const char* trt = St + (roleA ? 3 * QTILE : QTILE);
+            constexpr int NJ = 2 * G::NDB;
+            bf16x8 ta[2];
+            ta[0] = tr_operand<D>(trt, toff[0], 0);
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                for (int db = 0; db < G::NDB; ++db) {
-                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(St + 3 * QTILE, toff[db], kc),
-                                                                     pp[kc], dv[db], 0, 0, 0);
-                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(St + QTILE, toff[db], kc),
-                                                                     ps[kc], dk[db], 0, 0, 0);
-                }
+            for (int j = 0; j < NJ; ++j) {
+                const int kc = j / G::NDB, db = j % G::NDB;
+                if (j + 1 < NJ) ta[(j + 1) & 1] = tr_operand<D>(trt, toff[(j + 1) % G::NDB], (j + 1) / G::NDB);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[j & 1], xb[kc], acc[db], 0, 0, 0);
+            }
         }
         if (t + 3 < nqt) wait_barrier<2 * PT>();
         else if (t + 2 < nqt) wait_barrier<PT>();
@@ -494,31 +513,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     }
 
     if (!kvalid) return;
-    const long long orow = b * p.kv_bstride + (long long)kj * rs + (long long)h * D;
-    const bool accum = (p.flags & ATTN_ACCUMULATE) != 0;
     // A key excluded by the key-padding mask gets exactly zero (its lane may
     // hold anything: its scores were not masked, since they reach no other key).
-    const float ks = p.scale;
+    float* og = (roleA ? p.dv : p.dk) + b * p.kv_bstride + (long long)kj * rs + (long long)h * D;
+    const float sc = roleA ? 1.f : p.scale;
+    const bool accum = (p.flags & ATTN_ACCUMULATE) != 0;
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            float4* pk = (float4*)(p.dk + orow + db * 32 + 8 * g + 4 * hh);
-            float4* pv = (float4*)(p.dv + orow + db * 32 + 8 * g + 4 * hh);
-            float4 rk = make_float4(dk[db][4 * g] * ks, dk[db][4 * g + 1] * ks, dk[db][4 * g + 2] * ks,
-                                    dk[db][4 * g + 3] * ks);
-            float4 rv = make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
-            if (kmasked) {
-                rk = make_float4(0.f, 0.f, 0.f, 0.f);
-                rv = rk;
-            }
+            float4* dst = (float4*)(og + db * 32 + 8 * g + 4 * hh);
+            float4 r = make_float4(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc, acc[db][4 * g + 2] * sc,
+                                   acc[db][4 * g + 3] * sc);
+            if (kmasked) r = make_float4(0.f, 0.f, 0.f, 0.f);
             if (accum) {
-                const float4 a = *pk, c = *pv;
-                rk.x += a.x; rk.y += a.y; rk.z += a.z; rk.w += a.w;
-                rv.x += c.x; rv.y += c.y; rv.z += c.z; rv.w += c.w;
+                const float4 a = *dst;
+                r.x += a.x;
+                r.y += a.y;
+                r.z += a.z;
+                r.w += a.w;
             }
-            *pk = rk;
-            *pv = rv;
+            *dst = r;
         }
     }
 }
@@ -623,7 +638,7 @@ hipError_t launch_dq(const BwdParams& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_dkdv(const BwdParams& p, hipStream_t s) {
-    constexpr int BK = 128, LDS = 4 * (4 * 32 * 2 * D + 256);
+    constexpr int BK = 128, LDS = 4 * (4 * 32 * 2 * D + 256) + 4 * 4096;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
@@ -634,7 +649,7 @@ hipError_t launch_dkdv(const BwdParams& p, hipStream_t s) {
     q.n_tiles = (p.Tkv + BK - 1) / BK;
     const long long grid = (long long)q.n_tiles * p.H * p.B;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(256), LDS, s, q);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(512), LDS, s, q);
     return hipGetLastError();
 }
 
