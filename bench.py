@@ -17,6 +17,11 @@ roofline = the attention kernel alone: the same algorithmic FLOPs divided by
 cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample
          of the same workload (rank 0, one GPU only).
 
+--pass bwd times the backward of the same share instead (attn_ring_bwd, or
+attn_bwd for a single call): 8 d algorithmic FLOPs per allowed pair (dP, dV,
+dQ, dK; the recomputed scores are not counted), and the roofline takes the dQ
+and dK/dV kernels of one sub-call together as one launch.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -41,19 +46,30 @@ METRIC = "attention fwd TFLOP/s and % of MFMA bf16 peak (causal, d=128) on 1 MI3
 METRIC_BWD = "attention bwd TFLOP/s and % of MFMA bf16 peak (causal, d=128) on 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json")
-KERNEL_SOURCES = ["blockwise_online_softmax_attn_amd/csrc/fwd_bf16.hip",
-                  "blockwise_online_softmax_attn_amd/csrc/tile_io.h",
-                  "blockwise_online_softmax_attn_amd/csrc/common.h"]
+TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json"),
+                 "bwd": os.path.join(ROOT, "profiles", "attn_bwd_bf16_traffic.json")}
+KERNEL_SOURCES = {
+    "fwd": ["blockwise_online_softmax_attn_amd/csrc/fwd_bf16.hip",
+            "blockwise_online_softmax_attn_amd/csrc/tile_io.h",
+            "blockwise_online_softmax_attn_amd/csrc/common.h"],
+    "bwd": ["blockwise_online_softmax_attn_amd/csrc/bwd_bf16.hip",
+            "blockwise_online_softmax_attn_amd/csrc/tile_io.h",
+            "blockwise_online_softmax_attn_amd/csrc/common.h"],
+}
+# kernels whose counters make up one attention "launch" of each pass: the
+# forward kernel alone; for the backward the dQ and dK/dV kernels of one
+# sub-call together
+TRAFFIC_KERNELS = {"fwd": ("attn_fwd_bf16_kernel<128",),
+                   "bwd": ("bwd_dq_kernel<128", "bwd_dkdv_kernel<128")}
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha() -> str:
+def kernel_sources_sha(which: str = "fwd") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[which]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -211,9 +227,10 @@ def cpu_baseline(w, host_inputs, rows: int, heads: int, dout=None):
 COPY_KERNEL_HINT = "copy_f32_kernel"   # the library's plain float32 copy (calibration of the byte counters)
 
 
-def pmc_per_dispatch(csv_path: str, counter: str):
-    """Mean value of `counter` per dispatch, for the attention kernel and for
-    the calibration copy kernel, from a rocprofv3 --pmc counter_collection.csv."""
+def pmc_per_dispatch(csv_path: str, counter: str, which: str):
+    """Mean value of `counter` per dispatch of each attention kernel of the
+    pass, summed over those kernels (one attention launch), and of the
+    calibration copy kernel, from a rocprofv3 --pmc counter_collection.csv."""
     import csv
     import collections
     vals = collections.defaultdict(lambda: collections.defaultdict(float))
@@ -221,32 +238,39 @@ def pmc_per_dispatch(csv_path: str, counter: str):
         if r["Counter_Name"] != counter:
             continue
         name = r["Kernel_Name"]
-        kind = "attn" if "attn_fwd_bf16_kernel<128" in name else ("copy" if COPY_KERNEL_HINT in name else None)
+        kind = next((kn for kn in TRAFFIC_KERNELS[which] if kn in name), None)
+        if kind is None and COPY_KERNEL_HINT in name:
+            kind = "copy"
         if kind:
             vals[kind][r["Dispatch_Id"]] += float(r["Counter_Value"])
-    return {k: float(np.mean(list(v.values()))) for k, v in vals.items()}
+    means = {k: float(np.mean(list(v.values()))) for k, v in vals.items()}
+    means["attn"] = sum(means[kn] for kn in TRAFFIC_KERNELS[which])
+    return means
 
 
-def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, workload: str) -> dict:
-    """Scale the attention kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
+def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, workload: str, which: str) -> dict:
+    """Scale the attention kernels' FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
     by what the same counters read for a copy of known size, and record the
     kernel source hash they were taken with."""
-    f = pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
-    wv = pmc_per_dispatch(write_csv, "WRITE_SIZE")
+    f = pmc_per_dispatch(fetch_csv, "FETCH_SIZE", which)
+    wv = pmc_per_dispatch(write_csv, "WRITE_SIZE", which)
     nbytes = copy_mib * 2 ** 20
     scale_f = nbytes / (f["copy"] * 1024.0)
     scale_w = nbytes / (wv["copy"] * 1024.0)
     out = {
         "workload": workload,
-        "kernel_sources_sha256": kernel_sources_sha(),
+        "pass": which,
+        "kernels": list(TRAFFIC_KERNELS[which]),
+        "kernel_sources_sha256": kernel_sources_sha(which),
         "fetch_kib_per_dispatch": f["attn"], "write_kib_per_dispatch": wv["attn"],
+        "per_kernel_kib": {kn: {"fetch": f[kn], "write": wv[kn]} for kn in TRAFFIC_KERNELS[which]},
         "copy_bytes": nbytes, "copy_fetch_kib": f["copy"], "copy_write_kib": wv["copy"],
         "scale_fetch": scale_f, "scale_write": scale_w,
         "fetch_bytes_per_launch": f["attn"] * 1024.0 * scale_f,
         "write_bytes_per_launch": wv["attn"] * 1024.0 * scale_w,
     }
     out["bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
-    with open(TRAFFIC_FILE, "w") as fh:
+    with open(TRAFFIC_FILES[which], "w") as fh:
         json.dump(out, fh, indent=1)
     return out
 
@@ -270,7 +294,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.write_traffic:
         w = workloads.WORKLOADS[args.workload]
-        print(json.dumps(write_traffic(*args.write_traffic, args.copy_calibration_mib or 1024, w.name)))
+        print(json.dumps(write_traffic(*args.write_traffic, args.copy_calibration_mib or 1024, w.name,
+                                       args.which)))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the ring on a single GPU (the ring itself is emulated "
@@ -322,18 +347,23 @@ def main() -> int:
         torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
-    kern_ms = float(np.sum(kt.ms))
-    n_launch = len(kt.ms)
+    kms = np.asarray(kt.ms, dtype=np.float64)
+    kern_ms = float(kms.sum())
+    # one attention launch of the backward is the dQ kernel and the dK/dV
+    # kernel of one sub-call (timed in that order)
+    per_launch = 2 if bwd else 1
+    n_launch = len(kms) // per_launch
     achieved = flops * args.steps / (kern_ms * 1e-3) / 1e12 if kern_ms > 0 else None
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     log(f"{ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of peak); kernel-only "
         f"{achieved:.1f} TFLOP/s over {n_launch} launches (avg {kern_ms / max(n_launch, 1):.4f} ms)")
 
     traffic = None
-    if not bwd and os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    tfile = TRAFFIC_FILES[args.which]
+    if w.dtype == "bf16" and os.path.exists(tfile):
+        with open(tfile) as f:
             tr = json.load(f)
-        if tr.get("kernel_sources_sha256") == kernel_sources_sha() and tr.get("workload") == w.name:
+        if tr.get("kernel_sources_sha256") == kernel_sources_sha(args.which) and tr.get("workload") == w.name:
             traffic = tr.get("bytes_per_launch")
     roofline = {
         "bound": "mfma",
@@ -349,6 +379,9 @@ def main() -> int:
         "avg_launch_ms": kern_ms / max(n_launch, 1),
         "flops_per_launch": flops * args.steps / max(n_launch, 1),
     }
+    if bwd and len(kms) >= 2:
+        roofline["avg_ms_per_kernel"] = {f"bwd_dq_kernel<{w.d}>": float(kms[0::2].mean()),
+                                         f"bwd_dkdv_kernel<{w.d}>": float(kms[1::2].mean())}
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows x {args.cpu_heads} heads")
