@@ -16,7 +16,10 @@ Every function states the passage of the source pages it follows:
 * the sequence/context-parallelism post on brunomaga.github.io: section "Ring
   Attention" (fraction form), "Improving numerical stability" (safe softmax,
   accumulator rescale, LogSumExp), "Distributed algorithm" and "Implementation"
-  (forward and backward pass of the ring).
+  (forward and backward pass of the ring);
+* "Transformers and Attention" #53 (causal key/value caching), #55
+  (Longformer sliding windows), #57 (static caches and windowed retention),
+  #58 (ALiBi) for the variants: window, linear distance bias, decoding.
 
 Pins: every function here is checked by ``tests/test_oracle_pins.py`` against
 facts the pages or mathematics fix (printed worked example, closed forms,
@@ -34,6 +37,9 @@ from .reference import (  # noqa: F401
     sdpa_backward,
     attention,
     attention_backward,
+    alibi_bias,
+    kv_append,
+    decode,
     merge,
     ring_order,
     zigzag_chunks,

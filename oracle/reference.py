@@ -129,22 +129,45 @@ def _rotated(x, pos, base: float, dtype: str) -> np.ndarray:
     return round_to_dtype(rope_rotate_f32(x, pos, base), dtype)
 
 
-def _allowed(B, Tq, Tkv, q_pos, kv_pos, causal, kpm, attn_mask) -> np.ndarray:
+def _allowed(B, Tq, Tkv, q_pos, kv_pos, causal, kpm, attn_mask, window=(-1, -1)) -> np.ndarray:
     """allowed[b, i, j]: key-padding and attention-mask exclusions combined
-    ("Transformers and Attention" #2) and, if causal, key position <= query
-    position (#24)."""
+    ("Transformers and Attention" #2), if causal, key position <= query
+    position (#24), and the sliding window: a key at most `left` positions
+    before and at most `right` positions after the query (#55, Longformer:
+    each token connects to nearby positions; the post's flash-attention call
+    passes the window as a (left, right) pair, -1 meaning no limit on that
+    side)."""
     allowed = np.ones((B, Tq, Tkv), dtype=bool)
     if kpm is not None:
         allowed &= ~(np.asarray(kpm) != 0)[:, None, :]
     if attn_mask is not None:
         allowed &= ~(np.asarray(attn_mask) != 0)[None, :, :]
+    qp = np.asarray(q_pos)[None, :, None]
+    kp = np.asarray(kv_pos)[None, None, :]
     if causal:
-        allowed &= (np.asarray(kv_pos)[None, None, :] <= np.asarray(q_pos)[None, :, None])
+        allowed &= kp <= qp
+    left, right = window
+    if left >= 0:
+        allowed &= kp >= qp - left
+    if right >= 0:
+        allowed &= kp <= qp + right
     return allowed
 
 
+def alibi_bias(q_pos, kv_pos, slope: float) -> np.ndarray:
+    """ALiBi ("Transformers and Attention" #58): a penalty proportional to the
+    query-key distance, with a fixed slope per head, added to the scores
+    before the softmax: -slope * |pos_q - pos_k|, shape (Tq, Tkv).  It is
+    added to the scaled scores (the scores softmax sees); the absolute
+    distance makes it symmetric when keys lie after the query."""
+    qp = np.asarray(q_pos, dtype=np.float64)[:, None]
+    kp = np.asarray(kv_pos, dtype=np.float64)[None, :]
+    return -float(slope) * np.abs(qp - kp)
+
+
 def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=None,
-         rope_base: float = 0.0, dtype: str = "bf16") -> Tuple[np.ndarray, np.ndarray]:
+         rope_base: float = 0.0, dtype: str = "bf16", window=(-1, -1),
+         alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray]:
     """out, lse of softmax(q k^T / sqrt(d) + mask) v for every (batch, head).
 
     q: (B, Tq, H, d), k and v: (B, Tkv, H, d) holding the exact input values;
@@ -163,6 +186,9 @@ def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=No
     exactly 0 elsewhere, l = sum e, out = (e / l) v, lse = m + ln l (the
     log-sum-exp of the allowed scores, "LSE" in the same section).
     A row with no allowed key returns out = 0 and lse = -inf.
+    window = (left, right) limits the keys to a band around each query
+    (``_allowed``); alibi_slopes[H], if given, adds ``alibi_bias`` with the
+    head's slope to the scaled scores (lse then includes the bias).
 
     Returns out (B, Tq, H, d_v) and lse (B, H, Tq), both float64 (the value
     width d_v may differ from d, "Transformers and Attention" #24).
@@ -177,7 +203,7 @@ def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=No
     if rope_base > 0:
         q = _rotated(q, q_pos, rope_base, dtype)
         k = _rotated(k, kv_pos, rope_base, dtype)
-    allowed = _allowed(B, Tq, Tkv, q_pos, kv_pos, causal, kpm, attn_mask)
+    allowed = _allowed(B, Tq, Tkv, q_pos, kv_pos, causal, kpm, attn_mask, window)
 
     scale = 1.0 / math.sqrt(d)
     dv = v.shape[-1]
@@ -188,6 +214,8 @@ def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=No
         has = ok.any(axis=1)
         for h in range(H):
             s = scale * (q[b, :, h, :] @ k[b, :, h, :].T)            # (Tq, Tkv)
+            if alibi_slopes is not None:
+                s = s + alibi_bias(q_pos, kv_pos, alibi_slopes[h])
             sm = np.where(ok, s, NEG_INF)
             m = np.max(sm, axis=1) if Tkv else np.full(Tq, NEG_INF)
             m_safe = np.where(has, m, 0.0)
@@ -277,6 +305,82 @@ def attention(q, k, v, *, q_off: int = 0, kv_off: int = 0, **kw) -> Tuple[np.nda
     Tq = np.asarray(q).shape[1]
     Tkv = np.asarray(k).shape[1]
     return sdpa(q, k, v, q_off + np.arange(Tq), kv_off + np.arange(Tkv), **kw)
+
+
+# --------------------------------------------------------------------------
+# decoding over a key/value cache
+# --------------------------------------------------------------------------
+def kv_append(k_cache, v_cache, cache_len, k_new, v_new, *, rope_base: float = 0.0,
+              dtype: str = "bf16"):
+    """One decoding step's cache update ("Transformers and Attention" #53: the
+    new token's key and value are appended to the layer's cache; #57: a
+    static cache has a fixed number of slots and masks the unused ones).
+
+    k_cache, v_cache: (B, Tcap, H, d); cache_len[B]: filled slots (slot j
+    holds the token at position j); k_new, v_new: (B, H, d).  The new key is
+    stored rotated to its position cache_len[b] (``_rotated``: the float32
+    rotation rounded to ``dtype``), the value as given; cache_len[b] grows by
+    one.  A full cache (cache_len[b] == Tcap) is left unchanged.  Returns new
+    arrays (k_cache, v_cache, cache_len).
+    """
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    ln = np.array(cache_len, dtype=np.int64, copy=True)
+    Tcap = kc.shape[1]
+    for b in range(kc.shape[0]):
+        L = int(ln[b])
+        if L >= Tcap:
+            continue
+        kb = np.asarray(k_new[b], dtype=np.float64)[None, :, :]      # (1, H, d)
+        if rope_base > 0:
+            kb = _rotated(kb, np.array([L]), rope_base, dtype)
+        kc[b, L] = kb[0]
+        vc[b, L] = np.asarray(v_new[b], dtype=np.float64)
+        ln[b] = L + 1
+    return kc, vc, ln
+
+
+def decode(q, k_cache, v_cache, cache_len, *, rope_base: float = 0.0, dtype: str = "bf16",
+           window_left: int = -1, alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of the newest token over the cache ("Transformers and
+    Attention" #53: at step t the new query attends over the retained and
+    the current keys and values).
+
+    q: (B, H, d), the query of the token at position cache_len[b] - 1 (its
+    key and value already appended); keys are the cache slots [0,
+    cache_len[b]) as stored (already rotated by ``kv_append``), the query is
+    rotated to its position here.  window_left >= 0 keeps only the keys at
+    most that many positions back (#57: windowed layers retain a bounded
+    history); alibi_slopes as in ``sdpa``.  Causal order holds by
+    construction (no slot after the query is filled).  Returns out (B, H, d)
+    and lse (B, H); an empty cache row gives (0, -inf).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)
+    vc = np.asarray(v_cache, dtype=np.float64)
+    B, H, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    out = np.zeros((B, H, vc.shape[-1]), dtype=np.float64)
+    lse = np.full((B, H), NEG_INF, dtype=np.float64)
+    for b in range(B):
+        L = int(cache_len[b])
+        if L <= 0:
+            continue
+        pos = L - 1
+        lo = 0 if window_left < 0 else max(0, pos - window_left)
+        qb = q[b][None, :, :]                                        # (1, H, d)
+        if rope_base > 0:
+            qb = _rotated(qb, np.array([pos]), rope_base, dtype)
+        for h in range(H):
+            s = scale * (kc[b, lo:L, h, :] @ qb[0, h, :])            # (L - lo,)
+            if alibi_slopes is not None:
+                s = s + alibi_bias([pos], np.arange(lo, L), alibi_slopes[h])[0]
+            m = s.max()
+            e = np.exp(s - m)
+            l = e.sum()
+            out[b, h, :] = (e / l) @ vc[b, lo:L, h, :]
+            lse[b, h] = m + math.log(l)
+    return out, lse
 
 
 # --------------------------------------------------------------------------
