@@ -44,6 +44,8 @@ import workloads  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s and % of MFMA bf16 peak (causal, d=128) on 1 MI355X"
 METRIC_BWD = "attention bwd TFLOP/s and % of MFMA bf16 peak (causal, d=128) on 1 MI355X"
+METRIC_DECODE = "attention decode step GB/s over the key/value cache (bf16, d=128) on 1 MI355X"
+PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3
 TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json"),
@@ -223,6 +225,89 @@ def cpu_baseline(w, host_inputs, rows: int, heads: int, dout=None):
     }
 
 
+# ---------------------------------------------------------------- decoding
+def run_decode(args, w) -> dict:
+    """One decoding step per iteration over a static cache of w.T slots per
+    row (filled lengths from the workload's length range): attn_kv_append of
+    the new token, then attn_decode of its query.  Algorithmic bytes: every
+    visible cached key and value row read once (the append and the query are
+    a few KiB)."""
+    dev = torch.device("cuda:0")
+    lens0 = workloads.kpm_lengths(w)
+    log(f"workload {w.name}: drawing a {w.B}x{w.T}x{w.H}x{w.d} cache")
+    kc = workloads.draw_tokens(w, 1, range(w.n_chunks)).to(dev)
+    vc = workloads.draw_tokens(w, 2, range(w.n_chunks)).to(dev)
+    q = workloads.random_normal((w.B, w.H, w.d), workloads.seed_for(w, 0, 0), w.torch_dtype).to(dev)
+    kn = workloads.random_normal((w.B, w.H, w.d), workloads.seed_for(w, 0, 1), w.torch_dtype).to(dev)
+    vn = workloads.random_normal((w.B, w.H, w.d), workloads.seed_for(w, 0, 2), w.torch_dtype).to(dev)
+    ln = lens0.to(torch.int32).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    esize = 2 if w.dtype == "bf16" else 4
+
+    def step():
+        bosa.attn_kv_append(kn, vn, kc, vc, ln, rope_base=w.rope_base)
+        bosa.attn_decode(q, kc, vc, ln, out=out, lse=lse, rope_base=w.rope_base)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    L_start = ln.cpu().to(torch.int64)
+    # the s-th timed step sees L_start + s + 1 slots per row
+    nbytes = sum(int((L_start + s + 1).sum()) for s in range(args.steps)) * w.H * w.d * 2 * esize
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} decode steps")
+    with bosa.KernelTimer(max_launches=args.steps + 16) as kt:
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            step()
+        end.record()
+        torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    gbs = nbytes / args.steps / (ms * 1e-3) / 1e9
+    kms = np.asarray(kt.ms, dtype=np.float64)
+    achieved = nbytes / (kms.sum() * 1e-3) / 1e9 if kms.sum() > 0 else None
+    log(f"{ms:.4f} ms/step, {gbs:.0f} GB/s; decode kernel {achieved:.0f} GB/s over {len(kms)} launches "
+        f"(avg {kms.mean():.4f} ms)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+
+        import oracle
+        rows = 2
+        info = threadpoolctl.threadpool_info()
+        blas_threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        kh = kc[:rows].cpu().double().numpy()
+        vh = vc[:rows].cpu().double().numpy()
+        qh = q[:rows].cpu().double().numpy()
+        lh = ln[:rows].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.decode(qh, kh, vh, lh, rope_base=w.rope_base, dtype=w.dtype)
+        dt = time.perf_counter() - t0
+        cb = int(lh.sum()) * w.H * w.d * 2 * esize
+        cpu = {"value": cb / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+               "sample": (f"oracle.decode of batch rows 0..{rows - 1} (all {w.H} heads, {int(lh.sum())} visible "
+                          f"slots): {cb:.3e} algorithmic bytes in {dt:.2f} s (float64 numpy, BLAS threads="
+                          f"{blas_threads}, host cpus={os.cpu_count()})")}
+        log(f"cpu baseline {cpu['value']:.3f} GB/s")
+    return {
+        "metric": METRIC_DECODE, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "pct_of_peak": 100.0 * gbs / PEAK_HBM_GBS,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "cache_slots": w.T, "d": w.d,
+                   "filled_range": w.kpm_len_range, "rope_base": w.rope_base, "pass": "decode",
+                   "algorithmic_bytes_per_step": nbytes / args.steps},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS if achieved else None, "traffic": None,
+                     "kernel": f"decode_chunk_kernel<bf16,{w.d}>", "launches": int(len(kms)),
+                     "avg_launch_ms": float(kms.mean()) if len(kms) else None,
+                     "bytes_per_launch": nbytes / max(len(kms), 1)},
+        "cpu_baseline": cpu,
+    }
+
+
 # ---------------------------------------------------------------- HBM traffic
 COPY_KERNEL_HINT = "copy_f32_kernel"   # the library's plain float32 copy (calibration of the byte counters)
 
@@ -307,6 +392,9 @@ def main() -> int:
         return 2
     bosa.load()
     w = workloads.WORKLOADS[args.workload]
+    if w.decode:
+        print(json.dumps(run_decode(args, w)), flush=True)
+        return 0
     log(f"workload {w.name}: drawing inputs")
     plan, host, dev = build_inputs(w)
     bwd = args.which == "bwd"

@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     RingCall,
+    Variant,
     check,
     load,
 )
@@ -55,15 +56,28 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream or None
 
 
+def _variant(window, alibi_slopes, H: int):
+    """attn_variant for a (left, right) window and [H] float32 slopes, or None."""
+    if window is None and alibi_slopes is None:
+        return None, None
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    if alibi_slopes is not None and (alibi_slopes.shape != (H,) or alibi_slopes.dtype != torch.float32):
+        raise ValueError("alibi_slopes must be float32 of shape (H,)")
+    v = Variant(wl, wr, _dev(alibi_slopes, "alibi_slopes", torch.float32))
+    return ctypes.byref(v), v
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None, *, q_off: int = 0, kv_off: int = 0, causal: bool = False,
              kpm: Optional[torch.Tensor] = None, attn_mask: Optional[torch.Tensor] = None,
-             rope_base: float = 0.0, flags: int = 0, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+             rope_base: float = 0.0, flags: int = 0, window=None, alibi_slopes: Optional[torch.Tensor] = None,
+             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """out, lse = attention over one key/value block (see attn_fwd in attn.h).
 
     q (B, Tq, H, d), k/v (B, Tkv, H, d); kpm (B, Tkv) and attn_mask (Tq, Tkv)
     are uint8 with nonzero = excluded.  out is allocated in q's dtype, or
-    float32 with ATTN_OUT_F32; lse (B, H, Tq) float32."""
+    float32 with ATTN_OUT_F32; lse (B, H, Tq) float32.  window = (left,
+    right) (-1 = no limit) and alibi_slopes (H,) float32 select attn_fwd_ex."""
     load()
     B, Tq, H, d = q.shape
     Tkv = k.shape[1]
@@ -85,10 +99,64 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[to
         raise ValueError("kpm must be uint8 (B, Tkv)")
     if attn_mask is not None and (attn_mask.shape != (Tq, Tkv) or attn_mask.dtype != torch.uint8):
         raise ValueError("attn_mask must be uint8 (Tq, Tkv)")
-    rc = load().attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out", out_dtype),
-                         _dev(lse, "lse", torch.float32), B, H, Tq, Tkv, d, int(q_off), int(kv_off),
-                         1 if causal else 0, _dev(kpm, "kpm"), _dev(attn_mask, "attn_mask"), float(rope_base),
-                         code, int(flags), _stream(stream))
+    args = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out", out_dtype), _dev(lse, "lse", torch.float32),
+            B, H, Tq, Tkv, d, int(q_off), int(kv_off), 1 if causal else 0, _dev(kpm, "kpm"),
+            _dev(attn_mask, "attn_mask"), float(rope_base), code, int(flags))
+    var, _keep = _variant(window, alibi_slopes, H)
+    if var is None:
+        rc = load().attn_fwd(*args, _stream(stream))
+    else:
+        rc = load().attn_fwd_ex(*args, var, _stream(stream))
+    check(rc)
+    return out, lse
+
+
+def attn_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   cache_len: torch.Tensor, *, rope_base: float = 0.0, stream=None) -> None:
+    """Append one token per row to a static cache (see attn_kv_append in attn.h):
+    k_new, v_new (B, H, d); caches (B, Tcap, H, d); cache_len int32 (B,) on the
+    device, advanced by one for every row that had room."""
+    load()
+    B, Tcap, H, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or k_new.shape != (B, H, d) or v_new.shape != (B, H, d):
+        raise ValueError("cache / new-token shape mismatch")
+    if cache_len.shape != (B,):
+        raise ValueError("cache_len must have shape (B,)")
+    for t in (k_new, v_new, v_cache):
+        if t.dtype != k_cache.dtype:
+            raise TypeError("k_new, v_new and the caches must share a dtype")
+    rc = load().attn_kv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
+                               _dev(v_cache, "v_cache"), _dev(cache_len, "cache_len", torch.int32), B, H, Tcap, d,
+                               float(rope_base), _dtype_code(k_cache), _stream(stream))
+    check(rc)
+
+
+def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_len: torch.Tensor,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, *, rope_base: float = 0.0,
+                window_left: int = -1, alibi_slopes: Optional[torch.Tensor] = None, flags: int = 0,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """out (B, H, d), lse (B, H) of each row's newest query over its cache
+    (see attn_decode in attn.h)."""
+    load()
+    B, Tcap, H, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or q.shape != (B, H, d):
+        raise ValueError("q / cache shape mismatch")
+    if cache_len.shape != (B,):
+        raise ValueError("cache_len must have shape (B,)")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share a dtype")
+    out_dtype = torch.float32 if (flags & ATTN_OUT_F32) else q.dtype
+    if out is None:
+        out = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if out.shape != (B, H, d) or lse.shape != (B, H):
+        raise ValueError("out/lse shape mismatch")
+    var, _keep = _variant((window_left, -1) if window_left >= 0 else None, alibi_slopes, H)
+    rc = load().attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                            _dev(cache_len, "cache_len", torch.int32), _dev(out, "out", out_dtype),
+                            _dev(lse, "lse", torch.float32), B, H, Tcap, d, float(rope_base), _dtype_code(q),
+                            int(flags), var, _stream(stream))
     check(rc)
     return out, lse
 

@@ -14,9 +14,9 @@ ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_ACCUMULATE, ATTN_OUT_F32, ATTN_NO_TILE_SKIP = 1, 2, 4
 
 # Every symbol include/attn.h declares.
-EXPORTS = ("attn_fwd", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan", "attn_ring_fwd",
-           "attn_bwd", "attn_ring_bwd", "attn_profile_start", "attn_profile_stop", "attn_last_error",
-           "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan", "attn_ring_fwd",
+           "attn_bwd", "attn_ring_bwd", "attn_kv_append", "attn_decode", "attn_profile_start",
+           "attn_profile_stop", "attn_last_error", "attn_version")
 
 
 class RingCall(ctypes.Structure):
@@ -29,6 +29,15 @@ class RingCall(ctypes.Structure):
         ("kv_pos0", ctypes.c_longlong),
         ("kv_rows", ctypes.c_int),
         ("accumulate", ctypes.c_int),
+    ]
+
+
+class Variant(ctypes.Structure):
+    """attn_variant: sliding window (-1 = no limit) and ALiBi slopes."""
+    _fields_ = [
+        ("window_left", ctypes.c_longlong),
+        ("window_right", ctypes.c_longlong),
+        ("alibi_slopes", ctypes.c_void_p),
     ]
 
 
@@ -51,6 +60,10 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, ll, u, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_uint, ctypes.c_double
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, ll, i, vp, vp, d, i, u, vp]
+    var = ctypes.POINTER(Variant)
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, ll, i, vp, vp, d, i, u, var, vp]
+    lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, d, i, vp]
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, d, i, u, var, vp]
     lib.attn_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.rope_apply.argtypes = [vp, vp, d, i, i, i, i, i, vp]
     lib.attn_cast.argtypes = [vp, vp, ll, i, vp]
@@ -60,8 +73,9 @@ def load() -> ctypes.CDLL:
     lib.attn_ring_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, d, i, u, vp]
     lib.attn_profile_start.argtypes = [i]
     lib.attn_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_float), i]
-    for name in ("attn_fwd", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan", "attn_ring_fwd",
-                 "attn_bwd", "attn_ring_bwd", "attn_profile_start", "attn_profile_stop", "attn_version"):
+    for name in ("attn_fwd", "attn_fwd_ex", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan",
+                 "attn_ring_fwd", "attn_bwd", "attn_ring_bwd", "attn_kv_append", "attn_decode",
+                 "attn_profile_start", "attn_profile_stop", "attn_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p

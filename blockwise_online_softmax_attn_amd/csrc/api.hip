@@ -70,6 +70,8 @@ struct Call {
     long long q_bstride, kv_bstride, o_bstride, kpm_bstride, lse_bstride;
     int lse_hstride, amask_stride;
     const float2* rope_q; const float2* rope_k;
+    long long win_left = -1, win_right = -1;
+    const float* alibi = nullptr;
 };
 
 Call plain_call(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Tq, int Tkv,
@@ -124,6 +126,10 @@ int enqueue(const Call& c, int* list, hipStream_t s) {
     p.q_off = c.q_off; p.kv_off = c.kv_off; p.causal = c.causal ? 1 : 0;
     p.flags = c.flags;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.d));
+    p.win_left = c.win_left;
+    p.win_right = c.win_right;
+    p.alibi = c.alibi;
+    p.sqrt_d = (float)std::sqrt((double)c.d);
     if (c.dtype == ATTN_BF16) {
         if (list) {
             const int ntk = (c.Tkv + kTile - 1) / kTile;
@@ -265,7 +271,17 @@ int attn_profile_stop(float* ms, int cap) {
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Tq, int Tkv, int d,
              long long q_off, long long kv_off, int causal, const uint8_t* kpm, const uint8_t* attn_mask,
              double rope_base, int dtype, unsigned flags, attn_stream_t stream) {
+    return attn_fwd_ex(q, k, v, out, lse, B, H, Tq, Tkv, d, q_off, kv_off, causal, kpm, attn_mask, rope_base, dtype,
+                       flags, nullptr, stream);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Tq, int Tkv,
+                int d, long long q_off, long long kv_off, int causal, const uint8_t* kpm, const uint8_t* attn_mask,
+                double rope_base, int dtype, unsigned flags, const attn_variant* var, attn_stream_t stream) {
     g_err.clear();
+    if (var && (var->window_left < -1 || var->window_right < -1))
+        return fail(ATTN_ERR_INVALID_ARG, "window sizes must be >= -1 (got %lld, %lld)", var->window_left,
+                    var->window_right);
     if (int rc = check_sizes(B, H, Tq, Tkv, d)) return rc;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
     if (flags & ~(unsigned)(ATTN_ACCUMULATE | ATTN_OUT_F32 | ATTN_NO_TILE_SKIP))
@@ -285,6 +301,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     if (int rc = check_bf16_rows(dtype, H, d)) return rc;
 
     Call c = plain_call(q, k, v, out, lse, B, H, Tq, Tkv, d, q_off, kv_off, causal, kpm, attn_mask, dtype, flags);
+    if (var) {
+        c.win_left = var->window_left;
+        c.win_right = var->window_right;
+        c.alibi = var->alibi_slopes;
+    }
     hipStream_t s = (hipStream_t)stream;
     const bool rope = rope_base > 0.0 && Tkv > 0;
     // bf16: the keys are rotated once into a scratch copy that the attention
@@ -314,6 +335,74 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
         }
     }
     return enqueue(c, lst ? (int*)(wp + tab_q + tab_k + kbuf) : nullptr, s);
+}
+
+int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, int* cache_len, int B, int H,
+                   int Tcap, int d, double rope_base, int dtype, attn_stream_t stream) {
+    g_err.clear();
+    if (B < 0 || H < 0 || Tcap < 0) return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", d);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (!(rope_base >= 0.0) || std::isinf(rope_base)) return fail(ATTN_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
+    if (B == 0 || H == 0 || Tcap == 0) return ATTN_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !cache_len) return fail(ATTN_ERR_INVALID_ARG, "NULL pointer");
+    const uintptr_t al = dtype == ATTN_BF16 ? 3u : 7u;
+    if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_cache | (uintptr_t)v_cache) & al)
+        return fail(ATTN_ERR_INVALID_ARG, "tensors must be %d-byte aligned", (int)al + 1);
+    if ((long long)B * Tcap * H * d >= (1LL << 47)) return fail(ATTN_ERR_UNSUPPORTED, "cache too large");
+    hipError_t e = launch_kv_append(k_new, v_new, k_cache, v_cache, cache_len, B, H, Tcap, d,
+                                    rope_base > 0.0 ? std::log(rope_base) : 0.0, dtype == ATTN_BF16,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "cache append launch");
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_len, void* out, float* lse,
+                int B, int H, int Tcap, int d, double rope_base, int dtype, unsigned flags, const attn_variant* var,
+                attn_stream_t stream) {
+    g_err.clear();
+    if (B < 0 || H < 0 || Tcap < 0) return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", d);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (flags & ~(unsigned)ATTN_OUT_F32) return fail(ATTN_ERR_INVALID_ARG, "only ATTN_OUT_F32 may be passed");
+    if (!(rope_base >= 0.0) || std::isinf(rope_base)) return fail(ATTN_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
+    if (var && (var->window_left < -1 || var->window_right < -1))
+        return fail(ATTN_ERR_INVALID_ARG, "window sizes must be >= -1");
+    if (B == 0 || H == 0) return ATTN_OK;
+    if (!q || !out || !cache_len || (Tcap > 0 && (!k_cache || !v_cache))) return fail(ATTN_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(q) || (Tcap > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) || ((uintptr_t)out & 3))
+        return fail(ATTN_ERR_INVALID_ARG, "q and the caches must be 16-byte aligned, out 4-byte");
+    if ((long long)B * Tcap * H * d >= (1LL << 47)) return fail(ATTN_ERR_UNSUPPORTED, "cache too large");
+    const bool bf16 = dtype == ATTN_BF16;
+    // chunks of CH slots: enough workgroups to fill the chip for any batch
+    const int gran = decode_chunk_granule(d, bf16);
+    const long long bh = (long long)B * H;
+    long long nch = (8192 + bh - 1) / bh;
+    long long CH = Tcap > 0 ? (Tcap + nch - 1) / nch : gran;
+    CH = (CH + gran - 1) / gran * gran;
+    if (CH < 4LL * gran) CH = 4LL * gran;
+    nch = Tcap > 0 ? (Tcap + CH - 1) / CH : 1;
+    if (bh * nch >= (1LL << 31) || CH >= (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+    DecodeParams p{};
+    p.q = q; p.k = k_cache; p.v = v_cache; p.cache_len = cache_len; p.out = out; p.lse = lse;
+    p.alibi = var ? var->alibi_slopes : nullptr;
+    p.B = B; p.H = H; p.Tcap = Tcap; p.CH = (int)CH; p.n_chunks = (int)nch;
+    p.win_left = var ? var->window_left : -1;
+    p.log_base = rope_base > 0.0 ? std::log(rope_base) : 0.0;
+    p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    p.sqrt_d = (float)std::sqrt((double)d);
+    hipStream_t s = (hipStream_t)stream;
+    const size_t po = align_up((size_t)bh * nch * d * sizeof(float));
+    const size_t pl = align_up((size_t)bh * nch * sizeof(float));
+    Scratch ws;
+    hipError_t e = ws.alloc(po + pl, s);
+    if (e != hipSuccess) return hip_fail(e, "scratch allocation");
+    p.part_o = (float*)ws.ptr;
+    p.part_lse = (float*)((char*)ws.ptr + po);
+    if (Tcap > 0)
+        if (int rc = timed_launch([&] { return launch_decode_chunks(p, d, bf16, s); }, "decode kernel launch", s))
+            return rc;
+    e = launch_decode_merge(p, d, bf16 && !(flags & ATTN_OUT_F32), s);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "decode merge launch");
 }
 
 int attn_merge(float* out_a, float* lse_a, const void* out_b, const float* lse_b, int B, int H, int Tq, int d,

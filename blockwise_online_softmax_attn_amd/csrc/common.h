@@ -107,6 +107,11 @@ struct FwdParams {
     unsigned flags;
     float scale_log2;          // log2(e) / sqrt(d)
     int n_qtiles;
+    // sliding window: a key at most win_left positions before and at most
+    // win_right positions after the query (absolute positions); -1 = no limit
+    long long win_left, win_right;
+    const float* alibi;        // [H] slopes: score -= slope_h |pos_q - pos_k| (after 1/sqrt(d)), or null
+    float sqrt_d;              // sqrt(d): the bias in units of the unscaled dot product
 };
 
 // One attention backward launch (bf16 inputs, float32 outputs).  q and k are
@@ -142,7 +147,31 @@ struct BwdParams {
 constexpr uint32_t kTileClean = 0x80000000u;
 
 // Kernel launchers (each returns hipSuccess or the launch error).
+// One decoding call: the newest query of each (batch, head) against the
+// filled slots of a static cache, split into chunks of CH slots.
+struct DecodeParams {
+    const void* q;             // (B, H, d)
+    const void* k;             // (B, Tcap, H, d), keys stored rotated
+    const void* v;
+    const int* cache_len;      // [B] filled slots; the query sits at position cache_len[b] - 1
+    void* out;                 // (B, H, d)
+    float* lse;                // (B, H) or null
+    float* part_o;             // (B, H, n_chunks, d) partial outputs (normalised)
+    float* part_lse;           // (B, H, n_chunks)
+    const float* alibi;        // [H] slopes or null
+    int B, H, Tcap, CH, n_chunks;
+    long long win_left;        // -1: every filled slot
+    double log_base;           // ln(rope base), or 0: no rotation of the query
+    float scale_log2;          // log2(e) / sqrt(d)
+    float sqrt_d;
+};
+
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s);
+int decode_chunk_granule(int d, int is_bf16);
+hipError_t launch_decode_chunks(const DecodeParams& p, int d, int is_bf16, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeParams& p, int d, int out_bf16, hipStream_t s);
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, int* cache_len, int B,
+                            int H, int Tcap, int d, double log_base, int is_bf16, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_rope_table(float2* tab, long long pos0, int n, int d, double log_base, hipStream_t s);
 hipError_t launch_kpm_tiles(const uint8_t* kpm, long long kpm_bstride, int B, int Tkv, int tile,

@@ -202,7 +202,19 @@ __device__ __forceinline__ void accumulate_pv(const char* Vt, const uint32_t (&v
     }
 }
 
-template <int D>
+// ALiBi: add ab |base - key| to every score of the tile, where base =
+// (query position - position of the lane's first key) and ab = -slope sqrt(d)
+// (the penalty in units of the unscaled dot product).  Excluded scores stay -inf.
+__device__ __forceinline__ void add_alibi(f32x16& s0, f32x16& s1, float base, float ab) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float k0 = (float)(8 * (r >> 2) + (r & 3));
+        s0[r] = fmaf(fabsf(base - k0), ab, s0[r]);
+        s1[r] = fmaf(fabsf(base - (k0 + 32.f)), ab, s1[r]);
+    }
+}
+
+template <int D, bool ALIBI, bool WIN>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p) {
     using G = Geo<D>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -264,59 +276,95 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // ---- key tiles of this workgroup
+    // Keys some row of the workgroup may see: [klo, khi) (causal order and the
+    // window bound them unless every tile is to be visited).  Without a window
+    // (WIN false) every window term folds away at compile time.
+    const bool wl_on = WIN && p.win_left >= 0, wr_on = WIN && p.win_right >= 0;
     const int qlast = min(q0 + BM, Tq) - 1;
-    long long nk = Tkv;
-    if (causal && !noskip) {
-        const long long lim = delta + qlast + 1;
-        nk = lim < 0 ? 0 : (lim < nk ? lim : nk);
+    long long khi = Tkv, klo = 0;
+    if (!noskip) {
+        if (causal) khi = min(khi, delta + qlast + 1);
+        if (wr_on) khi = min(khi, delta + qlast + p.win_right + 1);
+        if (wl_on) klo = max(klo, delta + q0 - p.win_left);
     }
-    const int nt = (int)((nk + BN - 1) / BN);
+    khi = max(khi, 0LL);
+    const int t_hi = (int)((khi + BN - 1) / BN);
+    const int t_lo = klo >= khi ? t_hi : (int)(klo / BN);
+    // Tiles whose every key is allowed for every row: [tf_lo, tf_hi).
+    long long kf_hi = Tkv, kf_lo = 0;
+    if (causal) kf_hi = min(kf_hi, q0 + delta + 1);
+    if (wr_on) kf_hi = min(kf_hi, q0 + delta + p.win_right + 1);
+    if (wl_on) kf_lo = max(kf_lo, qlast + delta - p.win_left);
+    const long long tf_lo = (kf_lo + BN - 1) / BN;
+    const long long tf_hi = kf_hi < 0 ? 0 : kf_hi / BN;
+    const bool force_mask = noskip || p.amask != nullptr || (p.kpm && !p.kpm_list);
     // The live-tile list is read-only for this kernel: constant address space,
     // so its entries come in through scalar loads (a vector load would need a
     // vmcnt wait, which would also wait for the tile loads in flight).
     typedef const __attribute__((address_space(4))) int* cint_ptr;
-    const cint_ptr klist =
+    cint_ptr klist =
         (p.kpm_list && !noskip) ? (cint_ptr)(p.kpm_list + (long long)b * p.kpm_list_stride) : nullptr;
-    // Leading tiles with every key allowed for every row of the workgroup.
-    long long nfull = Tkv / BN;
-    if (causal) {
-        const long long lim = q0 + delta + 1;
-        const long long f = lim < 0 ? 0 : lim / BN;
-        nfull = f < nfull ? f : nfull;
-    }
-    if (klist) nfull = klist[1] < nfull ? klist[1] : nfull;
-    if (noskip || p.amask || (p.kpm && !klist)) nfull = 0;
-    const int n_full = (int)(nfull < nt ? nfull : nt);
-
-    auto tile_at = [&](int i) -> int { return klist ? (int)((uint32_t)klist[2 + i] & ~kTileClean) : i; };
-    auto clean_at = [&](int i) -> bool { return klist ? ((uint32_t)klist[2 + i] & kTileClean) != 0 : p.kpm == nullptr; };
-    // Number of tiles to visit: the live list is increasing, so cut it at nt.
-    int ntiles = nt;
+    int ntiles = t_hi - t_lo;
     if (klist) {
-        int lo = 0, hi = klist[0];   // first list entry >= nt
+        // list positions of the first live tile >= t_lo and >= t_hi
+        auto first_at_least = [&](int t) {
+            int lo = 0, hi = klist[0];
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((int)((uint32_t)klist[2 + mid] & ~kTileClean) < t) lo = mid + 1;
+                else hi = mid;
+            }
+            return lo;
+        };
+        const int i0 = first_at_least(t_lo);
+        ntiles = first_at_least(t_hi) - i0;
+        klist += i0;
+    }
+    auto tile_at = [&](int i) -> int { return klist ? (int)((uint32_t)klist[2 + i] & ~kTileClean) : t_lo + i; };
+    auto clean_at = [&](int i) -> bool { return klist ? ((uint32_t)klist[2 + i] & kTileClean) != 0 : p.kpm == nullptr; };
+    // Without a window the entirely allowed tiles are the leading ones: the
+    // first list entries are the clean tiles 0, 1, ... before the first
+    // tile with a padded key.
+    int n_full = 0;
+    if constexpr (!WIN) {
+        long long nf = tf_hi;
+        if (klist) nf = min(nf, (long long)klist[1]);
+        n_full = force_mask ? 0 : (int)min(nf, (long long)ntiles);
+    }
+    auto full_at = [&](int i) -> bool {
+        if constexpr (!WIN) {
+            return i < n_full;
+        } else {
+            const int t = tile_at(i);
+            return !force_mask && t >= tf_lo && t < tf_hi && clean_at(i);
+        }
+    };
+    // Tiles [w_first, n_act) hold allowed keys for some row of this wave
+    // (causal order and the window cut both ends); the others are skipped by
+    // this wave.
+    auto first_tile_after = [&](long long key) {   // first list position whose tile starts after key
+        int lo = 0, hi = ntiles;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if (tile_at(mid) < nt) lo = mid + 1;
+            if ((long long)tile_at(mid) * BN <= key) lo = mid + 1;
             else hi = mid;
         }
-        ntiles = lo;
-    }
-    // Tiles [0, n_act) hold allowed keys for some row of this wave (the
-    // leading full tiles, then up to the last tile the wave's causal limit
-    // reaches); the rest are skipped by this wave.
-    int n_act = ntiles;
+        return lo;
+    };
+    int n_act = ntiles, w_first = 0;
     if (!wvalid) {
-        n_act = n_full;
-    } else if (causal && !noskip) {
-        const long long lim = (long long)qwlast + delta;   // last allowed key of the wave
-        int lo = n_full, hi = ntiles;                        // first tile with key0 > lim
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if ((long long)tile_at(mid) * BN <= lim) lo = mid + 1;
-            else hi = mid;
+        n_act = 0;
+    } else if (!noskip) {
+        if (causal || wr_on) {
+            long long lim = causal ? (long long)qwlast + delta : (long long)Tkv;
+            if (wr_on) lim = min(lim, (long long)qwlast + delta + p.win_right);
+            n_act = first_tile_after(lim);
         }
-        n_act = lo;
+        if constexpr (WIN) {
+            if (wl_on) w_first = first_tile_after(qw0 + delta - p.win_left - BN);
+        }
     }
+    const float ab = ALIBI ? -p.alibi[h] * p.sqrt_d : 0.f;
 
     // ---- per-lane constants
     // LDS operand offsets (bytes within a tile)
@@ -364,11 +412,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
         TileMask mk{63, ~0ull, nullptr};
         const int key0 = tile_at(i) * BN;
         long long thr = (long long)Tkv - key0 - 1;
-        if (causal) {
-            const long long c = (long long)qi + delta - key0;
-            thr = c < thr ? c : thr;
-        }
+        if (causal) thr = min(thr, (long long)qi + delta - key0);
+        if (wr_on) thr = min(thr, (long long)qi + delta + p.win_right - key0);
         mk.thr4 = (int)(thr < -1 ? -1 : (thr > 63 ? 63 : thr)) - 4 * hh;
+        if (wl_on) {
+            const long long lo = (long long)qi + delta - p.win_left - key0;
+            mk.lo4 = (int)(lo < -1 ? -1 : (lo > 64 ? 64 : lo)) - 4 * hh;
+        }
         uint64_t km = ~0ull;
         if (kpm_row && !clean_at(i)) {
             const bool okk = key0 + lane < Tkv && kpm_row[key0 + lane] == 0;
@@ -396,7 +446,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     } else {
         wait_barrier<0>();
     }
-    if (n_act > 0) scores<D>(smem, koff, qreg, s0, s1);
+    if (n_act > 0 && w_first == 0) scores<D>(smem, koff, qreg, s0, s1);
 
     // One tile: softmax of the scores in (c0, c1), scores of the next tile
     // into (x0, x1), O += V P.  Called with the two register sets swapped on
@@ -404,8 +454,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     auto step = [&](int i, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1) {
         const bool more = i + 3 < ntiles;
         if (more) issue(i + 3);
-        if (i < n_act) {
-            if (i >= n_full) apply_mask(c0, c1, tile_mask(i));
+        if (i >= w_first && i < n_act) {
+            if (!full_at(i)) apply_mask(c0, c1, tile_mask(i));
+            if (ALIBI) add_alibi(c0, c1, (float)((long long)qi + delta - (long long)tile_at(i) * BN - 4 * hh), ab);
             update_max<D>(c0, c1, o, m_i, l_i, sl2);
             const float nm = (m_i == -INFINITY) ? 0.f : -m_i;
             bf16x8 pb[4];
@@ -417,6 +468,11 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
             exp_and_next<D>(c0, c1, nm, sl2, l_i, pb, smem + ((i + 1) % NSLOT) * G::SLOT, koff, qreg, x0, x1);
             accumulate_pv<D>(smem + (i % NSLOT) * G::SLOT + G::TILE, voff, pb, o);
             __builtin_amdgcn_s_setprio(0);
+        } else if constexpr (WIN) {
+            if (i + 1 == w_first && w_first < n_act) {
+                // first tile of a wave whose window starts later: its scores only
+                scores<D>(smem + ((i + 1) % NSLOT) * G::SLOT, koff, qreg, x0, x1);
+            }
         }
         // tile i + 2 resident for every wave; tile i + 3 may stay in flight
         if (more) wait_barrier<PT>();
@@ -485,12 +541,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     if (lse_ptr && hh == 0) *lse_ptr = lse_b;
 }
 
-template <int D>
+template <int D, bool ALIBI, bool WIN>
 hipError_t launch(const FwdParams& p, hipStream_t s) {
     using G = Geo<D>;
     static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_bf16_kernel<D>,
+        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_bf16_kernel<D, ALIBI, WIN>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
@@ -498,7 +554,7 @@ hipError_t launch(const FwdParams& p, hipStream_t s) {
     FwdParams q = p;
     q.n_qtiles = (p.Tq + BM - 1) / BM;
     const long long grid = (long long)q.n_qtiles * p.H * p.B;
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(NT), G::LDS_BYTES, s, q);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, ALIBI, WIN>), dim3((unsigned)grid), dim3(NT), G::LDS_BYTES, s, q);
     return hipGetLastError();
 }
 
@@ -506,8 +562,13 @@ hipError_t launch(const FwdParams& p, hipStream_t s) {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s) {
     if (p.rope_k) return hipErrorInvalidValue;   // keys must arrive rotated
-    if (d == 128) return launch<128>(p, s);
-    return launch<64>(p, s);
+    const bool win = p.win_left >= 0 || p.win_right >= 0;
+    if (d == 128) {
+        if (p.alibi) return win ? launch<128, true, true>(p, s) : launch<128, true, false>(p, s);
+        return win ? launch<128, false, true>(p, s) : launch<128, false, false>(p, s);
+    }
+    if (p.alibi) return win ? launch<64, true, true>(p, s) : launch<64, true, false>(p, s);
+    return win ? launch<64, false, true>(p, s) : launch<64, false, false>(p, s);
 }
 
 }  // namespace bosa

@@ -59,19 +59,23 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(const FwdParams p) 
         o[c] = o[c + 1] = o[c + 2] = o[c + 3] = 0.f;
     }
 
+    // keys some row of the workgroup may see: [klo, nk)
+    const bool wl_on = p.win_left >= 0, wr_on = p.win_right >= 0;
     const int qlast = min(q0 + BMF, p.Tq) - 1;
-    long long nk = p.Tkv;
-    if (p.causal && !noskip) {
-        long long lim = delta + qlast + 1;
-        nk = lim < 0 ? 0 : (lim < nk ? lim : nk);
+    long long nk = p.Tkv, klo = 0;
+    if (!noskip) {
+        if (p.causal) nk = min(nk, delta + qlast + 1);
+        if (wr_on) nk = min(nk, delta + qlast + p.win_right + 1);
+        if (wl_on) klo = max(klo, delta + q0 - p.win_left);
     }
     const uint8_t* kpm_row = p.kpm ? p.kpm + b * p.kpm_bstride : nullptr;
+    const float ab = p.alibi ? -p.alibi[h] * p.sqrt_d : 0.f;
 
     float m_i = -INFINITY, l_i = 0.f;
-    for (int key0 = 0; key0 < nk; key0 += BNF) {
+    for (long long key0 = klo / BNF * BNF; key0 < nk; key0 += BNF) {
         for (int idx = lane; idx < BNF * D / 4; idx += 64) {
             const int row = idx / (D / 4), c4 = idx % (D / 4);
-            const int key = key0 + row;
+            const long long key = key0 + row;
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
             if (key < p.Tkv) {
                 kx = *(const float4*)(kg + (long long)key * rs + 4 * c4);
@@ -106,11 +110,15 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(const FwdParams p) 
                 // lane pair: the lower half's partial is added first on both lanes
                 const float other = __shfl_xor(acc, 1);
                 acc = half ? (other + acc) : (acc + other);
-                const int key = key0 + j0 + j;
+                const long long key = key0 + j0 + j;
+                const long long rel = key - qi;   // key allowed by causal order iff rel <= delta
                 bool ok = key < p.Tkv;
                 if (ok && kpm_row) ok = kpm_row[key] == 0;
-                if (ok && p.causal) ok = (long long)key - qi <= delta;
+                if (ok && p.causal) ok = rel <= delta;
+                if (ok && wr_on) ok = rel <= delta + p.win_right;
+                if (ok && wl_on) ok = rel >= delta - p.win_left;
                 if (ok && p.amask && qvalid) ok = p.amask[(long long)qi * p.amask_stride + key] == 0;
+                if (ok && p.alibi) acc = fmaf(fabsf((float)(delta - rel)), ab, acc);
                 s[j] = ok ? acc : -INFINITY;
                 mx = fmaxf(mx, s[j]);
             }

@@ -67,21 +67,24 @@ __device__ __forceinline__ s16x4 tr_read(const char* p) {
 // Exclusions of a tile that is not entirely allowed.  The key behind
 // accumulator register r of the first (second) 32-key block has local index
 // 8 (r / 4) + 4 hh + r % 4 (+ 32).  thr4 = largest allowed local index minus
-// 4 hh (causal order and the key tail); kml = the tile's 64 key-padding
-// allowed bits shifted right by 4 hh; am = attention-mask row of this lane's
-// query at the tile's first key (shifted by 4 hh), or null.
+// 4 hh (causal order, the right edge of a window and the key tail); lo4 =
+// smallest allowed local index minus 4 hh (the left edge of a window);
+// kml = the tile's 64 key-padding allowed bits shifted right by 4 hh; am =
+// attention-mask row of this lane's query at the tile's first key (shifted
+// by 4 hh), or null.
 struct TileMask {
     int thr4;
     uint64_t kml;
     const uint8_t* am;
+    int lo4 = -128;
 };
 
 __device__ __forceinline__ void apply_mask(f32x16& s0, f32x16& s1, const TileMask& mk) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int b0 = 8 * (r >> 2) + (r & 3);
-        bool ok0 = b0 <= mk.thr4 && ((mk.kml >> b0) & 1);
-        bool ok1 = b0 + 32 <= mk.thr4 && ((mk.kml >> (b0 + 32)) & 1);
+        bool ok0 = b0 <= mk.thr4 && b0 >= mk.lo4 && ((mk.kml >> b0) & 1);
+        bool ok1 = b0 + 32 <= mk.thr4 && b0 + 32 >= mk.lo4 && ((mk.kml >> (b0 + 32)) & 1);
         if (mk.am) {
             ok0 = ok0 && mk.am[b0] == 0;
             ok1 = ok1 && mk.am[b0 + 32] == 0;

@@ -102,6 +102,98 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              double rope_base, int dtype, unsigned flags, attn_stream_t stream);
 
 /*
+ * Variants of an attention call ("Transformers and Attention" #55 Longformer:
+ * sliding-window attention connects each token to nearby positions; #58
+ * ALiBi: a penalty proportional to the query-key distance, with a fixed
+ * slope per head, added to the scores before the softmax).  The pages' ring
+ * step passes the same two knobs to its attention kernel as a (left, right)
+ * window and per-head slopes (brunomaga.github.io post, "Implementation").
+ *
+ *  window_left   a key is allowed only if pos_k >= pos_q - window_left;
+ *                -1 = no limit.  Combines with causal order and the masks.
+ *  window_right  a key is allowed only if pos_k <= pos_q + window_right;
+ *                -1 = no limit.
+ *  alibi_slopes  device float32 [H], or NULL: the score of every allowed pair
+ *                becomes q.k / sqrt(d) - slope_h * |pos_q - pos_k| (absolute
+ *                positions); lse includes the penalty.
+ */
+typedef struct attn_variant {
+    long long window_left;
+    long long window_right;
+    const float* alibi_slopes;
+} attn_variant;
+
+/*
+ * attn_fwd_ex -- attn_fwd with a sliding window and/or ALiBi slopes.
+ *
+ * Same arguments and conventions as attn_fwd, plus `var` (host pointer,
+ * read during the call; NULL = attn_fwd).  Windows must be >= -1.  Tiles
+ * outside every row's window are skipped like fully masked tiles.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                int B, int H, int Tq, int Tkv, int d,
+                long long q_off, long long kv_off, int causal,
+                const uint8_t* kpm, const uint8_t* attn_mask,
+                double rope_base, int dtype, unsigned flags,
+                const attn_variant* var, attn_stream_t stream);
+
+/*
+ * attn_kv_append -- one decoding step's cache update: append the new token's
+ * key and value to a static key/value cache.
+ *
+ * "Transformers and Attention" #53 (causal key/value caching: each step
+ * computes the new token's key and value and appends them to the layer's
+ * cache) and #57 (a static cache preallocates its slots; unused slots are
+ * masked).
+ *
+ *  k_new, v_new  device (B, H, d) of dtype `dtype` (4-byte aligned for bf16,
+ *                8-byte for float32).
+ *  k_cache, v_cache  device (B, Tcap, H, d), same dtype and alignment; slot j
+ *                of row b holds the token at position j.
+ *  cache_len     device int32 [B], read and written: slot L = cache_len[b]
+ *                receives the token, then cache_len[b] = L + 1.  A row with
+ *                L >= Tcap (full) or L < 0 is left unchanged -- nothing is
+ *                written past the last slot; the caller keeps L < Tcap.
+ *  rope_base     > 0: the key is stored rotated to position L (the rotation
+ *                and rounding of attn_fwd), so cached keys are rotated once.
+ *  d             64 or 128.
+ */
+int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, int* cache_len,
+                   int B, int H, int Tcap, int d, double rope_base, int dtype, attn_stream_t stream);
+
+/*
+ * attn_decode -- attention of each row's newest token over its cache.
+ *
+ * "Transformers and Attention" #53: the new query attends over the retained
+ * and the current keys and values (work proportional to the cached length);
+ * #57: windowed layers retain a bounded history.  The keys are split into
+ * chunks folded in parallel into partial (out, lse) results, merged as
+ * attn_merge does.
+ *
+ *  q            device (B, H, d), the query of the token at position
+ *               cache_len[b] - 1 (its key and value already appended), not
+ *               rotated: with rope_base > 0 it is rotated here.  16-byte aligned.
+ *  k_cache, v_cache  device (B, Tcap, H, d) as filled by attn_kv_append
+ *               (keys stored rotated); 16-byte aligned.
+ *  cache_len    device int32 [B], values clamped to [0, Tcap]; slots
+ *               [0, cache_len[b]) are visible.  Causal order holds by
+ *               construction (no slot after the query is filled).
+ *  out          device (B, H, d): dtype `dtype`, or float32 with ATTN_OUT_F32.
+ *  lse          device float32 (B, H), or NULL.  A row with no visible slot
+ *               gives out = 0, lse = -inf.
+ *  var          NULL, or window_left (only the slots at most that many
+ *               positions before the query) and alibi_slopes as for
+ *               attn_fwd_ex; window_right has no effect (nothing after the
+ *               query is filled).
+ *  flags        0 or ATTN_OUT_F32.
+ * The call allocates a stream-ordered scratch of B * H * chunks * (d + 1)
+ * floats for the partial results and frees it on `stream`.
+ */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_len,
+                void* out, float* lse, int B, int H, int Tcap, int d, double rope_base, int dtype,
+                unsigned flags, const attn_variant* var, attn_stream_t stream);
+
+/*
  * attn_merge -- (out_a, lse_a) <- (out_a, lse_a) (+) (out_b, lse_b), in place.
  *
  * The pages call an accumulate step after every ring step without defining

@@ -147,3 +147,34 @@ def test_ring_plan_for_the_two_ring_workloads():
             assert kp0 == qp0
             total += n * (n + 1) // 2
     assert total == oracle.zigzag_pairs_closed_form(8, 8192) == 1_073_750_016
+
+
+def test_variant_and_decode_entry_points_reject_bad_arguments():
+    lib = bosa.load()
+    P = 1 << 20
+    bad_window = _lib.Variant(-2, -1, None)
+    assert lib.attn_fwd_ex(P, P, P, P, P, 1, 1, 4, 4, 64, 0, 0, 0, None, None, 0.0, _lib.ATTN_BF16, 0,
+                           ctypes.byref(bad_window), None) == _lib.ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_ex(P, P, P, P, P, 1, 1, 4, 4, 96, 0, 0, 0, None, None, 0.0, _lib.ATTN_BF16, 0,
+                           None, None) == _lib.ATTN_ERR_UNSUPPORTED
+    # decode: head dim, dtype, flags, window, NULL pointers, alignment
+    dec = lambda **kw: lib.attn_decode(kw.get("q", P), P, P, kw.get("len", P), kw.get("out", P), None,  # noqa: E731
+                                       1, 2, 16, kw.get("d", 128), 0.0, kw.get("dtype", _lib.ATTN_BF16),
+                                       kw.get("flags", 0), kw.get("var"), None)
+    assert dec(d=80) == _lib.ATTN_ERR_UNSUPPORTED
+    assert dec(dtype=3) == _lib.ATTN_ERR_UNSUPPORTED
+    assert dec(flags=_lib.ATTN_ACCUMULATE) == _lib.ATTN_ERR_INVALID_ARG
+    assert dec(var=ctypes.byref(bad_window)) == _lib.ATTN_ERR_INVALID_ARG
+    assert dec(q=None) == _lib.ATTN_ERR_INVALID_ARG
+    assert dec(len=None) == _lib.ATTN_ERR_INVALID_ARG
+    assert dec(q=P + 8) == _lib.ATTN_ERR_INVALID_ARG
+    # append: sizes, dtype, alignment, NULL pointers; empty problems do nothing
+    app = lambda **kw: lib.attn_kv_append(kw.get("k", P), P, P, P, kw.get("len", P), kw.get("B", 1), 2, 16,  # noqa: E731
+                                          kw.get("d", 64), kw.get("rope", 0.0), kw.get("dtype", _lib.ATTN_F32), None)
+    assert app(B=-1) == _lib.ATTN_ERR_INVALID_ARG
+    assert app(d=32) == _lib.ATTN_ERR_UNSUPPORTED
+    assert app(dtype=9) == _lib.ATTN_ERR_UNSUPPORTED
+    assert app(rope=-2.0) == _lib.ATTN_ERR_INVALID_ARG
+    assert app(k=None) == _lib.ATTN_ERR_INVALID_ARG
+    assert app(k=P + 4) == _lib.ATTN_ERR_INVALID_ARG
+    assert app(B=0, k=None, len=None) == 0

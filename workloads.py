@@ -48,6 +48,8 @@ class Workload:
     ring_rank: int             # which rank's share is computed
     zigzag: bool               # zigzag (2P chunks) vs contiguous (P chunks) placement
     chunk: int                 # token granularity of the seeded draws
+    decode: bool = False       # one decoding step over a static cache of T slots per row
+                               # (kpm_len_range: filled slots per row; q is one token per row)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -74,6 +76,8 @@ WORKLOADS = {
                 (12288, 16384), 1, 0, False, 4096),
     4: Workload(4, "zigzag_ring_share_bf16_h32_d128_T131072_P8_rank0_causal_rope", "bf16", 1, 32, 131072,
                 128, True, 10000.0, 1.0, None, 8, 0, True, 8192),
+    5: Workload(5, "decode_step_bf16_b8_h32_d128_cache32768_rope", "bf16", 8, 32, 32768, 128, True, 10000.0,
+                1.0, (16384, 32000), 1, 0, False, 4096, decode=True),
 }
 
 
@@ -128,6 +132,13 @@ def random_normal(shape, seed: int, dtype: torch.dtype = torch.float32, sigma: f
     if sigma != 1.0:
         x.mul_(sigma)
     return x.to(dtype)
+
+
+def alibi_slopes(H: int) -> torch.Tensor:
+    """Per-head ALiBi slopes used as test and bench inputs: the geometric
+    sequence 2^(-8 h / H), h = 1 .. H, of the ALiBi paper (the digest entry
+    only says each head has a fixed slope), as float32."""
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32)
 
 
 def random_mask(shape, seed: int, p: float) -> torch.Tensor:
