@@ -49,7 +49,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3
 TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json"),
-                 "bwd": os.path.join(ROOT, "profiles", "attn_bwd_bf16_traffic.json")}
+                 "bwd": os.path.join(ROOT, "profiles", "attn_bwd_bf16_traffic.json"),
+                 "decode": os.path.join(ROOT, "profiles", "attn_decode_bf16_traffic.json")}
 KERNEL_SOURCES = {
     "fwd": ["blockwise_online_softmax_attn_amd/csrc/fwd_bf16.hip",
             "blockwise_online_softmax_attn_amd/csrc/tile_io.h",
@@ -57,12 +58,15 @@ KERNEL_SOURCES = {
     "bwd": ["blockwise_online_softmax_attn_amd/csrc/bwd_bf16.hip",
             "blockwise_online_softmax_attn_amd/csrc/tile_io.h",
             "blockwise_online_softmax_attn_amd/csrc/common.h"],
+    "decode": ["blockwise_online_softmax_attn_amd/csrc/decode.hip",
+               "blockwise_online_softmax_attn_amd/csrc/common.h"],
 }
 # kernels whose counters make up one attention "launch" of each pass: the
 # forward kernel alone; for the backward the dQ and dK/dV kernels of one
 # sub-call together
 TRAFFIC_KERNELS = {"fwd": ("attn_fwd_bf16_kernel<128",),
-                   "bwd": ("bwd_dq_kernel<128", "bwd_dkdv_kernel<128")}
+                   "bwd": ("bwd_dq_kernel<128", "bwd_dkdv_kernel<128"),
+                   "decode": ("decode_chunk_kernel<unsigned short, 128",)}
 
 
 def log(msg: str) -> None:
@@ -270,26 +274,35 @@ def run_decode(args, w) -> dict:
     achieved = nbytes / (kms.sum() * 1e-3) / 1e9 if kms.sum() > 0 else None
     log(f"{ms:.4f} ms/step, {gbs:.0f} GB/s; decode kernel {achieved:.0f} GB/s over {len(kms)} launches "
         f"(avg {kms.mean():.4f} ms)")
+    traffic = None
+    if os.path.exists(TRAFFIC_FILES["decode"]):
+        with open(TRAFFIC_FILES["decode"]) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sources_sha256") == kernel_sources_sha("decode") and tr.get("workload") == w.name:
+            traffic = tr.get("bytes_per_launch")
     cpu = None
     if not args.no_cpu_baseline:
         import threadpoolctl
 
         import oracle
-        rows = 2
         info = threadpoolctl.threadpool_info()
         blas_threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-        kh = kc[:rows].cpu().double().numpy()
-        vh = vc[:rows].cpu().double().numpy()
-        qh = q[:rows].cpu().double().numpy()
-        lh = ln[:rows].cpu().numpy()
-        t0 = time.perf_counter()
-        oracle.decode(qh, kh, vh, lh, rope_base=w.rope_base, dtype=w.dtype)
-        dt = time.perf_counter() - t0
-        cb = int(lh.sum()) * w.H * w.d * 2 * esize
+        kh = kc.cpu().double().numpy()
+        vh = vc.cpu().double().numpy()
+        qh = q.cpu().double().numpy()
+        lh = ln.cpu().numpy()
+        # the whole decoding step (every row and head), repeated until about 10 s of host time
+        reps, dt = 0, 0.0
+        while dt < 10.0 and reps < 200:
+            t0 = time.perf_counter()
+            oracle.decode(qh, kh, vh, lh, rope_base=w.rope_base, dtype=w.dtype)
+            dt += time.perf_counter() - t0
+            reps += 1
+        cb = reps * int(lh.sum()) * w.H * w.d * 2 * esize
         cpu = {"value": cb / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
-               "sample": (f"oracle.decode of batch rows 0..{rows - 1} (all {w.H} heads, {int(lh.sum())} visible "
-                          f"slots): {cb:.3e} algorithmic bytes in {dt:.2f} s (float64 numpy, BLAS threads="
-                          f"{blas_threads}, host cpus={os.cpu_count()})")}
+               "sample": (f"oracle.decode of the whole step ({w.B} rows x {w.H} heads, {int(lh.sum())} visible "
+                          f"slots) {reps} times: {cb:.3e} algorithmic bytes in {dt:.2f} s (float64 numpy, BLAS "
+                          f"threads={blas_threads}, host cpus={os.cpu_count()})")}
         log(f"cpu baseline {cpu['value']:.3f} GB/s")
     return {
         "metric": METRIC_DECODE, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -300,7 +313,7 @@ def run_decode(args, w) -> dict:
                    "filled_range": w.kpm_len_range, "rope_base": w.rope_base, "pass": "decode",
                    "algorithmic_bytes_per_step": nbytes / args.steps},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS if achieved else None, "traffic": None,
+                     "frac": achieved / PEAK_HBM_GBS if achieved else None, "traffic": traffic,
                      "kernel": f"decode_chunk_kernel<bf16,{w.d}>", "launches": int(len(kms)),
                      "avg_launch_ms": float(kms.mean()) if len(kms) else None,
                      "bytes_per_launch": nbytes / max(len(kms), 1)},
@@ -380,7 +393,7 @@ def main() -> int:
     if args.write_traffic:
         w = workloads.WORKLOADS[args.workload]
         print(json.dumps(write_traffic(*args.write_traffic, args.copy_calibration_mib or 1024, w.name,
-                                       args.which)))
+                                       "decode" if w.decode else args.which)))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the ring on a single GPU (the ring itself is emulated "
@@ -393,6 +406,11 @@ def main() -> int:
     bosa.load()
     w = workloads.WORKLOADS[args.workload]
     if w.decode:
+        if args.copy_calibration_mib:
+            src = torch.zeros(args.copy_calibration_mib * 2 ** 18, dtype=torch.float32, device="cuda:0")
+            bosa.attn_cast(src, torch.empty_like(src))
+            torch.cuda.synchronize()
+            del src
         print(json.dumps(run_decode(args, w)), flush=True)
         return 0
     log(f"workload {w.name}: drawing inputs")
@@ -472,7 +490,7 @@ def main() -> int:
                                          f"bwd_dkdv_kernel<{w.d}>": float(kms[1::2].mean())}
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_rows} rows x {args.cpu_heads} heads")
+        log(f"cpu baseline: oracle on {args.cpu_rows // 2 if bwd else args.cpu_rows} rows x {args.cpu_heads} heads")
         cpu = cpu_baseline(w, host, args.cpu_rows // 2 if bwd else args.cpu_rows, args.cpu_heads, dout_host)
         log(f"cpu baseline {cpu['value']:.3e} TFLOP/s")
     line = {

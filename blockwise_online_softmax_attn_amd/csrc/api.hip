@@ -373,14 +373,10 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
         return fail(ATTN_ERR_INVALID_ARG, "q and the caches must be 16-byte aligned, out 4-byte");
     if ((long long)B * Tcap * H * d >= (1LL << 47)) return fail(ATTN_ERR_UNSUPPORTED, "cache too large");
     const bool bf16 = dtype == ATTN_BF16;
-    // chunks of CH slots: enough workgroups to fill the chip for any batch
-    const int gran = decode_chunk_granule(d, bf16);
+    // chunks of CH slots
     const long long bh = (long long)B * H;
-    long long nch = (8192 + bh - 1) / bh;
-    long long CH = Tcap > 0 ? (Tcap + nch - 1) / nch : gran;
-    CH = (CH + gran - 1) / gran * gran;
-    if (CH < 4LL * gran) CH = 4LL * gran;
-    nch = Tcap > 0 ? (Tcap + CH - 1) / CH : 1;
+    const long long CH = decode_chunk_size(Tcap, bh, d, bf16);
+    const long long nch = Tcap > 0 ? (Tcap + CH - 1) / CH : 1;
     if (bh * nch >= (1LL << 31) || CH >= (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
     DecodeParams p{};
     p.q = q; p.k = k_cache; p.v = v_cache; p.cache_len = cache_len; p.out = out; p.lse = lse;

@@ -167,7 +167,7 @@ struct DecodeParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s);
-int decode_chunk_granule(int d, int is_bf16);
+long long decode_chunk_size(long long Tcap, long long bh, int d, int is_bf16);
 hipError_t launch_decode_chunks(const DecodeParams& p, int d, int is_bf16, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeParams& p, int d, int out_bf16, hipStream_t s);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, int* cache_len, int B,

@@ -18,7 +18,7 @@
 // products are summed with lane exchanges; each group keeps its own running
 // max, denominator and output slice, and the groups of a workgroup are
 // combined through LDS at the end.  Four keys per group are in flight per
-// iteration.
+// iteration, loaded non-temporally (each row is read once).
 #include "common.h"
 
 namespace bosa {
@@ -27,6 +27,7 @@ namespace {
 constexpr int DW = 4;        // waves per decode workgroup
 constexpr int DT = 64 * DW;  // threads
 constexpr int DU = 4;        // keys per group per iteration
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Elt;
@@ -118,8 +119,12 @@ __global__ __launch_bounds__(DT) void decode_chunk_kernel(const DecodeParams p) 
             const int j = j0 + u * NG;
             ku[u] = vu[u] = make_uint4(0, 0, 0, 0);
             if (j < c1) {
-                ku[u] = *(const uint4*)(kb + (long long)j * rs);
-                vu[u] = *(const uint4*)(vb + (long long)j * rs);
+                // each cached row is read once per step: non-temporal loads
+                // keep it from displacing reused data in the caches
+                const u32x4v a = __builtin_nontemporal_load((const u32x4v*)(kb + (long long)j * rs));
+                const u32x4v c = __builtin_nontemporal_load((const u32x4v*)(vb + (long long)j * rs));
+                ku[u] = make_uint4(a.x, a.y, a.z, a.w);
+                vu[u] = make_uint4(c.x, c.y, c.z, c.w);
             }
         }
         float s[DU];
@@ -279,9 +284,14 @@ hipError_t launch_chunks_a(const DecodeParams& p, hipStream_t s) {
 
 }  // namespace
 
-int decode_chunk_granule(int d, int is_bf16) {
+long long decode_chunk_size(long long Tcap, long long bh, int d, int is_bf16) {
     const int epl = is_bf16 ? 8 : 4;
-    return (64 / (d / epl)) * DW * DU;   // keys one workgroup iteration covers
+    const long long gran = (64 / (d / epl)) * DW * DU;   // keys one workgroup iteration covers
+    // enough workgroups to fill the chip for any batch, at least 4 iterations each
+    const long long nch = (8192 + bh - 1) / bh;
+    long long CH = Tcap > 0 ? (Tcap + nch - 1) / nch : gran;
+    CH = (CH + gran - 1) / gran * gran;
+    return CH < 4 * gran ? 4 * gran : CH;
 }
 
 hipError_t launch_decode_chunks(const DecodeParams& p, int d, int is_bf16, hipStream_t s) {
