@@ -446,15 +446,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
         const char* St = smem + slot_of(t) * SLOT;
         const float4* lp = (const float4*)(St + LDO);
         f32x16 x = f32x16{};   // S (wave A) or dP (wave B): lane = key, register r = query 8 (r/4) + 4 hh + r%4
+        constexpr int NJ = 2 * G::NDB;
+        bf16x8 ta[NJ];         // transposed operand of the second product (dO^T or Q^T)
+        float4 la[4], lc[4];   // (lse2, delta) pairs of this lane's query rows
         if (act) {
+            // every LDS operand of this tile is requested before the first
+            // matrix instruction, so the reads overlap the products
             const char* rows = St + (roleA ? 0 : 2 * QTILE);   // Q or dO, row swizzle
-            bf16x8 ra[2];
-            ra[0] = *(const bf16x8*)(rows + roff[0]);
+            const char* trt = St + (roleA ? 3 * QTILE : QTILE);
+            bf16x8 ra[G::NC];
 #pragma unroll
-            for (int c = 0; c < G::NC; ++c) {
-                if (c + 1 < G::NC) ra[(c + 1) & 1] = *(const bf16x8*)(rows + roff[c + 1]);
-                x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[c & 1], kv[c], x, 0, 0, 0);
+            for (int c = 0; c < G::NC; ++c) ra[c] = *(const bf16x8*)(rows + roff[c]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                la[j] = lp[4 * j + 2 * hh];
+                lc[j] = lp[4 * j + 2 * hh + 1];
             }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ta[j] = tr_operand<D>(trt, toff[j % G::NDB], j / G::NDB);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int c = 0; c < G::NC; ++c) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[c], kv[c], x, 0, 0, 0);
             if (roleA) {
                 if (t < tf || t >= tail) {
                     const int qa = t * BQ;
@@ -466,15 +478,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
                         x[r] = ok ? x[r] : -INFINITY;
                     }
                 }
-                // P = exp2(s sl2 - lse2) with the row's lse2 from LDS
+                // P = exp2(s sl2 - lse2) with the row's lse2
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float4 a = lp[4 * j + 2 * hh];
-                    const float4 c = lp[4 * j + 2 * hh + 1];
-                    x[4 * j + 0] = hw_exp2(fmaf(x[4 * j + 0], sl2, -a.x));
-                    x[4 * j + 1] = hw_exp2(fmaf(x[4 * j + 1], sl2, -a.z));
-                    x[4 * j + 2] = hw_exp2(fmaf(x[4 * j + 2], sl2, -c.x));
-                    x[4 * j + 3] = hw_exp2(fmaf(x[4 * j + 3], sl2, -c.z));
+                    x[4 * j + 0] = hw_exp2(fmaf(x[4 * j + 0], sl2, -la[j].x));
+                    x[4 * j + 1] = hw_exp2(fmaf(x[4 * j + 1], sl2, -la[j].z));
+                    x[4 * j + 2] = hw_exp2(fmaf(x[4 * j + 2], sl2, -lc[j].x));
+                    x[4 * j + 3] = hw_exp2(fmaf(x[4 * j + 3], sl2, -lc[j].z));
                     xch[64 * j] = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
                 }
             }
@@ -485,27 +495,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
                 // dS = P (dP - delta)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float4 a = lp[4 * j + 2 * hh];
-                    const float4 c = lp[4 * j + 2 * hh + 1];
                     const float4 pr = xch[64 * j];
-                    x[4 * j + 0] = pr.x * (x[4 * j + 0] - a.y);
-                    x[4 * j + 1] = pr.y * (x[4 * j + 1] - a.w);
-                    x[4 * j + 2] = pr.z * (x[4 * j + 2] - c.y);
-                    x[4 * j + 3] = pr.w * (x[4 * j + 3] - c.w);
+                    x[4 * j + 0] = pr.x * (x[4 * j + 0] - la[j].y);
+                    x[4 * j + 1] = pr.y * (x[4 * j + 1] - la[j].w);
+                    x[4 * j + 2] = pr.z * (x[4 * j + 2] - lc[j].y);
+                    x[4 * j + 3] = pr.w * (x[4 * j + 3] - lc[j].w);
                 }
             }
             // dV^T += dO^T P (wave A) or dK^T += Q^T dS (wave B)
             const bf16x8 xb[2] = {pack8(x, 0), pack8(x, 1)};
-            const char* trt = St + (roleA ? 3 * QTILE : QTILE);
-            constexpr int NJ = 2 * G::NDB;
-            bf16x8 ta[2];
-            ta[0] = tr_operand<D>(trt, toff[0], 0);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int kc = j / G::NDB, db = j % G::NDB;
-                if (j + 1 < NJ) ta[(j + 1) & 1] = tr_operand<D>(trt, toff[(j + 1) % G::NDB], (j + 1) / G::NDB);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[j & 1], xb[kc], acc[db], 0, 0, 0);
-            }
+            for (int j = 0; j < NJ; ++j)
+                acc[j % G::NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[j], xb[j / G::NDB], acc[j % G::NDB], 0, 0, 0);
         }
         if (t + 3 < nqt) wait_barrier<2 * PT>();
         else if (t + 2 < nqt) wait_barrier<PT>();
