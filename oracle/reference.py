@@ -230,7 +230,8 @@ def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=No
 
 
 def sdpa_backward(q, k, v, dout, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=None,
-                  rope_base: float = 0.0, dtype: str = "bf16") -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                  rope_base: float = 0.0, dtype: str = "bf16", window=(-1, -1),
+                  alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Gradients dq, dk, dv of L = sum_i dout_i . out_i for the ``sdpa``
     forward with the same arguments.
 
@@ -249,7 +250,9 @@ def sdpa_backward(q, k, v, dout, q_pos, kv_pos, *, causal: bool = False, kpm=Non
     and with RoPE dq = R(pos)^T dq', dk = R(pos)^T dk' (the rotation is
     orthogonal).  The rounding of the rotated operands to the input dtype is
     passed through unchanged (its derivative is taken as the identity).
-    A row with no allowed key contributes nothing.
+    A row with no allowed key contributes nothing.  A window removes pairs
+    like a mask; an ALiBi penalty enters P only (it does not depend on q or
+    k), so both carry over from ``sdpa`` unchanged.
 
     Shapes as in ``sdpa``; dout is (B, Tq, H, d_v).  Returns float64 dq
     (B, Tq, H, d), dk (B, Tkv, H, d), dv (B, Tkv, H, d_v).
@@ -266,7 +269,7 @@ def sdpa_backward(q, k, v, dout, q_pos, kv_pos, *, causal: bool = False, kpm=Non
     if rope_base > 0:
         qr = _rotated(q, q_pos, rope_base, dtype)
         kr = _rotated(k, kv_pos, rope_base, dtype)
-    allowed = _allowed(B, Tq, Tkv, q_pos, kv_pos, causal, kpm, attn_mask)
+    allowed = _allowed(B, Tq, Tkv, q_pos, kv_pos, causal, kpm, attn_mask, window)
     scale = 1.0 / math.sqrt(d)
     dq = np.zeros_like(qr)
     dk = np.zeros_like(kr)
@@ -276,6 +279,8 @@ def sdpa_backward(q, k, v, dout, q_pos, kv_pos, *, causal: bool = False, kpm=Non
         has = ok.any(axis=1)
         for h in range(H):
             s = scale * (qr[b, :, h, :] @ kr[b, :, h, :].T)
+            if alibi_slopes is not None:
+                s = s + alibi_bias(q_pos, kv_pos, alibi_slopes[h])
             m = np.where(has, np.max(np.where(ok, s, NEG_INF), axis=1) if Tkv else 0.0, 0.0)
             with np.errstate(over="ignore"):
                 e = np.where(ok, np.exp(s - m[:, None]), 0.0)

@@ -40,12 +40,16 @@ def _fd_grad(x, f, h=1e-6):
     dict(causal=True, q_off=2, kv_off=1, rope_base=100.0),
     dict(causal=False, kpm=np.array([[0, 1, 0, 0, 1, 0]], np.uint8), rope_base=50.0),
     dict(causal=True, q_off=4, kv_off=0, attn_mask=(np.arange(30).reshape(5, 6) % 4 == 1).astype(np.uint8)),
+    dict(causal=False, q_off=2, kv_off=0, window=(2, 1)),
+    dict(causal=True, q_off=3, kv_off=1, window=(3, -1), alibi_slopes=[0.5, 0.125], rope_base=100.0),
+    dict(causal=False, alibi_slopes=[0.25, 1.0]),
 ])
 def test_finite_differences(case):
     """Central differences of the forward definition in float64 (exact
     rotation, no rounding): catches a dropped row-sum term, a sign or scale
     error, transposed dS, a wrong RoPE back-rotation, gradients leaking
-    through masked pairs."""
+    through masked pairs or pairs outside a window, an ALiBi penalty left
+    out of P."""
     B, Tq, Tkv, H, d = 1, 5, 6, 2, 4
     q = _rand((B, Tq, H, d), 1)
     k = _rand((B, Tkv, H, d), 2)
