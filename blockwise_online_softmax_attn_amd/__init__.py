@@ -238,10 +238,12 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
              lse: torch.Tensor, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
              dv: Optional[torch.Tensor] = None, *, q_off: int = 0, kv_off: int = 0, causal: bool = False,
              kpm: Optional[torch.Tensor] = None, attn_mask: Optional[torch.Tensor] = None, rope_base: float = 0.0,
-             flags: int = 0, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+             flags: int = 0, window=None, alibi_slopes: Optional[torch.Tensor] = None,
+             stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dq, dk, dv of sum(dout * out) for the attn_fwd call with the same
     arguments (see attn_bwd in attn.h).  bf16 inputs; gradients bf16, or
-    float32 with ATTN_OUT_F32 (ATTN_ACCUMULATE adds into dq, dk, dv)."""
+    float32 with ATTN_OUT_F32 (ATTN_ACCUMULATE adds into dq, dk, dv).
+    window / alibi_slopes as for attn_fwd select attn_bwd_ex."""
     load()
     B, Tq, H, d = q.shape
     Tkv = k.shape[1]
@@ -264,11 +266,15 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
         raise ValueError("kpm must be uint8 (B, Tkv)")
     if attn_mask is not None and (attn_mask.shape != (Tq, Tkv) or attn_mask.dtype != torch.uint8):
         raise ValueError("attn_mask must be uint8 (Tq, Tkv)")
-    rc = load().attn_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"),
-                         _dev(lse, "lse", torch.float32), _dev(dq, "dq", gdt), _dev(dk, "dk", gdt),
-                         _dev(dv, "dv", gdt), B, H, Tq, Tkv, d, int(q_off), int(kv_off), 1 if causal else 0,
-                         _dev(kpm, "kpm"), _dev(attn_mask, "attn_mask"), float(rope_base), ATTN_BF16, int(flags),
-                         _stream(stream))
+    args = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"),
+            _dev(lse, "lse", torch.float32), _dev(dq, "dq", gdt), _dev(dk, "dk", gdt), _dev(dv, "dv", gdt),
+            B, H, Tq, Tkv, d, int(q_off), int(kv_off), 1 if causal else 0, _dev(kpm, "kpm"),
+            _dev(attn_mask, "attn_mask"), float(rope_base), ATTN_BF16, int(flags))
+    var, _keep = _variant(window, alibi_slopes, H)
+    if var is None:
+        rc = load().attn_bwd(*args, _stream(stream))
+    else:
+        rc = load().attn_bwd_ex(*args, var, _stream(stream))
     check(rc)
     return dq, dk, dv
 

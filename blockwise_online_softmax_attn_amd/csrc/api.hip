@@ -177,6 +177,8 @@ struct BwdCall {
     unsigned flags;
     long long q_bstride, kv_bstride, kpm_bstride, lse_bstride;
     int lse_hstride, amask_stride;
+    long long win_left = -1, win_right = -1;
+    const float* alibi = nullptr;
 };
 
 // Enqueue the dQ and dK/dV kernels of one sub-call; `list` is scratch of
@@ -194,6 +196,10 @@ int enqueue_bwd(const BwdCall& c, int* list, hipStream_t s) {
     p.flags = c.flags;
     p.scale = (float)(1.0 / std::sqrt((double)c.d));
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.d));
+    p.win_left = c.win_left;
+    p.win_right = c.win_right;
+    p.alibi = c.alibi;
+    p.sqrt_d = (float)std::sqrt((double)c.d);
     hipError_t e;
     if (list) {
         const int ntk = (c.Tkv + kTile - 1) / kTile;
@@ -588,7 +594,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              void* dq, void* dk, void* dv, int B, int H, int Tq, int Tkv, int d, long long q_off, long long kv_off,
              int causal, const uint8_t* kpm, const uint8_t* attn_mask, double rope_base, int dtype, unsigned flags,
              attn_stream_t stream) {
+    return attn_bwd_ex(q, k, v, out, dout, lse, dq, dk, dv, B, H, Tq, Tkv, d, q_off, kv_off, causal, kpm, attn_mask,
+                       rope_base, dtype, flags, nullptr, stream);
+}
+
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                void* dq, void* dk, void* dv, int B, int H, int Tq, int Tkv, int d, long long q_off,
+                long long kv_off, int causal, const uint8_t* kpm, const uint8_t* attn_mask, double rope_base,
+                int dtype, unsigned flags, const attn_variant* var, attn_stream_t stream) {
     g_err.clear();
+    if (var && (var->window_left < -1 || var->window_right < -1))
+        return fail(ATTN_ERR_INVALID_ARG, "window sizes must be >= -1");
     if (int rc = check_sizes(B, H, Tq, Tkv, d)) return rc;
     if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass supports bf16 inputs only");
     if (int rc = check_bf16_rows(dtype, H, d)) return rc;
@@ -671,6 +687,11 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
         if (e != hipSuccess) return hip_fail(e, "rotary launch");
     }
     BwdCall c{};
+    if (var) {
+        c.win_left = var->window_left;
+        c.win_right = var->window_right;
+        c.alibi = var->alibi_slopes;
+    }
     c.q = rope ? qr : q; c.k = rope ? kr : k; c.v = v; c.dout = dout; c.ld2 = ld2;
     c.dq = gq; c.dk = gk; c.dv = gv;
     c.B = B; c.H = H; c.Tq = Tq; c.Tkv = Tkv; c.d = d; c.q_off = q_off; c.kv_off = kv_off; c.causal = causal;

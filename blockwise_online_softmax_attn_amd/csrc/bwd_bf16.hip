@@ -103,7 +103,9 @@ __device__ __forceinline__ int xcd_order(int bid) {
 }
 
 // ============================================================== dQ
-template <int D>
+// VAR: a sliding window and/or ALiBi slopes (compile-time switch; without
+// them every window term folds away).
+template <int D, bool VAR>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     using G = BG<D>;
     constexpr int BN = 64, NW = 8, BM = 32 * NW, NSL = 3;
@@ -153,51 +155,84 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     if (qvalid) ld = p.ld2[b * p.lse_bstride + (long long)h * p.lse_hstride + qi];
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): only tile loads are counted below
 
-    // key tiles (as in the forward kernel)
+    // key tiles (as in the forward kernel): the keys some row of the
+    // workgroup may see are [klo, khi)
+    const bool wl_on = VAR && p.win_left >= 0, wr_on = VAR && p.win_right >= 0;
     const int qlast = min(q0 + BM, Tq) - 1;
-    long long nk = Tkv;
-    if (causal && !noskip) {
-        const long long lim = delta + qlast + 1;
-        nk = lim < 0 ? 0 : (lim < nk ? lim : nk);
+    long long khi = Tkv, klo = 0;
+    if (!noskip) {
+        if (causal) khi = min(khi, delta + qlast + 1);
+        if (wr_on) khi = min(khi, delta + qlast + p.win_right + 1);
+        if (wl_on) klo = max(klo, delta + q0 - p.win_left);
     }
-    const int nt = (int)((nk + BN - 1) / BN);
+    khi = max(khi, 0LL);
+    const int nt = (int)((khi + BN - 1) / BN);
+    const int t_lo = klo >= khi ? nt : (int)(klo / BN);
+    // tiles whose every key is allowed for every row: [tf_lo, tf_hi)
+    long long kf_hi = Tkv, kf_lo = 0;
+    if (causal) kf_hi = min(kf_hi, q0 + delta + 1);
+    if (wr_on) kf_hi = min(kf_hi, q0 + delta + p.win_right + 1);
+    if (wl_on) kf_lo = max(kf_lo, qlast + delta - p.win_left);
+    const long long tf_lo = (kf_lo + BN - 1) / BN;
+    const long long tf_hi = kf_hi < 0 ? 0 : kf_hi / BN;
+    const bool force_mask = noskip || p.amask != nullptr || (p.kpm && !p.kpm_list);
     typedef const __attribute__((address_space(4))) int* cint_ptr;
-    const cint_ptr klist =
-        (p.kpm_list && !noskip) ? (cint_ptr)(p.kpm_list + (long long)b * p.kpm_list_stride) : nullptr;
-    long long nfull = Tkv / BN;
-    if (causal) {
-        const long long lim = q0 + delta + 1;
-        const long long f = lim < 0 ? 0 : lim / BN;
-        nfull = f < nfull ? f : nfull;
-    }
-    if (klist) nfull = klist[1] < nfull ? klist[1] : nfull;
-    if (noskip || p.amask || (p.kpm && !klist)) nfull = 0;
-    const int n_full = (int)(nfull < nt ? nfull : nt);
-    auto tile_at = [&](int i) -> int { return klist ? (int)((uint32_t)klist[2 + i] & ~kTileClean) : i; };
-    auto clean_at = [&](int i) -> bool { return klist ? ((uint32_t)klist[2 + i] & kTileClean) != 0 : p.kpm == nullptr; };
-    int ntiles = nt;
+    cint_ptr klist = (p.kpm_list && !noskip) ? (cint_ptr)(p.kpm_list + (long long)b * p.kpm_list_stride) : nullptr;
+    int ntiles = nt - t_lo;
     if (klist) {
-        int lo = 0, hi = klist[0];
+        auto first_at_least = [&](int t) {
+            int lo = 0, hi = klist[0];
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((int)((uint32_t)klist[2 + mid] & ~kTileClean) < t) lo = mid + 1;
+                else hi = mid;
+            }
+            return lo;
+        };
+        const int i0 = first_at_least(t_lo);
+        ntiles = first_at_least(nt) - i0;
+        klist += i0;
+    }
+    auto tile_at = [&](int i) -> int { return klist ? (int)((uint32_t)klist[2 + i] & ~kTileClean) : t_lo + i; };
+    auto clean_at = [&](int i) -> bool { return klist ? ((uint32_t)klist[2 + i] & kTileClean) != 0 : p.kpm == nullptr; };
+    int n_full = 0;   // without a window the entirely allowed tiles are the leading ones
+    if constexpr (!VAR) {
+        long long nf = tf_hi;
+        if (klist) nf = min(nf, (long long)klist[1]);
+        n_full = force_mask ? 0 : (int)min(nf, (long long)ntiles);
+    }
+    auto full_at = [&](int i) -> bool {
+        if constexpr (!VAR) {
+            return i < n_full;
+        } else {
+            const int t = tile_at(i);
+            return !force_mask && t >= tf_lo && t < tf_hi && clean_at(i);
+        }
+    };
+    auto first_tile_after = [&](long long key) {   // first list position whose tile starts after key
+        int lo = 0, hi = ntiles;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if (tile_at(mid) < nt) lo = mid + 1;
+            if ((long long)tile_at(mid) * BN <= key) lo = mid + 1;
             else hi = mid;
         }
-        ntiles = lo;
-    }
-    int n_act = ntiles;
+        return lo;
+    };
+    // tiles [w_first, n_act) hold allowed keys for some row of this wave
+    int n_act = ntiles, w_first = 0;
     if (!wvalid) {
-        n_act = n_full;
-    } else if (causal && !noskip) {
-        const long long lim = (long long)qwlast + delta;
-        int lo = n_full, hi = ntiles;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if ((long long)tile_at(mid) * BN <= lim) lo = mid + 1;
-            else hi = mid;
+        n_act = 0;
+    } else if (!noskip) {
+        if (causal || wr_on) {
+            long long lim = causal ? (long long)qwlast + delta : (long long)Tkv;
+            if (wr_on) lim = min(lim, (long long)qwlast + delta + p.win_right);
+            n_act = first_tile_after(lim);
         }
-        n_act = lo;
+        if constexpr (VAR) {
+            if (wl_on) w_first = first_tile_after(qw0 + delta - p.win_left - BN);
+        }
     }
+    const float ab = (VAR && p.alibi) ? -p.alibi[h] * p.sqrt_d : 0.f;
 
     uint32_t roff[G::NC], toff[G::NDB];
     lane_offsets<D>(lane, roff, toff);
@@ -228,11 +263,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
         TileMask mk{63, ~0ull, nullptr};
         const int key0 = tile_at(i) * BN;
         long long thr = (long long)Tkv - key0 - 1;
-        if (causal) {
-            const long long c = (long long)qi + delta - key0;
-            thr = c < thr ? c : thr;
-        }
+        if (causal) thr = min(thr, (long long)qi + delta - key0);
+        if (wr_on) thr = min(thr, (long long)qi + delta + p.win_right - key0);
         mk.thr4 = (int)(thr < -1 ? -1 : (thr > 63 ? 63 : thr)) - 4 * hh;
+        if (wl_on) {
+            const long long lo = (long long)qi + delta - p.win_left - key0;
+            mk.lo4 = (int)(lo < -1 ? -1 : (lo > 64 ? 64 : lo)) - 4 * hh;
+        }
         uint64_t km = ~0ull;
         if (kpm_row && !clean_at(i)) {
             const bool okk = key0 + lane < Tkv && kpm_row[key0 + lane] == 0;
@@ -257,7 +294,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     for (int i = 0; i < ntiles; ++i) {
         const bool more = i + 2 < ntiles;
         if (more) issue(i + 2);
-        if (i < n_act) {
+        if (i >= w_first && i < n_act) {
             const char* St = smem + slot_of(i) * SLOT;
             f32x16 s0 = f32x16{}, s1 = f32x16{}, d0 = f32x16{}, d1 = f32x16{};
 #pragma unroll
@@ -271,7 +308,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
                 d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, oreg[c], d0, 0, 0, 0);
                 d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, oreg[c], d1, 0, 0, 0);
             }
-            if (i >= n_full) apply_mask(s0, s1, tile_mask(i));
+            if (!full_at(i)) apply_mask(s0, s1, tile_mask(i));
+            if (VAR && p.alibi) add_alibi(s0, s1, (float)((long long)qi + delta - (long long)tile_at(i) * BN - 4 * hh), ab);
             // dS^T = P^T (dP^T - delta), P^T = exp2(s sl2 - lse2); lane = query
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -326,7 +364,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
 // taking P (float32) from wave A through LDS.  Each wave holds one operand
 // (K or V) and one accumulator (dV^T or dK^T), so two waves fit per SIMD;
 // waves w and w + 4 share a SIMD, one of each role.
-template <int D>
+template <int D, bool VAR>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     using G = BG<D>;
     constexpr int NW = 8, BK = 128, BQ = 32, NSL = 4;
@@ -375,23 +413,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
-    // Query tiles: from the first that can see key k0 to the end.
+    // Query tiles: [t0, t_end) for the workgroup, [tw0, tw_end) for this wave.
+    // Key j pairs with queries lb(j) .. ub(j) (local indices): causal order
+    // or the right edge of a window bound them below, the left edge above.
     const int nqt = (Tq + BQ - 1) / BQ;
-    int t0 = 0;
-    if (causal && !noskip) {
-        const long long first = (long long)k0 - delta;
-        t0 = first <= 0 ? 0 : (first >= Tq ? nqt : (int)(first / BQ));
-    }
-    int tw0 = t0, tf = 0;
+    const bool wl_on = VAR && p.win_left >= 0, wr_on = VAR && p.win_right >= 0;
+    auto lb = [&](long long j) -> long long {
+        return causal ? j - delta : (wr_on ? j - delta - p.win_right : 0);
+    };
+    auto ub = [&](long long j) -> long long { return wl_on ? j - delta + p.win_left : (long long)Tq - 1; };
+    auto tile_of = [&](long long i) -> int { return i <= 0 ? 0 : (i >= Tq ? nqt : (int)(i / BQ)); };
+    auto tile_end = [&](long long i) -> int { return i < 0 ? 0 : (i >= Tq ? nqt : (int)(i / BQ) + 1); };
+    const int t0 = noskip ? 0 : tile_of(lb(k0));
+    const int t_end = (noskip || !wl_on) ? nqt : tile_end(ub((long long)k0 + BK - 1));
+    const int tw0 = noskip ? 0 : tile_of(lb(kw0));
+    const int tw_end = (noskip || !wl_on) ? nqt : tile_end(ub((long long)kw0 + 31));
+    // tiles with every pair of this wave allowed: [tf, tf_hi), before the ragged tail
+    int tf = 0, tf_hi = nqt;
     {
-        const long long first = (long long)kw0 - delta;
-        if (causal && !noskip) tw0 = first <= 0 ? 0 : (first >= Tq ? nqt : (int)(first / BQ));
-        const long long full = (long long)kw0 + 31 - delta;
-        tf = !causal ? 0 : (full <= 0 ? 0 : (int)((full + BQ - 1) / BQ));
+        const long long full = lb((long long)kw0 + 31);
+        tf = full <= 0 ? 0 : (int)((full + BQ - 1) / BQ);
+        if (wl_on) {
+            const long long u = ub(kw0) + 1;
+            tf_hi = u <= 0 ? 0 : (int)min((long long)nqt, u / BQ);
+        }
         if (p.amask || noskip) tf = nqt;
     }
     const bool wactive = kw0 < Tkv;
     const int tail = Tq % BQ ? nqt - 1 : nqt;
+    const float ab = (VAR && p.alibi) ? -p.alibi[h] * p.sqrt_d : 0.f;
 
     uint32_t roff[G::NC], toff[G::NDB];
     lane_offsets<D>(lane, roff, toff);
@@ -428,7 +478,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) acc[db] = f32x16{};
 
-    const int ntl = nqt - t0;
+    const int ntl = t_end - t0;
     if (ntl > 0) issue(t0);
     if (ntl > 1) issue(t0 + 1);
     if (ntl > 2) {
@@ -439,10 +489,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     } else {
         wait_barrier<0>();
     }
-    for (int t = t0; t < nqt; ++t) {
-        const bool more = t + 3 < nqt;
+    for (int t = t0; t < t_end; ++t) {
+        const bool more = t + 3 < t_end;
         if (more) issue(t + 3);
-        const bool act = wactive && t >= tw0;   // the same for both waves of a key block
+        const bool act = wactive && t >= tw0 && t < tw_end;   // the same for both waves of a key block
         const char* St = smem + slot_of(t) * SLOT;
         const float4* lp = (const float4*)(St + LDO);
         f32x16 x = f32x16{};   // S (wave A) or dP (wave B): lane = key, register r = query 8 (r/4) + 4 hh + r%4
@@ -468,12 +518,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
             for (int c = 0; c < G::NC; ++c) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[c], kv[c], x, 0, 0, 0);
             if (roleA) {
-                if (t < tf || t >= tail) {
+                if (VAR && p.alibi) {
+                    // penalty ab |pos_q - pos_k| on every score of the tile
+                    const float base = (float)((long long)t * BQ + 4 * hh + delta - kj);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        x[r] = fmaf(fabsf(base + (float)(8 * (r >> 2) + (r & 3))), ab, x[r]);
+                }
+                if (t < tf || t >= tf_hi || t >= tail) {
                     const int qa = t * BQ;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int qi = qa + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        bool ok = qi < Tq && (!causal || (long long)kj - qi <= delta);
+                        const long long rel = (long long)kj - qi;   // allowed by causal order iff rel <= delta
+                        bool ok = qi < Tq && (!causal || rel <= delta);
+                        if (wr_on) ok = ok && rel <= delta + p.win_right;
+                        if (wl_on) ok = ok && rel >= delta - p.win_left;
                         if (p.amask && ok && kvalid) ok = p.amask[(long long)qi * p.amask_stride + kj] == 0;
                         x[r] = ok ? x[r] : -INFINITY;
                     }
@@ -508,8 +568,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
             for (int j = 0; j < NJ; ++j)
                 acc[j % G::NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[j], xb[j / G::NDB], acc[j % G::NDB], 0, 0, 0);
         }
-        if (t + 3 < nqt) wait_barrier<2 * PT>();
-        else if (t + 2 < nqt) wait_barrier<PT>();
+        if (t + 3 < t_end) wait_barrier<2 * PT>();
+        else if (t + 2 < t_end) wait_barrier<PT>();
         else wait_barrier<0>();
     }
 
@@ -620,12 +680,12 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float4* __restrict__ x, l
 
 inline unsigned grid_for(long long n, int block) { return (unsigned)((n + block - 1) / block); }
 
-template <int D>
+template <int D, bool VAR>
 hipError_t launch_dq(const BwdParams& p, hipStream_t s) {
     constexpr int BM = 256, LDS = 3 * 3 * 64 * 2 * D;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        hipError_t e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D, VAR>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
@@ -633,16 +693,16 @@ hipError_t launch_dq(const BwdParams& p, hipStream_t s) {
     q.n_tiles = (p.Tq + BM - 1) / BM;
     const long long grid = (long long)q.n_tiles * p.H * p.B;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)grid), dim3(512), LDS, s, q);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, VAR>), dim3((unsigned)grid), dim3(512), LDS, s, q);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool VAR>
 hipError_t launch_dkdv(const BwdParams& p, hipStream_t s) {
     constexpr int BK = 128, LDS = 4 * (4 * 32 * 2 * D + 256) + 4 * 4096;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, VAR>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
@@ -650,18 +710,22 @@ hipError_t launch_dkdv(const BwdParams& p, hipStream_t s) {
     q.n_tiles = (p.Tkv + BK - 1) / BK;
     const long long grid = (long long)q.n_tiles * p.H * p.B;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(512), LDS, s, q);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, VAR>), dim3((unsigned)grid), dim3(512), LDS, s, q);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t s) {
-    return d == 128 ? launch_dq<128>(p, s) : launch_dq<64>(p, s);
+    const bool var = p.win_left >= 0 || p.win_right >= 0 || p.alibi;
+    if (d == 128) return var ? launch_dq<128, true>(p, s) : launch_dq<128, false>(p, s);
+    return var ? launch_dq<64, true>(p, s) : launch_dq<64, false>(p, s);
 }
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t s) {
-    return d == 128 ? launch_dkdv<128>(p, s) : launch_dkdv<64>(p, s);
+    const bool var = p.win_left >= 0 || p.win_right >= 0 || p.alibi;
+    if (d == 128) return var ? launch_dkdv<128, true>(p, s) : launch_dkdv<128, false>(p, s);
+    return var ? launch_dkdv<64, true>(p, s) : launch_dkdv<64, false>(p, s);
 }
 
 hipError_t launch_bwd_delta(const void* dout, const void* out, const float* lse, float2* ld2, int B, int H, int Tq,

@@ -141,6 +141,9 @@ struct BwdParams {
     float scale_log2;          // log2(e) / sqrt(d)
     float scale;               // 1 / sqrt(d)
     int n_tiles;               // query tiles (dq kernel) or key tiles (dk/dv kernel) per (b, h)
+    long long win_left, win_right;   // sliding window as in FwdParams; -1 = no limit
+    const float* alibi;        // [H] slopes or null
+    float sqrt_d;
 };
 
 // Entry of a live-tile list: tile index, top bit set when no key of the tile is masked.

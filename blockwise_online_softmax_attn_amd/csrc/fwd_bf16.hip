@@ -202,18 +202,6 @@ __device__ __forceinline__ void accumulate_pv(const char* Vt, const uint32_t (&v
     }
 }
 
-// ALiBi: add ab |base - key| to every score of the tile, where base =
-// (query position - position of the lane's first key) and ab = -slope sqrt(d)
-// (the penalty in units of the unscaled dot product).  Excluded scores stay -inf.
-__device__ __forceinline__ void add_alibi(f32x16& s0, f32x16& s1, float base, float ab) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const float k0 = (float)(8 * (r >> 2) + (r & 3));
-        s0[r] = fmaf(fabsf(base - k0), ab, s0[r]);
-        s1[r] = fmaf(fabsf(base - (k0 + 32.f)), ab, s1[r]);
-    }
-}
-
 template <int D, bool ALIBI, bool WIN>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p) {
     using G = Geo<D>;

@@ -94,4 +94,16 @@ __device__ __forceinline__ void apply_mask(f32x16& s0, f32x16& s1, const TileMas
     }
 }
 
+// ALiBi: add ab |base - key| to every score of the tile, where base =
+// (query position - position of the lane's first key) and ab = -slope sqrt(d)
+// (the penalty in units of the unscaled dot product).  Excluded scores stay -inf.
+__device__ __forceinline__ void add_alibi(f32x16& s0, f32x16& s1, float base, float ab) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float k0 = (float)(8 * (r >> 2) + (r & 3));
+        s0[r] = fmaf(fabsf(base - k0), ab, s0[r]);
+        s1[r] = fmaf(fabsf(base - (k0 + 32.f)), ab, s1[r]);
+    }
+}
+
 }  // namespace bosa

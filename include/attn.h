@@ -325,6 +325,19 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              attn_stream_t stream);
 
 /*
+ * attn_bwd_ex -- attn_bwd for a call made with attn_fwd_ex: the same window
+ * and ALiBi slopes (`var`, host pointer read during the call; NULL =
+ * attn_bwd).  The penalty enters P only (it does not depend on q or k) and
+ * the window removes pairs like a mask, so the gradients are those of the
+ * forward definition with the variant ("Transformers and Attention" #55, #58).
+ */
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, int B, int H, int Tq, int Tkv, int d,
+                long long q_off, long long kv_off, int causal, const uint8_t* kpm,
+                const uint8_t* attn_mask, double rope_base, int dtype, unsigned flags,
+                const attn_variant* var, attn_stream_t stream);
+
+/*
  * attn_ring_bwd -- backward of a rank's ring share (the inverse of
  * attn_ring_fwd): the sub-calls of attn_ring_plan, each computing the block
  * gradients of the local rows against one K/V block, with dq accumulated over
