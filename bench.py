@@ -12,7 +12,8 @@ value  = algorithmic TFLOP/s of the step: 4 d FLOPs per allowed (query, key)
          tiles skip is not counted.
 roofline = the attention kernel alone: the same algorithmic FLOPs divided by
          the kernel's own time, measured with HIP events recorded around every
-         launch on the launch's stream during the timed steps, against the
+         launch on the launch's stream over K further steps run after the
+         timed ones (so the events add no gaps to the step time), against the
          MI355X dense bf16 MFMA peak (2516.6 TFLOP/s).
 cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample
          of the same workload (rank 0, one GPU only).
@@ -261,17 +262,24 @@ def run_decode(args, w) -> dict:
     nbytes = sum(int((L_start + s + 1).sum()) for s in range(args.steps)) * w.H * w.d * 2 * esize
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {args.steps} decode steps")
-    with bosa.KernelTimer(max_launches=args.steps + 16) as kt:
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
-            step()
-        end.record()
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     gbs = nbytes / args.steps / (ms * 1e-3) / 1e9
+    # the decode kernel alone, timed with events around each launch over K
+    # further steps (kept out of the step time above)
+    L2 = ln.cpu().to(torch.int64)
+    nbytes_k = sum(int((L2 + s + 1).sum()) for s in range(args.steps)) * w.H * w.d * 2 * esize
+    with bosa.KernelTimer(max_launches=args.steps + 16) as kt:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
     kms = np.asarray(kt.ms, dtype=np.float64)
-    achieved = nbytes / (kms.sum() * 1e-3) / 1e9 if kms.sum() > 0 else None
+    achieved = nbytes_k / (kms.sum() * 1e-3) / 1e9 if kms.sum() > 0 else None
     log(f"{ms:.4f} ms/step, {gbs:.0f} GB/s; decode kernel {achieved:.0f} GB/s over {len(kms)} launches "
         f"(avg {kms.mean():.4f} ms)")
     traffic = None
@@ -316,7 +324,7 @@ def run_decode(args, w) -> dict:
                      "frac": achieved / PEAK_HBM_GBS if achieved else None, "traffic": traffic,
                      "kernel": f"decode_chunk_kernel<bf16,{w.d}>", "launches": int(len(kms)),
                      "avg_launch_ms": float(kms.mean()) if len(kms) else None,
-                     "bytes_per_launch": nbytes / max(len(kms), 1)},
+                     "bytes_per_launch": nbytes_k / max(len(kms), 1)},
         "cpu_baseline": cpu,
     }
 
@@ -444,14 +452,20 @@ def main() -> int:
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    # the attention kernels alone: HIP events around every launch, on the
+    # launch's stream, over K further steps (kept out of the step time above,
+    # where they would add a gap per launch)
     with bosa.KernelTimer(max_launches=args.steps * launches + 16) as kt:
-        torch.cuda.synchronize()
-        start.record()
         for _ in range(args.steps):
             step()
-        end.record()
         torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
     kms = np.asarray(kt.ms, dtype=np.float64)
     kern_ms = float(kms.sum())
