@@ -59,6 +59,11 @@ struct Scratch {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Positions are limited to |pos| <= 2^52 and lengths to 2^31, so a window
+// wider than 2^54 excludes nothing: it is passed on as "no limit" (-1),
+// which keeps the kernels' position + window sums far from overflow.
+long long window_arg(long long w) { return w > (1LL << 54) ? -1 : w; }
+
 struct Call {
     const void* q; const void* k; const void* v; void* out; float* lse;
     int B, H, Tq, Tkv, d;
@@ -308,8 +313,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
 
     Call c = plain_call(q, k, v, out, lse, B, H, Tq, Tkv, d, q_off, kv_off, causal, kpm, attn_mask, dtype, flags);
     if (var) {
-        c.win_left = var->window_left;
-        c.win_right = var->window_right;
+        c.win_left = window_arg(var->window_left);
+        c.win_right = window_arg(var->window_right);
         c.alibi = var->alibi_slopes;
     }
     hipStream_t s = (hipStream_t)stream;
@@ -388,7 +393,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     p.q = q; p.k = k_cache; p.v = v_cache; p.cache_len = cache_len; p.out = out; p.lse = lse;
     p.alibi = var ? var->alibi_slopes : nullptr;
     p.B = B; p.H = H; p.Tcap = Tcap; p.CH = (int)CH; p.n_chunks = (int)nch;
-    p.win_left = var ? var->window_left : -1;
+    p.win_left = var ? window_arg(var->window_left) : -1;
     p.log_base = rope_base > 0.0 ? std::log(rope_base) : 0.0;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     p.sqrt_d = (float)std::sqrt((double)d);
@@ -688,8 +693,8 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
     }
     BwdCall c{};
     if (var) {
-        c.win_left = var->window_left;
-        c.win_right = var->window_right;
+        c.win_left = window_arg(var->window_left);
+        c.win_right = window_arg(var->window_right);
         c.alibi = var->alibi_slopes;
     }
     c.q = rope ? qr : q; c.k = rope ? kr : k; c.v = v; c.dout = dout; c.ld2 = ld2;

@@ -285,3 +285,26 @@ def test_variant_backward_parity(case):
         e = float(np.abs(gv - r).max()) / scale
         note(f"  {name}: max|err|/max|ref| = {e:.3e}")
         assert e <= 2e-2, f"{name}: relative error {e}"
+
+
+def test_huge_windows_are_no_limit():
+    """Windows wider than any position difference (up to 2^63 - 1) exclude
+    nothing: the results equal the call without a window bit for bit, in
+    the forward, the backward and decoding."""
+    B, H, T, d = 1, 2, 200, 128
+    big = (1 << 63) - 1
+    q, k, v = (rnd((B, T, H, d), 9500 + i, torch.bfloat16) for i in range(3))
+    o1, l1 = run(q, k, v, causal=True, q_off=1000, kv_off=900)
+    o2, l2 = run(q, k, v, causal=True, q_off=1000, kv_off=900, window=(big, big))
+    o3, l3 = run(q, k, v, causal=False, window=(big, -1))
+    o4, l4 = run(q, k, v, causal=False)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+    kc = rnd((1, 300, H, d), 9510, torch.bfloat16).to(DEV)
+    vc = rnd((1, 300, H, d), 9511, torch.bfloat16).to(DEV)
+    ln = torch.tensor([257], dtype=torch.int32, device=DEV)
+    qn = rnd((1, H, d), 9512, torch.bfloat16).to(DEV)
+    a, la = bosa.attn_decode(qn, kc, vc, ln, window_left=big)
+    b2, lb = bosa.attn_decode(qn, kc, vc, ln)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b2) and torch.equal(la, lb)
