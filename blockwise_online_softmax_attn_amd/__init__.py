@@ -211,9 +211,11 @@ def attn_ring_plan(T: int, P: int, rank: int, zigzag: bool, causal: bool) -> Lis
 def attn_ring_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, P: int, rank: int, zigzag: bool,
                   causal: bool = True, kpm: Optional[torch.Tensor] = None, rope_base: float = 0.0, flags: int = 0,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                  acc: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                  acc: Optional[torch.Tensor] = None, window=None, alibi_slopes: Optional[torch.Tensor] = None,
+                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """One rank's ring-attention share: local q (B, T/P, H, d) against the
-    full k, v (B, T, H, d) in ring order, merged into (out, lse)."""
+    full k, v (B, T, H, d) in ring order, merged into (out, lse).  window /
+    alibi_slopes select attn_ring_fwd_ex."""
     load()
     B, T, H, d = k.shape
     Tl = q.shape[1]
@@ -226,10 +228,14 @@ def attn_ring_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, P: int, 
         lse = torch.empty((B, H, Tl), dtype=torch.float32, device=q.device)
     if acc is None:
         acc = out if q.dtype == torch.float32 else torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    rc = load().attn_ring_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out", q.dtype),
-                              _dev(lse, "lse", torch.float32), _dev(acc, "acc", torch.float32), B, H, T, d, P,
-                              rank, int(zigzag), int(causal), _dev(kpm, "kpm"), float(rope_base), code,
-                              int(flags), _stream(stream))
+    args = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out", q.dtype), _dev(lse, "lse", torch.float32),
+            _dev(acc, "acc", torch.float32), B, H, T, d, P, rank, int(zigzag), int(causal), _dev(kpm, "kpm"),
+            float(rope_base), code, int(flags))
+    var, _keep = _variant(window, alibi_slopes, H)
+    if var is None:
+        rc = load().attn_ring_fwd(*args, _stream(stream))
+    else:
+        rc = load().attn_ring_fwd_ex(*args, var, _stream(stream))
     check(rc)
     return out, lse
 
@@ -283,7 +289,8 @@ def attn_ring_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
                   lse: torch.Tensor, *, P: int, rank: int, zigzag: bool, causal: bool = True,
                   kpm: Optional[torch.Tensor] = None, rope_base: float = 0.0, flags: int = 0,
                   dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                  dv: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+                  dv: Optional[torch.Tensor] = None, window=None, alibi_slopes: Optional[torch.Tensor] = None,
+                  stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Backward of one rank's ring share: local q, out, dout (B, T/P, H, d),
     full k, v (B, T, H, d), lse from attn_ring_fwd.  Returns dq (local) and
     this rank's contributions dk, dv (full length)."""
@@ -298,12 +305,15 @@ def attn_ring_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
     dq = torch.empty(q.shape, dtype=gdt, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=gdt, device=q.device) if dk is None else dk
     dv = torch.empty(k.shape, dtype=gdt, device=q.device) if dv is None else dv
-    rc = load().attn_ring_bwd(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
-                              _dev(v, "v", torch.bfloat16), _dev(out, "out", torch.bfloat16),
-                              _dev(dout, "dout", torch.bfloat16), _dev(lse, "lse", torch.float32),
-                              _dev(dq, "dq", gdt), _dev(dk, "dk", gdt), _dev(dv, "dv", gdt), B, H, T, d, P, rank,
-                              int(zigzag), int(causal), _dev(kpm, "kpm"), float(rope_base), ATTN_BF16, int(flags),
-                              _stream(stream))
+    args = (_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+            _dev(out, "out", torch.bfloat16), _dev(dout, "dout", torch.bfloat16), _dev(lse, "lse", torch.float32),
+            _dev(dq, "dq", gdt), _dev(dk, "dk", gdt), _dev(dv, "dv", gdt), B, H, T, d, P, rank, int(zigzag),
+            int(causal), _dev(kpm, "kpm"), float(rope_base), ATTN_BF16, int(flags))
+    var, _keep = _variant(window, alibi_slopes, H)
+    if var is None:
+        rc = load().attn_ring_bwd(*args, _stream(stream))
+    else:
+        rc = load().attn_ring_bwd_ex(*args, var, _stream(stream))
     check(rc)
     return dq, dk, dv
 

@@ -15,7 +15,7 @@ ATTN_ACCUMULATE, ATTN_OUT_F32, ATTN_NO_TILE_SKIP = 1, 2, 4
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan", "attn_ring_fwd",
-           "attn_bwd", "attn_bwd_ex", "attn_ring_bwd", "attn_kv_append", "attn_decode", "attn_profile_start",
+           "attn_ring_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_ring_bwd", "attn_ring_bwd_ex", "attn_kv_append", "attn_decode", "attn_profile_start",
            "attn_profile_stop", "attn_last_error", "attn_version")
 
 
@@ -63,6 +63,8 @@ def load() -> ctypes.CDLL:
     var = ctypes.POINTER(Variant)
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, ll, i, vp, vp, d, i, u, var, vp]
     lib.attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, ll, ll, i, vp, vp, d, i, u, var, vp]
+    lib.attn_ring_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, d, i, u, var, vp]
+    lib.attn_ring_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, d, i, u, var, vp]
     lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, d, i, vp]
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, d, i, u, var, vp]
     lib.attn_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
@@ -75,7 +77,8 @@ def load() -> ctypes.CDLL:
     lib.attn_profile_start.argtypes = [i]
     lib.attn_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_float), i]
     for name in ("attn_fwd", "attn_fwd_ex", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan",
-                 "attn_ring_fwd", "attn_bwd", "attn_bwd_ex", "attn_ring_bwd", "attn_kv_append", "attn_decode",
+                 "attn_ring_fwd", "attn_ring_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_ring_bwd", "attn_ring_bwd_ex",
+                 "attn_kv_append", "attn_decode",
                  "attn_profile_start", "attn_profile_stop", "attn_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.attn_last_error.argtypes = []

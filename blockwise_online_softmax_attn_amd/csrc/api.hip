@@ -64,6 +64,38 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 // which keeps the kernels' position + window sums far from overflow.
 long long window_arg(long long w) { return w > (1LL << 54) ? -1 : w; }
 
+// Whether a (query block, key block) sub-call of a ring share holds any pair
+// that causal order and the window allow: the key - query position
+// differences of the pair of blocks span [lo, hi]; the allowed ones
+// [-window_left, min(0 if causal, window_right)].
+bool subcall_live(const attn_ring_call& c, int causal, long long wl, long long wr) {
+    const long long lo = c.kv_pos0 - (c.q_pos0 + c.q_rows - 1);
+    const long long hi = c.kv_pos0 + c.kv_rows - 1 - c.q_pos0;
+    long long amax = hi, amin = lo;
+    if (causal) amax = std::min(amax, 0LL);
+    if (wr >= 0) amax = std::min(amax, wr);
+    if (wl >= 0) amin = std::max(amin, -wl);
+    return amin <= amax;
+}
+
+// Remove the sub-calls no pair of which the window allows, and renumber the
+// write / accumulate order: the first remaining sub-call of a query block
+// writes its partial, the later ones merge into it.
+void drop_dead_subcalls(std::vector<attn_ring_call>& plan, int causal, long long wl, long long wr) {
+    if (wl < 0 && wr < 0) return;
+    std::vector<attn_ring_call> live;
+    bool touched[2] = {false, false};
+    for (const attn_ring_call& c : plan) {
+        if (!subcall_live(c, causal, wl, wr)) continue;
+        attn_ring_call e = c;
+        const int ph = c.q_row0 == 0 ? 0 : 1;
+        e.accumulate = touched[ph] ? 1 : 0;
+        touched[ph] = true;
+        live.push_back(e);
+    }
+    plan.swap(live);
+}
+
 struct Call {
     const void* q; const void* k; const void* v; void* out; float* lse;
     int B, H, Tq, Tkv, d;
@@ -494,7 +526,17 @@ int attn_ring_plan(int T, int P, int rank, int zigzag, int causal, attn_ring_cal
 int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse, float* acc, int B, int H, int T,
                   int d, int P, int rank, int zigzag, int causal, const uint8_t* kpm, double rope_base, int dtype,
                   unsigned flags, attn_stream_t stream) {
+    return attn_ring_fwd_ex(q, k, v, out, lse, acc, B, H, T, d, P, rank, zigzag, causal, kpm, rope_base, dtype, flags,
+                            nullptr, stream);
+}
+
+int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, float* acc, int B, int H,
+                     int T, int d, int P, int rank, int zigzag, int causal, const uint8_t* kpm, double rope_base,
+                     int dtype, unsigned flags, const attn_variant* var, attn_stream_t stream) {
     g_err.clear();
+    if (var && (var->window_left < -1 || var->window_right < -1))
+        return fail(ATTN_ERR_INVALID_ARG, "window sizes must be >= -1");
+    const long long wl = var ? window_arg(var->window_left) : -1, wr = var ? window_arg(var->window_right) : -1;
     const int n = attn_ring_plan(T, P, rank, zigzag, causal, nullptr, 0);
     if (n < 0) return -n;
     const int Tl = T / P;
@@ -509,6 +551,8 @@ int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float*
     if (int rc = check_bf16_rows(dtype, H, d)) return rc;
     std::vector<attn_ring_call> plan(n);
     attn_ring_plan(T, P, rank, zigzag, causal, plan.data(), n);
+    drop_dead_subcalls(plan, causal, wl, wr);
+    const int n_live = (int)plan.size();
 
     hipStream_t s = (hipStream_t)stream;
     const bool rope = rope_base > 0.0;
@@ -518,12 +562,12 @@ int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float*
     const size_t tab_q = rope ? align_up((size_t)Tl * (d / 2) * sizeof(float2)) : 0;
     const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(float2)) : 0;
     const size_t kbuf = krot ? align_up((size_t)B * T * H * d * 2) : 0;
-    std::vector<size_t> lst_off(n, 0);
+    std::vector<size_t> lst_off(n_live, 0);
     size_t total = tab_q + tab_k + kbuf;
-    std::vector<Call> calls(n);
+    std::vector<Call> calls(n_live);
     const int rs = H * d;
     const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
-    for (int i = 0; i < n; ++i) {
+    for (int i = 0; i < n_live; ++i) {
         const attn_ring_call& e = plan[i];
         Call c{};
         c.q = (const char*)q + (size_t)e.q_row0 * rs * esz;
@@ -535,6 +579,9 @@ int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float*
         c.q_off = e.q_pos0; c.kv_off = e.kv_pos0; c.causal = causal;
         c.kpm = kpm ? kpm + e.kv_pos0 : nullptr;
         c.amask = nullptr;
+        c.win_left = wl;
+        c.win_right = wr;
+        c.alibi = var ? var->alibi_slopes : nullptr;
         c.dtype = dtype;
         c.flags = (flags & ATTN_NO_TILE_SKIP) | ATTN_OUT_F32 | (e.accumulate ? ATTN_ACCUMULATE : 0u);
         c.q_bstride = (long long)Tl * rs;
@@ -569,7 +616,7 @@ int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float*
         }
     }
     bool covered[2] = {false, false};
-    for (int i = 0; i < n; ++i) {
+    for (int i = 0; i < n_live; ++i) {
         Call& c = calls[i];
         if (rope) {
             c.rope_q = (const float2*)wp + (size_t)plan[i].q_row0 * (d / 2);
@@ -727,7 +774,18 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
 int attn_ring_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, int B, int H, int T, int d, int P, int rank, int zigzag, int causal,
                   const uint8_t* kpm, double rope_base, int dtype, unsigned flags, attn_stream_t stream) {
+    return attn_ring_bwd_ex(q, k, v, out, dout, lse, dq, dk, dv, B, H, T, d, P, rank, zigzag, causal, kpm, rope_base,
+                            dtype, flags, nullptr, stream);
+}
+
+int attn_ring_bwd_ex(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int T, int d, int P, int rank,
+                     int zigzag, int causal, const uint8_t* kpm, double rope_base, int dtype, unsigned flags,
+                     const attn_variant* var, attn_stream_t stream) {
     g_err.clear();
+    if (var && (var->window_left < -1 || var->window_right < -1))
+        return fail(ATTN_ERR_INVALID_ARG, "window sizes must be >= -1");
+    const long long wl = var ? window_arg(var->window_left) : -1, wr = var ? window_arg(var->window_right) : -1;
     const int n = attn_ring_plan(T, P, rank, zigzag, causal, nullptr, 0);
     if (n < 0) return -n;
     const int Tl = T / P;
@@ -743,6 +801,8 @@ int attn_ring_bwd(const void* q, const void* k, const void* v, const void* out, 
         if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
     std::vector<attn_ring_call> plan(n);
     attn_ring_plan(T, P, rank, zigzag, causal, plan.data(), n);
+    drop_dead_subcalls(plan, causal, wl, wr);
+    const int n_live = (int)plan.size();
 
     hipStream_t s = (hipStream_t)stream;
     const bool rope = rope_base > 0.0;
@@ -753,9 +813,9 @@ int attn_ring_bwd(const void* q, const void* k, const void* v, const void* out, 
     const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(float2)) : 0;
     const size_t qr_b = rope ? align_up(nq * 2) : 0, kr_b = rope ? align_up(nk * 2) : 0;
     const size_t g_b = align_up(nq * 4) + 2 * align_up(nk * 4);
-    std::vector<size_t> lst_off(n, 0);
+    std::vector<size_t> lst_off(n_live, 0);
     size_t total = ld_b + tab_q + tab_k + qr_b + kr_b + g_b;
-    for (int i = 0; i < n; ++i) {
+    for (int i = 0; i < n_live; ++i) {
         lst_off[i] = total;
         total += kpm_list_bytes(kpm ? kpm + plan[i].kv_pos0 : nullptr, dtype, flags, B, plan[i].kv_rows);
     }
@@ -792,7 +852,7 @@ int attn_ring_bwd(const void* q, const void* k, const void* v, const void* out, 
         if (e != hipSuccess) return hip_fail(e, "rotary launch");
     }
     const size_t esz = 2;
-    for (int i = 0; i < n; ++i) {
+    for (int i = 0; i < n_live; ++i) {
         const attn_ring_call& pc = plan[i];
         BwdCall c{};
         c.q = (rope ? (const char*)qr : (const char*)q) + (size_t)pc.q_row0 * rs * esz;
@@ -807,6 +867,9 @@ int attn_ring_bwd(const void* q, const void* k, const void* v, const void* out, 
         c.q_off = pc.q_pos0; c.kv_off = pc.kv_pos0; c.causal = causal;
         c.kpm = kpm ? kpm + pc.kv_pos0 : nullptr;
         c.amask = nullptr;
+        c.win_left = wl;
+        c.win_right = wr;
+        c.alibi = var ? var->alibi_slopes : nullptr;
         c.flags = (flags & ATTN_NO_TILE_SKIP) | ATTN_ACCUMULATE;
         c.q_bstride = (long long)Tl * rs; c.kv_bstride = (long long)T * rs; c.kpm_bstride = T;
         c.lse_bstride = (long long)H * Tl; c.lse_hstride = Tl; c.amask_stride = 0;

@@ -288,6 +288,19 @@ int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float*
                   attn_stream_t stream);
 
 /*
+ * attn_ring_fwd_ex -- attn_ring_fwd with a sliding window and/or ALiBi slopes
+ * (`var` as for attn_fwd_ex, host pointer read during the call; NULL =
+ * attn_ring_fwd).  Sub-calls whose key block lies outside the window of
+ * every query of their block are not issued: with a window the share needs
+ * only the blocks near its queries ("Transformers and Attention" #55: with a
+ * fixed window the number of interactions grows linearly with length).
+ */
+int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, float* acc,
+                     int B, int H, int T, int d, int P, int rank, int zigzag, int causal,
+                     const uint8_t* kpm, double rope_base, int dtype, unsigned flags,
+                     const attn_variant* var, attn_stream_t stream);
+
+/*
  * attn_bwd -- attention backward: gradients of L = sum(dout * out) for the
  * attn_fwd call with the same q, k, v, positions, masks and rotary base.
  *
@@ -359,6 +372,15 @@ int attn_ring_bwd(const void* q, const void* k, const void* v, const void* out, 
                   int B, int H, int T, int d, int P, int rank, int zigzag, int causal,
                   const uint8_t* kpm, double rope_base, int dtype, unsigned flags,
                   attn_stream_t stream);
+
+/*
+ * attn_ring_bwd_ex -- attn_ring_bwd for a share computed by attn_ring_fwd_ex
+ * with the same `var` (the same sub-calls are skipped).
+ */
+int attn_ring_bwd_ex(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int T, int d, int P,
+                     int rank, int zigzag, int causal, const uint8_t* kpm, double rope_base, int dtype,
+                     unsigned flags, const attn_variant* var, attn_stream_t stream);
 
 /*
  * Kernel timing for measurement tools.  Between attn_profile_start and

@@ -308,3 +308,59 @@ def test_huge_windows_are_no_limit():
     b2, lb = bosa.attn_decode(qn, kc, vc, ln)
     torch.cuda.synchronize()
     assert torch.equal(a, b2) and torch.equal(la, lb)
+
+
+# ------------------------------------------------------------------ ring shares with variants
+def _ring_share_inputs(w, T, heads, rank):
+    P = w.ring_P
+    parts = 2 * P if w.zigzag else P
+    c = T // parts
+    ww = workloads.Workload(**{**w.__dict__, "T": T, "chunk": c})
+    k = workloads.draw_tokens(ww, 1, range(parts), heads)
+    v = workloads.draw_tokens(ww, 2, range(parts), heads)
+    qpos = oracle.local_query_positions(T, P, rank, w.zigzag)
+    qchunks = sorted(set((qpos // c).tolist()), key=lambda x: list(qpos // c).index(x))
+    q = workloads.draw_tokens(ww, 0, qchunks, heads)
+    dout = workloads.draw_tokens(ww, 3, qchunks, heads)
+    return q, k, v, dout, qpos
+
+
+@pytest.mark.parametrize("wi,T,rank,window,alibi", [
+    (2, 4096, 3, (700, -1), False),
+    (2, 4096, 2, (300, -1), True),
+    (4, 8192, 0, (1000, -1), True),
+    (4, 8192, 5, (3000, -1), False),
+])
+def test_ring_share_with_window(wi, T, rank, window, alibi):
+    """attn_ring_fwd_ex / attn_ring_bwd_ex: the share's rows against every key
+    at absolute positions with the window and penalty equal the oracle's; the
+    executor issues fewer attention launches than the full plan (sub-calls
+    whose key block lies outside every row's window are not issued)."""
+    w = workloads.WORKLOADS[wi]
+    heads = 2
+    q, k, v, dout, qpos = _ring_share_inputs(w, T, heads, rank)
+    slopes = workloads.alibi_slopes(heads) if alibi else None
+    note(f"ring {w.name} T={T} rank={rank} window={window} alibi={alibi}")
+    qd, kd, vd, od = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV)
+    sd = None if slopes is None else slopes.to(DEV)
+    n_plan = len(bosa.attn_ring_plan(T, w.ring_P, rank, w.zigzag, w.causal))
+    with bosa.KernelTimer(256) as kt:
+        out, lse = bosa.attn_ring_fwd(qd, kd, vd, P=w.ring_P, rank=rank, zigzag=w.zigzag, causal=w.causal,
+                                      rope_base=w.rope_base, window=window, alibi_slopes=sd)
+        torch.cuda.synchronize()
+    note(f"  {len(kt.ms)} attention launches of {n_plan} sub-calls in the plan")
+    assert 0 < len(kt.ms) < n_plan
+    ro, rl = oracle.sdpa(np64(q), np64(k), np64(v), qpos, np.arange(T), causal=w.causal, rope_base=w.rope_base,
+                         dtype="bf16", window=window, alibi_slopes=None if slopes is None else slopes.double().numpy())
+    compare(out.cpu(), lse.cpu(), ro, rl, "bf16", "forward")
+    grads = bosa.attn_ring_bwd(qd, kd, vd, out, od, lse, P=w.ring_P, rank=rank, zigzag=w.zigzag, causal=w.causal,
+                               rope_base=w.rope_base, window=window, alibi_slopes=sd)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa_backward(np64(q), np64(k), np64(v), np64(dout), qpos, np.arange(T), causal=w.causal,
+                               rope_base=w.rope_base, dtype="bf16", window=window,
+                               alibi_slopes=None if slopes is None else slopes.double().numpy())
+    for name, gg, r in zip(("dq", "dk", "dv"), grads, ref):
+        gv = np64(gg.cpu())
+        e = float(np.abs(gv - r).max()) / float(np.abs(r).max())
+        note(f"  {name}: max|err|/max|ref| = {e:.3e}")
+        assert np.all(np.isfinite(gv)) and e <= 2e-2, f"{name}: relative error {e}"
