@@ -37,53 +37,68 @@ struct BG {
     static constexpr int ROW = 2 * D;     // bytes per bf16 row in LDS
     static constexpr int RP = 256 / ROW;  // rows per 256-byte bank window
     static constexpr int RPB = 1024 / ROW;
-    // Stored granule position = granule ^ h(row).  hk: conflict-free 16-lane
-    // row reads (ds_read_b128); hv: conflict-free transposed reads.
-    static __device__ __forceinline__ int hk(int r) { return (r / RP) % GPR; }
-    static __device__ __forceinline__ int hv(int r) { return 4 * ((r / RP) % (GPR / 4)); }
+    // Stored granule position = granule ^ h(row), one permutation for both
+    // read patterns: it is a bijection on 16 consecutive bank windows (the
+    // 16 rows of a 16-lane ds_read_b128 hit distinct banks) and gives the 4
+    // rows of a transposed-read pass distinct groups of 4 granules.
+    static __device__ __forceinline__ int h(int r) {
+        const int w = r / RP;
+        return 4 * (w % (GPR / 4)) + (w / (GPR / 4)) % 4;
+    }
 };
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
+// Wait until at most n tiles of PT loads each are still in flight
+// (0 <= n <= N; n is wave-uniform), then synchronise the workgroup.
+template <int PT, int N>
+__device__ __forceinline__ void wait_tiles(int n) {
+    if constexpr (N == 0) {
+        wait_barrier<0>();
+    } else {
+        if (n >= N) wait_barrier<N * PT>();
+        else wait_tiles<PT, N - 1>(n);
+    }
+}
+
 // A operand of a 32x32x16 MFMA holding the transpose of 16 rows x 32 columns
 // of a row-major LDS tile (rows 16 kc .. 16 kc + 15, columns 32 db ..).
 template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(const char* tile, uint32_t voff_db, int kc) {
-    const char* p0 = tile + voff_db + (16 * kc) * BG<D>::ROW;
-    const s16x4 r0 = tr_read(p0);
-    const s16x4 r1 = tr_read(p0 + 8 * BG<D>::ROW);
+__device__ __forceinline__ bf16x8 tr_operand(const char* tile, uint2 voff_db, int kc) {
+    const char* p0 = tile + (16 * kc) * BG<D>::ROW;
+    const s16x4 r0 = tr_read(p0 + voff_db.x);
+    const s16x4 r1 = tr_read(p0 + voff_db.y);
     const s16x8 a = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
     return __builtin_bit_cast(bf16x8, a);
 }
 
 // Per-lane byte offsets of the transposed reads for each 32-column block
-// (stored with the hv swizzle), and of the row reads of granule 2c + hh of
-// row lane % 32 (stored with the hk swizzle).
+// (rows r0 and r0 + 8 of a 16-row chunk; the swizzle repeats every 16 rows),
+// and of the row reads of granule 2c + hh of row lane % 32.
 template <int D>
-__device__ __forceinline__ void lane_offsets(int lane, uint32_t (&roff)[BG<D>::NC], uint32_t (&toff)[BG<D>::NDB]) {
+__device__ __forceinline__ void lane_offsets(int lane, uint32_t (&roff)[BG<D>::NC], uint2 (&toff)[BG<D>::NDB]) {
     using G = BG<D>;
     const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
-    for (int c = 0; c < G::NC; ++c) roff[c] = l32 * G::ROW + 16 * ((2 * c + hh) ^ G::hk(l32));
+    for (int c = 0; c < G::NC; ++c) roff[c] = l32 * G::ROW + 16 * ((2 * c + hh) ^ G::h(l32));
     const int jj = lane & 15, grp = lane >> 4;
     const int r0 = 4 * (grp >> 1) + (jj >> 2);
-    const int hv = G::hv(r0);
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {
         const int g = 4 * db + 2 * (grp & 1) + ((jj & 3) >> 1);
-        toff[db] = r0 * G::ROW + 16 * (g ^ hv) + 8 * (jj & 1);
+        toff[db].x = r0 * G::ROW + 16 * (g ^ G::h(r0)) + 8 * (jj & 1);
+        toff[db].y = (r0 + 8) * G::ROW + 16 * (g ^ G::h(r0 + 8)) + 8 * (jj & 1);
     }
 }
 
 // Source offset (bytes, relative to the tile's first row) of the granule a
-// lane moves into 1 KB block m of a tile stored with swizzle h.
-template <int D, bool TR>
+// lane moves into 1 KB block m of a tile.
+template <int D>
 __device__ __forceinline__ uint32_t dma_offset(int m, int lane, uint32_t rs2) {
     using G = BG<D>;
     const int row = m * G::RPB + lane / G::GPR;
     const int pos = lane % G::GPR;
-    const int h = TR ? G::hv(row) : G::hk(row);
-    return (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ h);
+    return (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ G::h(row));
 }
 
 // Packed bf16 operand from accumulator registers 8 cc .. 8 cc + 7.
@@ -108,11 +123,11 @@ __device__ __forceinline__ int xcd_order(int bid) {
 template <int D, bool VAR>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     using G = BG<D>;
-    constexpr int BN = 64, NW = 8, BM = 32 * NW, NSL = 3;
+    constexpr int BN = 64, NW = 8, BM = 32 * NW, NSL = 4;
     constexpr int TILE = BN * G::ROW;        // bytes of one 64-row tile
-    constexpr int SLOT = 3 * TILE;           // K (row swizzle) | K (transposed swizzle) | V
+    constexpr int SLOT = 2 * TILE;           // K | V (one swizzle serves row and transposed reads)
     constexpr int NI = TILE / 1024 / NW;     // 1 KB blocks per wave per tile copy
-    constexpr int PT = 3 * NI;               // loads per wave per tile
+    constexpr int PT = 2 * NI;               // loads per wave per tile
     static_assert(NI >= 1 && (TILE / 1024) % NW == 0, "blocks must divide over the waves");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -234,14 +249,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     }
     const float ab = (VAR && p.alibi) ? -p.alibi[h] * p.sqrt_d : 0.f;
 
-    uint32_t roff[G::NC], toff[G::NDB];
+    uint32_t roff[G::NC];
+    uint2 toff[G::NDB];
     lane_offsets<D>(lane, roff, toff);
-    uint32_t dr[NI], dt[NI];
+    uint32_t dr[NI];
 #pragma unroll
-    for (int n = 0; n < NI; ++n) {
-        dr[n] = dma_offset<D, false>(w * NI + n, lane, rs2);
-        dt[n] = dma_offset<D, true>(w * NI + n, lane, rs2);
-    }
+    for (int n = 0; n < NI; ++n) dr[n] = dma_offset<D>(w * NI + n, lane, rs2);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
     auto slot_of = [&](int i) -> int { return __builtin_amdgcn_readfirstlane(i % NSL); };
     auto issue = [&](int i) {
@@ -253,9 +266,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
         for (int n = 0; n < NI; ++n) load_lds16(dr[n], rk, base + 1024u * n);
 #pragma unroll
-        for (int n = 0; n < NI; ++n) load_lds16(dt[n], rk, base + TILE + 1024u * n);
-#pragma unroll
-        for (int n = 0; n < NI; ++n) load_lds16(dr[n], rv, base + 2 * TILE + 1024u * n);
+        for (int n = 0; n < NI; ++n) load_lds16(dr[n], rv, base + TILE + 1024u * n);
     };
     const uint8_t* kpm_row = p.kpm ? p.kpm + b * p.kpm_bstride : nullptr;
     const uint8_t* am_row = (p.amask && qvalid) ? p.amask + (long long)qi * p.amask_stride : nullptr;
@@ -284,16 +295,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) acc[db] = f32x16{};
 
-    if (ntiles > 0) issue(0);
-    if (ntiles > 1) {
-        issue(1);
-        wait_barrier<PT>();
-    } else {
-        wait_barrier<0>();
-    }
+    // tiles i + 1 .. i + NSL - 1 are loaded while tile i is processed
+    for (int i = 0; i < NSL - 1 && i < ntiles; ++i) issue(i);
+    wait_tiles<PT, NSL - 2>(min(NSL - 2, ntiles - 1));
     for (int i = 0; i < ntiles; ++i) {
-        const bool more = i + 2 < ntiles;
-        if (more) issue(i + 2);
+        if (i + NSL - 1 < ntiles) issue(i + NSL - 1);
         if (i >= w_first && i < n_act) {
             const char* St = smem + slot_of(i) * SLOT;
             f32x16 s0 = f32x16{}, s1 = f32x16{}, d0 = f32x16{}, d1 = f32x16{};
@@ -301,8 +307,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
             for (int c = 0; c < G::NC; ++c) {
                 const bf16x8 k0 = *(const bf16x8*)(St + roff[c]);
                 const bf16x8 k1 = *(const bf16x8*)(St + roff[c] + 32 * G::ROW);
-                const bf16x8 v0 = *(const bf16x8*)(St + 2 * TILE + roff[c]);
-                const bf16x8 v1 = *(const bf16x8*)(St + 2 * TILE + roff[c] + 32 * G::ROW);
+                const bf16x8 v0 = *(const bf16x8*)(St + TILE + roff[c]);
+                const bf16x8 v1 = *(const bf16x8*)(St + TILE + roff[c] + 32 * G::ROW);
                 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[c], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[c], s1, 0, 0, 0);
                 d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, oreg[c], d0, 0, 0, 0);
@@ -328,11 +334,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
             for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
                 for (int kc = 0; kc < 4; ++kc)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(St + TILE, toff[db], kc), ds[kc],
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(St, toff[db], kc), ds[kc],
                                                                       acc[db], 0, 0, 0);
         }
-        if (more) wait_barrier<PT>();
-        else wait_barrier<0>();
+        // tile i + 1 resident for the next step
+        wait_tiles<PT, NSL - 2>(min(i + NSL - 1, ntiles - 1) - (i + 1));
     }
 
     if (!qvalid) return;
@@ -367,13 +373,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
 template <int D, bool VAR>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     using G = BG<D>;
-    constexpr int NW = 8, BK = 128, BQ = 32, NSL = 4;
+    constexpr int NW = 8, BK = 128, BQ = 32, NSL = 6;
     constexpr int QTILE = BQ * G::ROW;           // bytes of one 32-row tile
-    constexpr int LDO = 4 * QTILE;               // (lse2, delta) of the tile after the four copies
-    constexpr int SLOT = 4 * QTILE + 256;        // Q | Q^T | dO | dO^T | 32 x float2
-    constexpr int XCH = NSL * SLOT;              // P exchange: 4 blocks x 4 KB
+    constexpr int LDO = 2 * QTILE;               // (lse2, delta) of the tile after the two copies
+    constexpr int SLOT = 2 * QTILE + 256;        // Q | dO | 32 x float2
+    constexpr int XCH = NSL * SLOT;              // P exchange after the slots: 4 blocks x 4 KB
     constexpr int NBLK = QTILE / 1024;           // 1 KB blocks per copy
-    constexpr int PW = 4 * NBLK / NW;            // blocks per wave per tile (all in one copy)
+    constexpr int PW = 2 * NBLK / NW;            // blocks per wave per tile (all in one copy)
     constexpr int PT = PW + 1;                   // loads per wave per tile
     static_assert(PW >= 1 && NBLK % PW == 0, "a wave's blocks must lie in one copy");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -443,18 +449,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const int tail = Tq % BQ ? nqt - 1 : nqt;
     const float ab = (VAR && p.alibi) ? -p.alibi[h] * p.sqrt_d : 0.f;
 
-    uint32_t roff[G::NC], toff[G::NDB];
+    uint32_t roff[G::NC];
+    uint2 toff[G::NDB];
     lane_offsets<D>(lane, roff, toff);
-    // tile loads: this wave moves blocks PW*w .. PW*w+PW-1 of the 4 NBLK blocks
-    // (copies: Q row swizzle, Q transposed, dO row, dO transposed)
+    // tile loads: this wave moves blocks PW*w .. PW*w+PW-1 of the 2 NBLK blocks
+    // (copies: Q, dO)
     const int copy = (PW * w) / NBLK;
-    const bool from_q = copy < 2, tr_sw = copy & 1;
+    const bool from_q = copy == 0;
     uint32_t dofs[PW];
 #pragma unroll
-    for (int n = 0; n < PW; ++n) {
-        const int m = (PW * w + n) % NBLK;
-        dofs[n] = tr_sw ? dma_offset<D, true>(m, lane, rs2) : dma_offset<D, false>(m, lane, rs2);
-    }
+    for (int n = 0; n < PW; ++n) dofs[n] = dma_offset<D>((PW * w + n) % NBLK, lane, rs2);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
     const char* srcg = (const char*)((const uint16_t*)(from_q ? p.q : p.dout) + b * p.q_bstride + (long long)h * D);
     const float2* ldg = p.ld2 + b * p.lse_bstride + (long long)h * p.lse_hstride;
@@ -479,19 +483,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     for (int db = 0; db < G::NDB; ++db) acc[db] = f32x16{};
 
     const int ntl = t_end - t0;
-    if (ntl > 0) issue(t0);
-    if (ntl > 1) issue(t0 + 1);
-    if (ntl > 2) {
-        issue(t0 + 2);
-        wait_barrier<2 * PT>();
-    } else if (ntl > 1) {
-        wait_barrier<PT>();
-    } else {
-        wait_barrier<0>();
-    }
+    // tiles t + 1 .. t + NSL - 1 are loaded while tile t is processed
+    for (int i = 0; i < NSL - 1 && i < ntl; ++i) issue(t0 + i);
+    wait_tiles<PT, NSL - 2>(min(NSL - 2, ntl - 1));
     for (int t = t0; t < t_end; ++t) {
-        const bool more = t + 3 < t_end;
-        if (more) issue(t + 3);
+        if (t + NSL - 1 < t_end) issue(t + NSL - 1);
         const bool act = wactive && t >= tw0 && t < tw_end;   // the same for both waves of a key block
         const char* St = smem + slot_of(t) * SLOT;
         const float4* lp = (const float4*)(St + LDO);
@@ -502,8 +498,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
         if (act) {
             // every LDS operand of this tile is requested before the first
             // matrix instruction, so the reads overlap the products
-            const char* rows = St + (roleA ? 0 : 2 * QTILE);   // Q or dO, row swizzle
-            const char* trt = St + (roleA ? 3 * QTILE : QTILE);
+            const char* rows = St + (roleA ? 0 : QTILE);   // Q or dO, row reads
+            const char* trt = St + (roleA ? QTILE : 0);    // dO or Q, transposed reads
             bf16x8 ra[G::NC];
 #pragma unroll
             for (int c = 0; c < G::NC; ++c) ra[c] = *(const bf16x8*)(rows + roff[c]);
@@ -568,9 +564,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
             for (int j = 0; j < NJ; ++j)
                 acc[j % G::NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[j], xb[j / G::NDB], acc[j % G::NDB], 0, 0, 0);
         }
-        if (t + 3 < t_end) wait_barrier<2 * PT>();
-        else if (t + 2 < t_end) wait_barrier<PT>();
-        else wait_barrier<0>();
+        wait_tiles<PT, NSL - 2>(min(t + NSL - 1, t_end - 1) - (t + 1));
     }
 
     if (!kvalid) return;
@@ -682,7 +676,7 @@ inline unsigned grid_for(long long n, int block) { return (unsigned)((n + block 
 
 template <int D, bool VAR>
 hipError_t launch_dq(const BwdParams& p, hipStream_t s) {
-    constexpr int BM = 256, LDS = 3 * 3 * 64 * 2 * D;
+    constexpr int BM = 256, LDS = 4 * 2 * 64 * 2 * D;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D, VAR>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
@@ -699,7 +693,7 @@ hipError_t launch_dq(const BwdParams& p, hipStream_t s) {
 
 template <int D, bool VAR>
 hipError_t launch_dkdv(const BwdParams& p, hipStream_t s) {
-    constexpr int BK = 128, LDS = 4 * (4 * 32 * 2 * D + 256) + 4 * 4096;
+    constexpr int BK = 128, LDS = 6 * (2 * 32 * 2 * D + 256) + 4 * 4096;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, VAR>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
