@@ -23,6 +23,10 @@ attn_bwd for a single call): 8 d algorithmic FLOPs per allowed pair (dP, dV,
 dQ, dK; the recomputed scores are not counted), and the roofline takes the dQ
 and dK/dV kernels of one sub-call together as one launch.
 
+step_ms  = median, min and max wall time of single steps, from one HIP event
+         at each step boundary over K more steps (a third pass; value and
+         ms_per_step come from the first, which has no events inside it).
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -186,6 +190,32 @@ def make_bwd_step(w, plan, dev_inputs):
 
 
 # ---------------------------------------------------------------- CPU baseline
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def step_stats(step, n: int) -> dict:
+    """Wall time of each of n further steps: one HIP event at every step
+    boundary on the current stream (a separate pass, after the timed one)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = np.asarray([ev[i].elapsed_time(ev[i + 1]) for i in range(n)], dtype=np.float64)
+    return {"median": float(np.median(t)), "min": float(t.min()), "max": float(t.max()), "steps": n}
+
+
 def cpu_baseline(w, host_inputs, rows: int, heads: int, dout=None):
     """The fp64 oracle, as it stands, on the heaviest `rows` local query rows
     of the first `heads` heads against every key (bounded sample); the
@@ -221,6 +251,7 @@ def cpu_baseline(w, host_inputs, rows: int, heads: int, dout=None):
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"{rows} query rows (local rows {sel[0]}..{sel[-1]}, positions {int(qpos[sel[0]])}.."
                    f"{int(qpos[sel[-1]])}) x {heads} of {w.H} heads x B={w.B} against all {w.T} keys, "
                    f"{'causal' if w.causal else 'non-causal'}{', RoPE' if w.rope_base else ''}"
@@ -280,6 +311,7 @@ def run_decode(args, w) -> dict:
         torch.cuda.synchronize()
     kms = np.asarray(kt.ms, dtype=np.float64)
     achieved = nbytes_k / (kms.sum() * 1e-3) / 1e9 if kms.sum() > 0 else None
+    stats = step_stats(step, args.steps)
     log(f"{ms:.4f} ms/step, {gbs:.0f} GB/s; decode kernel {achieved:.0f} GB/s over {len(kms)} launches "
         f"(avg {kms.mean():.4f} ms)")
     traffic = None
@@ -308,14 +340,15 @@ def run_decode(args, w) -> dict:
             reps += 1
         cb = reps * int(lh.sum()) * w.H * w.d * 2 * esize
         cpu = {"value": cb / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+               "cpu_model": cpu_model(),
                "sample": (f"oracle.decode of the whole step ({w.B} rows x {w.H} heads, {int(lh.sum())} visible "
                           f"slots) {reps} times: {cb:.3e} algorithmic bytes in {dt:.2f} s (float64 numpy, BLAS "
                           f"threads={blas_threads}, host cpus={os.cpu_count()})")}
         log(f"cpu baseline {cpu['value']:.3f} GB/s")
     return {
         "metric": METRIC_DECODE, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "warmup": args.warmup, "ms_per_step": ms, "step_ms": stats, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "pct_of_peak": 100.0 * gbs / PEAK_HBM_GBS,
         "config": {"workload": w.name, "B": w.B, "H": w.H, "cache_slots": w.T, "d": w.d,
                    "filled_range": w.kpm_len_range, "rope_base": w.rope_base, "pass": "decode",
@@ -466,6 +499,7 @@ def main() -> int:
         for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
+    stats = step_stats(step, args.steps)
     tflops = flops / (ms * 1e-3) / 1e12
     kms = np.asarray(kt.ms, dtype=np.float64)
     kern_ms = float(kms.sum())
@@ -515,6 +549,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "step_ms": stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
