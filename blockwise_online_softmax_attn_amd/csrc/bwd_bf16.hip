@@ -677,12 +677,8 @@ inline unsigned grid_for(long long n, int block) { return (unsigned)((n + block 
 template <int D, bool VAR>
 hipError_t launch_dq(const BwdParams& p, hipStream_t s) {
     constexpr int BM = 256, LDS = 4 * 2 * 64 * 2 * D;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D, VAR>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = set_lds_limit((const void*)bwd_dq_kernel<D, VAR>, LDS, lds_set); e != hipSuccess) return e;
     BwdParams q = p;
     q.n_tiles = (p.Tq + BM - 1) / BM;
     const long long grid = (long long)q.n_tiles * p.H * p.B;
@@ -694,12 +690,8 @@ hipError_t launch_dq(const BwdParams& p, hipStream_t s) {
 template <int D, bool VAR>
 hipError_t launch_dkdv(const BwdParams& p, hipStream_t s) {
     constexpr int BK = 128, LDS = 6 * (2 * 32 * 2 * D + 256) + 4 * 4096;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, VAR>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = set_lds_limit((const void*)bwd_dkdv_kernel<D, VAR>, LDS, lds_set); e != hipSuccess) return e;
     BwdParams q = p;
     q.n_tiles = (p.Tkv + BK - 1) / BK;
     const long long grid = (long long)q.n_tiles * p.H * p.B;

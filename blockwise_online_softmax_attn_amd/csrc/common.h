@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/attn.h"
 
 namespace bosa {
@@ -148,6 +150,20 @@ struct BwdParams {
 
 // Entry of a live-tile list: tile index, top bit set when no key of the tile is masked.
 constexpr uint32_t kTileClean = 0x80000000u;
+
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per device (`done` holds one bit per device id below 64; higher ids set it
+// on every call).  Concurrent first calls may both set it, which is harmless.
+inline hipError_t set_lds_limit(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 // Kernel launchers (each returns hipSuccess or the launch error).
 // One decoding call: the newest query of each (batch, head) against the

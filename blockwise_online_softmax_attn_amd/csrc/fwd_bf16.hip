@@ -532,13 +532,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
 template <int D, bool ALIBI, bool WIN>
 hipError_t launch(const FwdParams& p, hipStream_t s) {
     using G = Geo<D>;
-    static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_bf16_kernel<D, ALIBI, WIN>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = set_lds_limit((const void*)attn_fwd_bf16_kernel<D, ALIBI, WIN>, G::LDS_BYTES, lds_set);
+        e != hipSuccess)
+        return e;
     FwdParams q = p;
     q.n_qtiles = (p.Tq + BM - 1) / BM;
     const long long grid = (long long)q.n_qtiles * p.H * p.B;
