@@ -84,13 +84,17 @@ enum {
  *  lse        device float32 (B, H, Tq); may be NULL unless ATTN_ACCUMULATE.
  *  B, H, Tq, Tkv  sizes >= 0 (B, H or Tq = 0: nothing to do; Tkv = 0: every
  *             row is empty).  d: 64 or 128.
- *  q_off, kv_off  absolute position of row 0 of q and of k/v.
+ *  q_off, kv_off  absolute position of row 0 of q and of k/v; |q_off|,
+ *             |kv_off| <= 2^52 (ATTN_ERR_INVALID_ARG otherwise).
  *  causal     nonzero: key j is allowed for query i only if kv_off+j <= q_off+i.
  *  kpm        device uint8 (B, Tkv) or NULL.  attn_mask: device uint8 (Tq, Tkv) or NULL.
  *  rope_base  > 0: rotate adjacent coordinate pairs (2t, 2t+1) of q and k by
- *             pos * rope_base^(-2t/d) (cos/sin accurate to float32 rounding),
- *             in float32, and round the rotated values to `dtype` before the
- *             dot product.  0: no rotary embedding.
+ *             pos * rope_base^(-2t/d) (the angle formed in float64, its cos
+ *             and sin rounded to float32), in float32, and round the rotated
+ *             values to `dtype` before the dot product.  0: no rotary
+ *             embedding.  A float64 angle carries an absolute error that
+ *             grows with the position: about 1e-4 rad near position 2^40,
+ *             tenths of a radian near 2^52.
  *  dtype      ATTN_BF16 (bf16 MFMA, float32 accumulation and softmax) or
  *             ATTN_F32 (float32 throughout).
  *  flags      ATTN_ACCUMULATE | ATTN_OUT_F32 | ATTN_NO_TILE_SKIP.
