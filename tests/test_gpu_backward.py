@@ -210,3 +210,30 @@ def test_ring_backward_share(wi, T, heads, ranks):
         ref = oracle.sdpa_backward(np64(q), np64(k), np64(v), np64(dout), qpos, np.arange(T), causal=w.causal,
                                    rope_base=w.rope_base, dtype="bf16")
         compare_grads((dq.cpu(), dk.cpu(), dv.cpu()), ref, f"rank{rank}")
+
+
+@pytest.mark.parametrize("zigzag,causal", [(True, True), (False, False)])
+def test_ring_backward_with_key_padding(zigzag, causal):
+    """attn_ring_bwd with a key-padding mask over the whole sequence (one
+    batch row padded to a length that ends inside a block, one with random
+    holes), RoPE, every rank of P = 4: dq, dk, dv against the oracle."""
+    P, B, H, T, d = 4, 2, 2, 1024, 128
+    kpm = workloads.random_mask((B, T), 9500 + int(zigzag), 0.15)
+    kpm[0, 700:] = 1
+    for rank in range(P):
+        qpos = oracle.local_query_positions(T, P, rank, zigzag)
+        seed = 9510 + 10 * rank + int(zigzag)
+        q = rnd((B, T // P, H, d), seed)
+        k = rnd((B, T, H, d), seed + 1)
+        v = rnd((B, T, H, d), seed + 2)
+        dout = rnd((B, T // P, H, d), seed + 3)
+        note(f"ring backward kpm: zigzag={zigzag} causal={causal} rank={rank}")
+        qd, kd, vd, od, md = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), kpm.to(DEV)
+        out, lse = bosa.attn_ring_fwd(qd, kd, vd, P=P, rank=rank, zigzag=zigzag, causal=causal, kpm=md,
+                                      rope_base=10000.0)
+        dq, dk, dv = bosa.attn_ring_bwd(qd, kd, vd, out, od, lse, P=P, rank=rank, zigzag=zigzag, causal=causal,
+                                        kpm=md, rope_base=10000.0)
+        torch.cuda.synchronize()
+        ref = oracle.sdpa_backward(np64(q), np64(k), np64(v), np64(dout), qpos, np.arange(T), causal=causal,
+                                   kpm=kpm.numpy(), rope_base=10000.0, dtype="bf16")
+        compare_grads((dq.cpu(), dk.cpu(), dv.cpu()), ref, f"rank{rank}")

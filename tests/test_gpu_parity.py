@@ -14,7 +14,7 @@ import torch
 import blockwise_online_softmax_attn_amd as bosa
 import oracle
 import workloads
-from gpu_helpers import DEV, compare, gpu_fwd, note, np64, ref_fwd
+from gpu_helpers import DEV, compare, dt_name, gpu_fwd, note, np64, ref_fwd
 
 pytestmark = pytest.mark.gpu
 
@@ -289,3 +289,38 @@ def test_block_order_and_size_invariance(order, chunk):
     torch.cuda.synchronize()
     ro, rl = ref_fwd(q, k, v, q_off=q_off, causal=True, rope_base=10000.0)
     compare(acc.cpu(), lse.cpu(), ro, rl, "bf16", f"{order}/{chunk}")
+
+
+# ------------------------------------------------------------------ ring shares with key padding
+RING_KPM_CASES = [
+    # (P, zigzag, causal, dtype, d)
+    (4, False, False, torch.bfloat16, 128),
+    (4, True, True, torch.bfloat16, 64),
+    (2, True, True, torch.float32, 128),
+    (4, False, True, torch.float32, 64),
+]
+
+
+@pytest.mark.parametrize("case", range(len(RING_KPM_CASES)))
+def test_ring_share_with_key_padding(case):
+    """attn_ring_fwd with a key-padding mask over the whole sequence (each
+    sub-call sees the mask at its block's keys): two batch rows, one padded
+    to a valid length that ends inside a block, one with random holes, RoPE,
+    every rank, against the oracle over every key."""
+    P, zigzag, causal, dtype, d = RING_KPM_CASES[case]
+    B, H, T = 2, 2, 1536
+    kpm = workloads.random_mask((B, T), 9400 + case, 0.15)
+    kpm[0, 1000:] = 1
+    for rank in range(P):
+        qpos = oracle.local_query_positions(T, P, rank, zigzag)
+        seed = 9410 + 10 * case + rank
+        q = rnd((B, T // P, H, d), seed, dtype)
+        k = rnd((B, T, H, d), seed + 100, dtype)
+        v = rnd((B, T, H, d), seed + 200, dtype)
+        note(f"ring kpm case {case}: P={P} zigzag={zigzag} causal={causal} {dtype} d={d} rank={rank}")
+        out, lse = bosa.attn_ring_fwd(q.to(DEV), k.to(DEV), v.to(DEV), P=P, rank=rank, zigzag=zigzag, causal=causal,
+                                      kpm=kpm.to(DEV), rope_base=10000.0)
+        torch.cuda.synchronize()
+        ro, rl = oracle.sdpa(np64(q), np64(k), np64(v), qpos, np.arange(T), causal=causal, kpm=kpm.numpy(),
+                             rope_base=10000.0, dtype=dt_name(q))
+        compare(out.cpu(), lse.cpu(), ro, rl, dt_name(q), f"rank{rank}")
