@@ -351,15 +351,17 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
     }
     hipStream_t s = (hipStream_t)stream;
     const bool rope = rope_base > 0.0 && Tkv > 0;
-    // bf16: the keys are rotated once into a scratch copy that the attention
-    // kernel streams; float32: the kernel rotates keys on the fly.
+    // bf16: the queries and the keys are rotated once into scratch copies that
+    // the attention kernel reads (the same float32 rotation it would apply);
+    // float32: the kernel rotates them on the fly.
     const bool krot = rope && dtype == ATTN_BF16;
     const size_t tab_q = rope ? align_up((size_t)Tq * (d / 2) * sizeof(float2)) : 0;
     const size_t tab_k = rope ? align_up((size_t)Tkv * (d / 2) * sizeof(float2)) : 0;
     const size_t kbuf = krot ? align_up((size_t)B * Tkv * H * d * 2) : 0;
+    const size_t qbuf = krot ? align_up((size_t)B * Tq * H * d * 2) : 0;
     const size_t lst = kpm_list_bytes(c);
     Scratch ws;
-    hipError_t e = ws.alloc(tab_q + tab_k + kbuf + lst, s);
+    hipError_t e = ws.alloc(tab_q + tab_k + kbuf + qbuf + lst, s);
     if (e != hipSuccess) return hip_fail(e, "scratch allocation");
     char* wp = (char*)ws.ptr;
     if (rope) {
@@ -371,13 +373,17 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
         if (e != hipSuccess) return hip_fail(e, "rotary table launch");
         if (krot) {
             void* kr = wp + tab_q + tab_k;
+            void* qr = wp + tab_q + tab_k + kbuf;
             e = launch_rope_copy_bf16(k, kr, c.rope_k, B, Tkv, H, d, s);
-            if (e != hipSuccess) return hip_fail(e, "key rotation launch");
+            if (e == hipSuccess) e = launch_rope_copy_bf16(q, qr, c.rope_q, B, Tq, H, d, s);
+            if (e != hipSuccess) return hip_fail(e, "key / query rotation launch");
             c.k = kr;
+            c.q = qr;
             c.rope_k = nullptr;
+            c.rope_q = nullptr;
         }
     }
-    return enqueue(c, lst ? (int*)(wp + tab_q + tab_k + kbuf) : nullptr, s);
+    return enqueue(c, lst ? (int*)(wp + tab_q + tab_k + kbuf + qbuf) : nullptr, s);
 }
 
 int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, int* cache_len, int B, int H,
@@ -557,13 +563,18 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
     hipStream_t s = (hipStream_t)stream;
     const bool rope = rope_base > 0.0;
     // bf16: every key block is rotated once (at its absolute positions) into
-    // a scratch copy, as the block's owner would before passing it on.
+    // a scratch copy, as the block's owner would before passing it on, and so
+    // are the local queries, which every sub-call reads again (rotating them
+    // in each sub-call's kernel would re-read the float32 cos/sin table, twice
+    // the bytes of the queries, once per sub-call); the copies hold the same
+    // values the kernel's own rotation gives.
     const bool krot = rope && dtype == ATTN_BF16;
     const size_t tab_q = rope ? align_up((size_t)Tl * (d / 2) * sizeof(float2)) : 0;
     const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(float2)) : 0;
     const size_t kbuf = krot ? align_up((size_t)B * T * H * d * 2) : 0;
+    const size_t qbuf = krot ? align_up((size_t)B * Tl * H * d * 2) : 0;
     std::vector<size_t> lst_off(n_live, 0);
-    size_t total = tab_q + tab_k + kbuf;
+    size_t total = tab_q + tab_k + kbuf + qbuf;
     std::vector<Call> calls(n_live);
     const int rs = H * d;
     const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
@@ -612,16 +623,20 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
         if (err != hipSuccess) return hip_fail(err, "rotary table launch");
         if (krot) {
             err = launch_rope_copy_bf16(k, wp + tab_q + tab_k, (const float2*)(wp + tab_q), B, T, H, d, s);
-            if (err != hipSuccess) return hip_fail(err, "key rotation launch");
+            if (err == hipSuccess)
+                err = launch_rope_copy_bf16(q, wp + tab_q + tab_k + kbuf, (const float2*)wp, B, Tl, H, d, s);
+            if (err != hipSuccess) return hip_fail(err, "key / query rotation launch");
         }
     }
     bool covered[2] = {false, false};
     for (int i = 0; i < n_live; ++i) {
         Call& c = calls[i];
-        if (rope) {
+        if (krot) {
+            c.k = (const uint16_t*)(wp + tab_q + tab_k) + (size_t)plan[i].kv_pos0 * rs;
+            c.q = (const uint16_t*)(wp + tab_q + tab_k + kbuf) + (size_t)plan[i].q_row0 * rs;
+        } else if (rope) {
             c.rope_q = (const float2*)wp + (size_t)plan[i].q_row0 * (d / 2);
-            if (krot) c.k = (const uint16_t*)(wp + tab_q + tab_k) + (size_t)plan[i].kv_pos0 * rs;
-            else c.rope_k = (const float2*)(wp + tab_q) + (size_t)plan[i].kv_pos0 * (d / 2);
+            c.rope_k = (const float2*)(wp + tab_q) + (size_t)plan[i].kv_pos0 * (d / 2);
         }
         const size_t lb = kpm_list_bytes(c);
         if (int rc = enqueue(c, lb ? (int*)(wp + lst_off[i]) : nullptr, s)) return rc;

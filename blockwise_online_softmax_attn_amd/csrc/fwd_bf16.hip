@@ -245,18 +245,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     const int qwlast = min(qw0 + 31, Tq - 1);
     const long long delta = p.q_off - p.kv_off;   // key j allowed for query i iff j - i <= delta
 
-    // ---- Q operand: lane holds query qi, d = 16c + 8hh + 0..7 for each chunk c.
+    // ---- Q operand (already rotated when the rotary embedding is on): lane
+    // holds query qi, d = 16c + 8hh + 0..7 for each chunk c.
     bf16x8 qreg[G::NC];
 #pragma unroll
     for (int c = 0; c < G::NC; ++c) {
         uint4 x = make_uint4(0, 0, 0, 0);
-        if (qvalid) {
-            x = *(const uint4*)(qg + (long long)qi * rs + 16 * c + 8 * hh);
-            if (p.rope_q) {
-                const float4* tp = (const float4*)(p.rope_q + (long long)qi * (D / 2) + 8 * c + 4 * hh);
-                x = rope8_bf16(x, tp[0], tp[1]);
-            }
-        }
+        if (qvalid) x = *(const uint4*)(qg + (long long)qi * rs + 16 * c + 8 * hh);
         qreg[c] = __builtin_bit_cast(bf16x8, x);
     }
     // Finish the Q loads here: the vmcnt bookkeeping of the loop below counts
@@ -546,7 +541,7 @@ hipError_t launch(const FwdParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s) {
-    if (p.rope_k) return hipErrorInvalidValue;   // keys must arrive rotated
+    if (p.rope_q || p.rope_k) return hipErrorInvalidValue;   // queries and keys arrive rotated
     const bool win = p.win_left >= 0 || p.win_right >= 0;
     if (d == 128) {
         if (p.alibi) return win ? launch<128, true, true>(p, s) : launch<128, true, false>(p, s);
