@@ -56,6 +56,11 @@ def compare(out, lse, ref_out, ref_lse, dtype: str, what: str = ""):
     fin = np.isfinite(ref_lse)
     assert np.array_equal(np.isfinite(l), fin), f"{what}: empty-row pattern differs"
     assert np.all(l[~fin] == -np.inf)
+    if dtype == "f32" and fin.any():
+        # a float32 lse is itself rounded to half a unit in the last place of
+        # its magnitude; where distance penalties make |lse| large (ALiBi),
+        # 1e-5 falls below a few such units, so 4 of them are allowed
+        tol_l = max(tol_l, 4.0 * float(np.spacing(np.float32(np.abs(ref_lse[fin]).max()))))
     eo = float(np.abs(o - ref_out).max()) if o.size else 0.0
     el = float(np.abs(l[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
     row_err = np.sqrt(((o - ref_out) ** 2).sum(-1)) + 1e-300

@@ -1,0 +1,166 @@
+"""Seeded random sweep of the GPU path against the oracle.
+
+Each case draws its shape, positions, masks, rotary base, window and ALiBi
+slopes from its own generator (seed = a fixed base + the case number), so a
+failure names a case that replays exactly.  Sizes stay small enough for the
+oracle; they are ragged on purpose (neither rows nor keys a multiple of the
+64-key tile or the 32-row wave).  Forward in both dtypes, backward, ring
+shares and decoding; the tolerances are those of the other parity tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import blockwise_online_softmax_attn_amd as bosa
+import oracle
+import workloads
+from gpu_helpers import DEV, compare, note, np64
+from test_gpu_backward import compare_grads
+
+pytestmark = pytest.mark.gpu
+
+N_FWD, N_BWD, N_RING, N_DEC = 40, 16, 8, 8
+
+
+def _draw(shape, seed, dtype):
+    return workloads.random_normal(shape, seed, dtype)
+
+
+def _variant(rng, H, span):
+    """A window (30% of cases) with each side either unlimited or up to
+    `span` positions, and ALiBi slopes (25% of cases)."""
+    window = None
+    if rng.random() < 0.3:
+        side = lambda: -1 if rng.random() < 0.3 else int(rng.integers(0, span))
+        window = (side(), side())
+    slopes = workloads.alibi_slopes(H) if rng.random() < 0.25 else None
+    return window, slopes
+
+
+def _mask(shape, seed, p):
+    return workloads.random_mask(shape, seed, p) if p > 0 else None
+
+
+def _oracle_kw(window, slopes):
+    return dict(window=(-1, -1) if window is None else window,
+                alibi_slopes=None if slopes is None else slopes.double().numpy())
+
+
+@pytest.mark.parametrize("case", range(N_FWD))
+def test_random_forward(case):
+    rng = np.random.default_rng(20000 + case)
+    dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    d = int(rng.choice([64, 128]))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    Tq, Tkv = int(rng.integers(1, 600)), int(rng.integers(1, 700))
+    causal = bool(rng.random() < 0.6)
+    q_off, kv_off = int(rng.integers(0, 1500)), int(rng.integers(0, 1500))
+    kpm_p = float(rng.choice([0.0, 0.0, 0.2, 0.7]))
+    am_p = float(rng.choice([0.0, 0.0, 0.0, 0.1]))
+    rope = float(rng.choice([0.0, 10000.0, 500.0]))
+    window, slopes = _variant(rng, H, 400)
+    seed = 21000 + 10 * case
+    note(f"random forward {case}: {dtype} d={d} B={B} H={H} Tq={Tq} Tkv={Tkv} offs=({q_off},{kv_off}) "
+         f"causal={causal} kpm={kpm_p} amask={am_p} rope={rope} window={window} alibi={slopes is not None}")
+    q, k, v = _draw((B, Tq, H, d), seed, dtype), _draw((B, Tkv, H, d), seed + 1, dtype), _draw((B, Tkv, H, d), seed + 2, dtype)
+    kpm, am = _mask((B, Tkv), seed + 3, kpm_p), _mask((Tq, Tkv), seed + 4, am_p)
+    out, lse = bosa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), q_off=q_off, kv_off=kv_off, causal=causal,
+                             kpm=None if kpm is None else kpm.to(DEV), attn_mask=None if am is None else am.to(DEV),
+                             rope_base=rope, window=window, alibi_slopes=None if slopes is None else slopes.to(DEV))
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(np64(q), np64(k), np64(v), q_off=q_off, kv_off=kv_off, causal=causal,
+                              kpm=None if kpm is None else kpm.numpy(), attn_mask=None if am is None else am.numpy(),
+                              rope_base=rope, dtype="f32" if dtype == torch.float32 else "bf16",
+                              **_oracle_kw(window, slopes))
+    compare(out.cpu(), lse.cpu(), ro, rl, "f32" if dtype == torch.float32 else "bf16", f"case {case}")
+
+
+@pytest.mark.parametrize("case", range(N_BWD))
+def test_random_backward(case):
+    rng = np.random.default_rng(22000 + case)
+    d = int(rng.choice([64, 128]))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    Tq, Tkv = int(rng.integers(1, 400)), int(rng.integers(1, 500))
+    causal = bool(rng.random() < 0.6)
+    q_off, kv_off = int(rng.integers(0, 1000)), int(rng.integers(0, 1000))
+    kpm_p = float(rng.choice([0.0, 0.0, 0.3]))
+    am_p = float(rng.choice([0.0, 0.0, 0.0, 0.1]))
+    rope = float(rng.choice([0.0, 10000.0]))
+    window, slopes = _variant(rng, H, 300)
+    seed = 23000 + 10 * case
+    note(f"random backward {case}: d={d} B={B} H={H} Tq={Tq} Tkv={Tkv} offs=({q_off},{kv_off}) causal={causal} "
+         f"kpm={kpm_p} amask={am_p} rope={rope} window={window} alibi={slopes is not None}")
+    bf = torch.bfloat16
+    q, k, v = _draw((B, Tq, H, d), seed, bf), _draw((B, Tkv, H, d), seed + 1, bf), _draw((B, Tkv, H, d), seed + 2, bf)
+    dout = _draw((B, Tq, H, d), seed + 3, bf)
+    kpm, am = _mask((B, Tkv), seed + 4, kpm_p), _mask((Tq, Tkv), seed + 5, am_p)
+    kw = dict(q_off=q_off, kv_off=kv_off, causal=causal, kpm=None if kpm is None else kpm.to(DEV),
+              attn_mask=None if am is None else am.to(DEV), rope_base=rope, window=window,
+              alibi_slopes=None if slopes is None else slopes.to(DEV))
+    qd, kd, vd, od = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV)
+    out, lse = bosa.attn_fwd(qd, kd, vd, **kw)
+    grads = bosa.attn_bwd(qd, kd, vd, out, od, lse, flags=bosa.ATTN_OUT_F32, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(np64(q), np64(k), np64(v), np64(dout), q_off=q_off, kv_off=kv_off,
+                                    causal=causal, kpm=None if kpm is None else kpm.numpy(),
+                                    attn_mask=None if am is None else am.numpy(), rope_base=rope, dtype="bf16",
+                                    **_oracle_kw(window, slopes))
+    compare_grads([g.cpu() for g in grads], ref, f"case {case}")
+
+
+@pytest.mark.parametrize("case", range(N_RING))
+def test_random_ring_share(case):
+    rng = np.random.default_rng(24000 + case)
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    d = int(rng.choice([64, 128]))
+    P = int(rng.choice([2, 4]))
+    zigzag = bool(rng.random() < 0.5)
+    c = int(rng.integers(20, 160))
+    T = (2 * P if zigzag else P) * c
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    causal = bool(rng.random() < 0.7)
+    rank = int(rng.integers(0, P))
+    kpm_p = float(rng.choice([0.0, 0.2]))
+    rope = float(rng.choice([0.0, 10000.0]))
+    window, slopes = _variant(rng, H, 2 * c)
+    seed = 25000 + 10 * case
+    note(f"random ring {case}: {dtype} d={d} P={P} zigzag={zigzag} T={T} B={B} H={H} rank={rank} causal={causal} "
+         f"kpm={kpm_p} rope={rope} window={window} alibi={slopes is not None}")
+    q = _draw((B, T // P, H, d), seed, dtype)
+    k, v = _draw((B, T, H, d), seed + 1, dtype), _draw((B, T, H, d), seed + 2, dtype)
+    kpm = _mask((B, T), seed + 3, kpm_p)
+    out, lse = bosa.attn_ring_fwd(q.to(DEV), k.to(DEV), v.to(DEV), P=P, rank=rank, zigzag=zigzag, causal=causal,
+                                  kpm=None if kpm is None else kpm.to(DEV), rope_base=rope, window=window,
+                                  alibi_slopes=None if slopes is None else slopes.to(DEV))
+    torch.cuda.synchronize()
+    qpos = oracle.local_query_positions(T, P, rank, zigzag)
+    ro, rl = oracle.sdpa(np64(q), np64(k), np64(v), qpos, np.arange(T), causal=causal,
+                         kpm=None if kpm is None else kpm.numpy(), rope_base=rope,
+                         dtype="f32" if dtype == torch.float32 else "bf16", **_oracle_kw(window, slopes))
+    compare(out.cpu(), lse.cpu(), ro, rl, "f32" if dtype == torch.float32 else "bf16", f"case {case}")
+
+
+@pytest.mark.parametrize("case", range(N_DEC))
+def test_random_decode(case):
+    rng = np.random.default_rng(26000 + case)
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    d = int(rng.choice([64, 128]))
+    B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    Tcap = int(rng.integers(1, 3000))
+    lens = rng.integers(0, Tcap + 1, size=B)
+    rope = float(rng.choice([0.0, 10000.0]))
+    wl = -1 if rng.random() < 0.6 else int(rng.integers(0, 500))
+    slopes = workloads.alibi_slopes(H) if rng.random() < 0.3 else None
+    seed = 27000 + 10 * case
+    note(f"random decode {case}: {dtype} d={d} B={B} H={H} Tcap={Tcap} lens={lens.tolist()} rope={rope} "
+         f"window_left={wl} alibi={slopes is not None}")
+    kc, vc = _draw((B, Tcap, H, d), seed, dtype), _draw((B, Tcap, H, d), seed + 1, dtype)
+    qn = _draw((B, H, d), seed + 2, dtype)
+    ln = torch.tensor(lens, dtype=torch.int32)
+    out, lse = bosa.attn_decode(qn.to(DEV), kc.to(DEV), vc.to(DEV), ln.to(DEV), rope_base=rope, window_left=wl,
+                                alibi_slopes=None if slopes is None else slopes.to(DEV))
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(np64(qn), np64(kc), np64(vc), lens, rope_base=rope,
+                           dtype="f32" if dtype == torch.float32 else "bf16", window_left=wl,
+                           alibi_slopes=None if slopes is None else slopes.double().numpy())
+    compare(out.cpu(), lse.cpu(), ro, rl, "f32" if dtype == torch.float32 else "bf16", f"case {case}")
