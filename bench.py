@@ -4,8 +4,10 @@
 Default workload: one rank's share of an 8-way zigzag ring at 128K context
 (B=1, H=32, d=128, bf16, causal, RoPE base 10000): 16384 local query rows
 against 131072 keys in ring order, 17 attention sub-calls merged into a float32
-accumulator and cast to bf16.  One step is one whole share (attn_ring_fwd),
-inputs resident in HBM.  `--workload N` selects another of the five workloads.
+accumulator and cast to bf16 (the sub-calls of each query half run up to four
+to a launch of the chained kernel: 6 launches per step).  One step is one whole
+share (attn_ring_fwd), inputs resident in HBM.  `--workload N` selects another
+of the five workloads.
 
 value  = algorithmic TFLOP/s of the step: 4 d FLOPs per allowed (query, key)
          pair (two contractions, 2 FLOPs per multiply-add); masked work that
@@ -69,7 +71,7 @@ KERNEL_SOURCES = {
 # kernels whose counters make up one attention "launch" of each pass: the
 # forward kernel alone; for the backward the dQ and dK/dV kernels of one
 # sub-call together
-TRAFFIC_KERNELS = {"fwd": ("attn_fwd_bf16_kernel<128",),
+TRAFFIC_KERNELS = {"fwd": ("attn_fwd_bf16_chain_kernel<128",),
                    "bwd": ("bwd_dq_kernel<128", "bwd_dkdv_kernel<128"),
                    "decode": ("decode_chunk_kernel<unsigned short, 128",)}
 
@@ -470,7 +472,7 @@ def main() -> int:
     # backward dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q (the scores
     # the kernels recompute are not counted)
     flops = (8.0 if bwd else 4.0) * w.d * pairs
-    log(f"{pairs} allowed pairs/step = {flops:.4e} FLOPs; {launches} attention launches/step; warmup {args.warmup}")
+    log(f"{pairs} allowed pairs/step = {flops:.4e} FLOPs; {launches} attention sub-calls/step; warmup {args.warmup}")
     if args.copy_calibration_mib:
         # a plain copy of known size through the library's float32 copy kernel:
         # reads and writes copy_calibration_mib MiB once each
@@ -527,8 +529,8 @@ def main() -> int:
         "frac": (achieved / peak) if achieved else None,
         "traffic": traffic,
         "kernel": (f"bwd_dq_kernel<{w.d}> + bwd_dkdv_kernel<{w.d}>" if bwd else
-                   "attn_fwd_bf16_kernel<128>" if (w.dtype == "bf16" and w.d == 128) else
-                   ("attn_fwd_bf16_kernel<64>" if w.dtype == "bf16" else f"attn_fwd_f32_kernel<{w.d}>")),
+                   (f"attn_fwd_bf16_chain_kernel<{w.d}>" if plan is not None else f"attn_fwd_bf16_kernel<{w.d}>")
+                   if w.dtype == "bf16" else f"attn_fwd_f32_kernel<{w.d}>"),
         "launches": n_launch,
         "avg_launch_ms": kern_ms / max(n_launch, 1),
         "flops_per_launch": flops * args.steps / max(n_launch, 1),
@@ -560,7 +562,8 @@ def main() -> int:
             "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "Tq_local": int(dev[0].shape[1]), "d": w.d,
             "causal": w.causal, "rope_base": w.rope_base, "kpm_len_range": w.kpm_len_range,
             "ring_P": w.ring_P, "ring_rank": w.ring_rank, "zigzag": w.zigzag,
-            "attention_launches_per_step": launches, "algorithmic_flops_per_step": flops,
+            "attention_subcalls_per_step": launches, "attention_launches_per_step": n_launch // args.steps,
+            "algorithmic_flops_per_step": flops,
             "pass": args.which,
         },
         "roofline": roofline,

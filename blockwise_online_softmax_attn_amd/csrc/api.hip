@@ -141,16 +141,8 @@ size_t kpm_list_bytes(const Call& c) {
     return align_up((size_t)c.B * (size_t)(ntk + 2) * sizeof(int));
 }
 
-// Enqueue one validated call.  `list` is scratch of kpm_list_bytes(c) bytes.
-int enqueue(const Call& c, int* list, hipStream_t s) {
-    hipError_t e;
-    if (c.Tkv == 0) {
-        if (c.flags & ATTN_ACCUMULATE) return ATTN_OK;  // merging an empty partial changes nothing
-        const bool f32out = c.dtype == ATTN_F32 || (c.flags & ATTN_OUT_F32);
-        e = launch_fill_empty(c.out, f32out ? 0 : 1, c.lse, c.B, c.H, c.Tq, c.d, c.o_bstride, c.H * c.d,
-                              c.lse_bstride, c.lse_hstride, s);
-        return e == hipSuccess ? ATTN_OK : hip_fail(e, "empty-key fill");
-    }
+// Kernel parameters of one validated call (without its live-tile list).
+FwdParams fwd_params(const Call& c) {
     FwdParams p{};
     p.q = c.q; p.k = c.k; p.v = c.v; p.out = c.out; p.lse = c.lse;
     p.kpm = c.kpm; p.amask = c.amask;
@@ -167,14 +159,32 @@ int enqueue(const Call& c, int* list, hipStream_t s) {
     p.win_right = c.win_right;
     p.alibi = c.alibi;
     p.sqrt_d = (float)std::sqrt((double)c.d);
-    if (c.dtype == ATTN_BF16) {
-        if (list) {
-            const int ntk = (c.Tkv + kTile - 1) / kTile;
-            e = launch_kpm_tiles(c.kpm, c.kpm_bstride, c.B, c.Tkv, kTile, list, ntk + 2, s);
-            if (e != hipSuccess) return hip_fail(e, "key-padding tile list launch");
-            p.kpm_list = list;
-            p.kpm_list_stride = ntk + 2;
-        }
+    return p;
+}
+
+// Build the live-tile list of a call's key-padding mask into `list` (scratch
+// of kpm_list_bytes(c) bytes).
+int build_tile_list(const Call& c, int* list, hipStream_t s) {
+    const int ntk = (c.Tkv + kTile - 1) / kTile;
+    const hipError_t e = launch_kpm_tiles(c.kpm, c.kpm_bstride, c.B, c.Tkv, kTile, list, ntk + 2, s);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "key-padding tile list launch");
+}
+
+// Enqueue one validated call.  `list` is scratch of kpm_list_bytes(c) bytes.
+int enqueue(const Call& c, int* list, hipStream_t s) {
+    hipError_t e;
+    if (c.Tkv == 0) {
+        if (c.flags & ATTN_ACCUMULATE) return ATTN_OK;  // merging an empty partial changes nothing
+        const bool f32out = c.dtype == ATTN_F32 || (c.flags & ATTN_OUT_F32);
+        e = launch_fill_empty(c.out, f32out ? 0 : 1, c.lse, c.B, c.H, c.Tq, c.d, c.o_bstride, c.H * c.d,
+                              c.lse_bstride, c.lse_hstride, s);
+        return e == hipSuccess ? ATTN_OK : hip_fail(e, "empty-key fill");
+    }
+    FwdParams p = fwd_params(c);
+    if (c.dtype == ATTN_BF16 && list) {
+        if (int rc = build_tile_list(c, list, s)) return rc;
+        p.kpm_list = list;
+        p.kpm_list_stride = (c.Tkv + kTile - 1) / kTile + 2;
     }
     const bool timed = g_prof.on && g_prof.n < g_prof.cap;
     if (timed && (e = hipEventRecord(g_prof.ev[2 * g_prof.n], s)) != hipSuccess) return hip_fail(e, "event record");
@@ -638,9 +648,59 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
             c.rope_q = (const float2*)wp + (size_t)plan[i].q_row0 * (d / 2);
             c.rope_k = (const float2*)(wp + tab_q) + (size_t)plan[i].kv_pos0 * (d / 2);
         }
-        const size_t lb = kpm_list_bytes(c);
-        if (int rc = enqueue(c, lb ? (int*)(wp + lst_off[i]) : nullptr, s)) return rc;
-        covered[plan[i].q_row0 == 0 ? 0 : 1] = true;
+    }
+    // bf16 without a window or ALiBi: a query block's sub-calls run in plan
+    // order, several to a launch of the chained kernel, with the same
+    // per-block partials and merges as one launch per sub-call.  A chain ends
+    // after kMaxChain blocks or after a block that causal order cuts through
+    // the query block (its workgroups then finish at different times, and a
+    // new launch lines them up again, so the workgroups of one head keep
+    // reading the same key tiles at about the same time).
+    const bool chain = dtype == ATTN_BF16 && wl < 0 && wr < 0 && !(var && var->alibi_slopes);
+    if (chain) {
+        for (int i = 0; i < n_live; ++i)
+            if (kpm_list_bytes(calls[i]))
+                if (int rc = build_tile_list(calls[i], (int*)(wp + lst_off[i]), s)) return rc;
+        auto cut = [&](int i) {
+            return causal && plan[i].kv_pos0 + plan[i].kv_rows - 1 > plan[i].q_pos0;
+        };
+        for (int ph = 0; ph < 2; ++ph) {
+            std::vector<int> idx;
+            for (int i = 0; i < n_live; ++i)
+                if ((plan[i].q_row0 == 0 ? 0 : 1) == ph) idx.push_back(i);
+            for (size_t j0 = 0, n1 = 0; j0 < idx.size(); j0 += n1) {
+                n1 = 0;
+                while (j0 + n1 < idx.size() && (int)n1 < kMaxChain) {
+                    ++n1;
+                    if (cut(idx[j0 + n1 - 1])) break;
+                }
+                ChainParams cpm{};
+                cpm.p = fwd_params(calls[idx[j0]]);
+                cpm.nblk = (int)n1;
+                for (int j = 0; j < cpm.nblk; ++j) {
+                    const Call& c = calls[idx[j0 + j]];
+                    ChainBlock& cb = cpm.blk[j];
+                    cb.k = c.k;
+                    cb.v = c.v;
+                    cb.kpm = c.kpm;
+                    cb.kpm_list = kpm_list_bytes(c) ? (const int*)(wp + lst_off[idx[j0 + j]]) : nullptr;
+                    cb.kv_off = c.kv_off;
+                    cb.Tkv = c.Tkv;
+                    cb.accumulate = plan[idx[j0 + j]].accumulate;
+                }
+                if (int rc = timed_launch([&] { return launch_fwd_bf16_chain(cpm, d, s); },
+                                          "attention kernel launch", s))
+                    return rc;
+            }
+            if (!idx.empty()) covered[ph] = true;
+        }
+    } else {
+        for (int i = 0; i < n_live; ++i) {
+            const Call& c = calls[i];
+            const size_t lb = kpm_list_bytes(c);
+            if (int rc = enqueue(c, lb ? (int*)(wp + lst_off[i]) : nullptr, s)) return rc;
+            covered[plan[i].q_row0 == 0 ? 0 : 1] = true;
+        }
     }
     // rows no sub-call reached (not possible with a causal diagonal, kept for safety)
     const int parts = zigzag ? 2 : 1;

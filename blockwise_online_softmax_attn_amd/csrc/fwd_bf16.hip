@@ -524,6 +524,333 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     if (lse_ptr && hh == 0) *lse_ptr = lse_b;
 }
 
+// ---------------------------------------------------------------------------
+// A ring share's query block against its key/value blocks in ring order, in
+// one launch.  Each workgroup keeps its 256 query rows (Q in registers) and
+// runs the tile pipeline of attn_fwd_bf16_kernel over the concatenation of
+// every block's live tiles, so the loads of a block's first tiles overlap the
+// last tiles of the block before; after a block's last tile each wave writes
+// that block's partial (out, lse) or merges it into the float32 partial (the
+// same epilogue as one launch per block), then starts the next block from an
+// empty state.  The results are those of one attn_fwd_bf16_kernel launch per
+// block, bit for bit.  No window, ALiBi or attention mask.
+template <int D>
+__global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainParams cp) {
+    using G = Geo<D>;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const FwdParams& p = cp.p;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+
+    // workgroup order: as in attn_fwd_bf16_kernel
+    int bid = blockIdx.x;
+    {
+        const int full = (int)gridDim.x & ~7;
+        if (bid < full) bid = (bid & 7) * (full >> 3) + (bid >> 3);
+    }
+    const int qt = p.n_qtiles - 1 - bid % p.n_qtiles;
+    bid /= p.n_qtiles;
+    const int h = bid % p.H;
+    const int b = bid / p.H;
+
+    const int rs = p.row_stride;
+    const uint32_t rs2 = 2u * (uint32_t)rs;
+    const int Tq = p.Tq;
+    const uint16_t* qg = (const uint16_t*)p.q + b * p.q_bstride + (long long)h * D;
+    const bool noskip = (p.flags & ATTN_NO_TILE_SKIP) != 0;
+    const bool causal = p.causal != 0;
+    const float sl2 = p.scale_log2;
+    const int nb = cp.nblk;
+
+    const int q0 = qt * BM;
+    const int qw0 = q0 + w * 32;
+    const int qi = qw0 + l32;
+    const bool qvalid = qi < Tq;
+    const bool wvalid = qw0 < Tq;
+    const int qwlast = min(qw0 + 31, Tq - 1);
+    const int qlast = min(q0 + BM, Tq) - 1;
+
+    // ---- Q operand (rotated when the rotary embedding is on)
+    bf16x8 qreg[G::NC];
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (qvalid) x = *(const uint4*)(qg + (long long)qi * rs + 16 * c + 8 * hh);
+        qreg[c] = __builtin_bit_cast(bf16x8, x);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+    // ---- per block: live tiles of the workgroup, leading tiles every row
+    // allows, tiles that hold allowed keys for this wave's rows; kept in this
+    // wave's LDS table (ntiles | nfull | nact, kMaxChain entries each).
+    typedef const __attribute__((address_space(4))) int* cint_ptr;
+    auto block_list = [&](int s) __attribute__((always_inline)) -> cint_ptr {
+        const int* l = cp.blk[s].kpm_list;
+        const int stride = (cp.blk[s].Tkv + BN - 1) / BN + 2;   // a list per batch row: count, clean, entries
+        return (l && !noskip) ? (cint_ptr)(l + (long long)b * stride) : nullptr;
+    };
+    auto list_tile = [&](cint_ptr kl, int i) __attribute__((always_inline)) -> int { return (int)((uint32_t)kl[2 + i] & ~kTileClean); };
+    int* tab = (int*)(smem + NSLOT * G::SLOT) + w * 3 * kMaxChain;
+    int ntot = 0;
+    for (int s = 0; s < nb; ++s) {
+        const long long delta = p.q_off - cp.blk[s].kv_off;
+        const int Tkv = cp.blk[s].Tkv;
+        cint_ptr kl = block_list(s);
+        long long khi = Tkv;
+        if (!noskip && causal) khi = min(khi, delta + qlast + 1);
+        khi = max(khi, 0LL);
+        const int t_hi = (int)((khi + BN - 1) / BN);
+        int ntl = t_hi;
+        if (kl) {
+            int lo = 0, hi = kl[0];
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (list_tile(kl, mid) < t_hi) lo = mid + 1;
+                else hi = mid;
+            }
+            ntl = lo;
+        }
+        long long kf_hi = Tkv;
+        if (causal) kf_hi = min(kf_hi, q0 + delta + 1);
+        long long nf = kf_hi < 0 ? 0 : kf_hi / BN;
+        if (kl) nf = min(nf, (long long)kl[1]);
+        const bool fm = noskip || (cp.blk[s].kpm && !cp.blk[s].kpm_list);
+        const int nfull = fm ? 0 : (int)min(nf, (long long)ntl);
+        int nact = ntl;
+        if (!wvalid) {
+            nact = 0;
+        } else if (!noskip && causal) {
+            const long long lim = (long long)qwlast + delta;
+            int lo = 0, hi = ntl;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((long long)(kl ? list_tile(kl, mid) : mid) * BN <= lim) lo = mid + 1;
+                else hi = mid;
+            }
+            nact = lo;
+        }
+        if (lane == 0) {
+            tab[s] = ntl;
+            tab[kMaxChain + s] = nfull;
+            tab[2 * kMaxChain + s] = nact;
+        }
+        ntot += ntl;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the table is written before it is read
+
+    // ---- per-lane constants (as in attn_fwd_bf16_kernel)
+    uint32_t koff[G::NC];
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) koff[c] = l32 * G::ROW + 16 * ((2 * c + hh) ^ G::hk(l32));
+    uint32_t voff[G::NDB];
+    {
+        const int jj = lane & 15, grp = lane >> 4;
+        const int r0 = 4 * (grp >> 1) + (jj >> 2);
+        const int hv = G::hv(r0);
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+            const int g = 4 * db + 2 * (grp & 1) + ((jj & 3) >> 1);
+            voff[db] = r0 * G::ROW + 16 * (g ^ hv) + 8 * (jj & 1);
+        }
+    }
+    uint32_t dk[G::NI], dv[G::NI];
+#pragma unroll
+    for (int n = 0; n < G::NI; ++n) {
+        const int m = w * G::NI + n;
+        const int row = m * G::RPB + lane / G::GPR;
+        const int pos = lane % G::GPR;
+        dk[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ G::hk(row));
+        dv[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ G::hv(row));
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+
+    // ---- load cursor: block ls, list position li of the next tile to load,
+    // and that block's addressing (read from the kernel arguments and the
+    // table only when the cursor enters a block: a scalar or LDS read in
+    // every tile would make the tile's operand reads wait with it)
+    int ls = 0, li = 0, l_ntl = 0, l_Tkv = 0;
+    const char* l_kg = nullptr;
+    const char* l_vg = nullptr;
+    cint_ptr l_list = nullptr;
+    auto load_enter = [&](int s) __attribute__((always_inline)) {
+        l_ntl = tab[s];
+        l_Tkv = cp.blk[s].Tkv;
+        l_kg = (const char*)((const uint16_t*)cp.blk[s].k + b * p.kv_bstride + (long long)h * D);
+        l_vg = (const char*)((const uint16_t*)cp.blk[s].v + b * p.kv_bstride + (long long)h * D);
+        l_list = block_list(s);
+    };
+    auto load_skip = [&]() __attribute__((always_inline)) {   // past exhausted (or empty) blocks
+        while (ls < nb && li >= l_ntl) {
+            ++ls;
+            li = 0;
+            if (ls < nb) load_enter(ls);
+        }
+    };
+    if (nb > 0) load_enter(0);
+    load_skip();
+    auto issue_next = [&](int g) __attribute__((always_inline)) {   // the cursor's tile is global tile g
+        const int key0 = (l_list ? list_tile(l_list, li) : li) * BN;
+        const uint32_t nbytes = (uint32_t)min(l_Tkv - 1 - key0, BN - 1) * rs2 + 2u * D;
+        const u32x4 rk = buffer_rsrc(l_kg + (long long)key0 * rs2, nbytes);
+        const u32x4 rv = buffer_rsrc(l_vg + (long long)key0 * rs2, nbytes);
+        const uint32_t base = lds0 + (uint32_t)(g % NSLOT) * G::SLOT + (uint32_t)(w * G::NI) * 1024u;
+#pragma unroll
+        for (int n = 0; n < G::NI; ++n) load_lds16(dk[n], rk, base + 1024u * n);
+#pragma unroll
+        for (int n = 0; n < G::NI; ++n) load_lds16(dv[n], rv, base + G::TILE + 1024u * n);
+        if (++li >= l_ntl) load_skip();
+    };
+
+    // ---- compute cursor: block cs, list position ci, and that block's state
+    int cs = 0, ci = 0;
+    long long c_delta = 0;
+    int c_Tkv = 0, c_ntl = 0, c_nfull = 0, c_nact = 0;
+    cint_ptr c_list = nullptr;
+    const uint8_t* c_kpm = nullptr;
+    bool c_clean_all = true;
+    auto enter = [&](int s) __attribute__((always_inline)) {
+        c_delta = p.q_off - cp.blk[s].kv_off;
+        c_Tkv = cp.blk[s].Tkv;
+        c_list = block_list(s);
+        c_kpm = cp.blk[s].kpm ? cp.blk[s].kpm + b * p.kpm_bstride : nullptr;
+        c_clean_all = cp.blk[s].kpm == nullptr;
+        c_ntl = tab[s];
+        c_nfull = tab[kMaxChain + s];
+        c_nact = tab[2 * kMaxChain + s];
+    };
+    auto tile_mask = [&](int i) __attribute__((always_inline)) -> TileMask {
+        TileMask mk{63, ~0ull, nullptr};
+        const int key0 = (c_list ? list_tile(c_list, i) : i) * BN;
+        long long thr = (long long)c_Tkv - key0 - 1;
+        if (causal) thr = min(thr, (long long)qi + c_delta - key0);
+        mk.thr4 = (int)(thr < -1 ? -1 : (thr > 63 ? 63 : thr)) - 4 * hh;
+        const bool clean = c_list ? ((uint32_t)c_list[2 + i] & kTileClean) != 0 : c_clean_all;
+        uint64_t km = ~0ull;
+        if (c_kpm && !clean) {
+            const bool okk = key0 + lane < c_Tkv && c_kpm[key0 + lane] == 0;
+            km = __ballot(okk);
+        }
+        mk.kml = km >> (4 * hh);
+        return mk;
+    };
+
+    float m_i = -INFINITY;
+    float l_i = 0.f;
+    f32x16 o[G::NDB];
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) o[db] = f32x16{};
+
+    // partial of block s from (m_i, l_i, o), then the empty state
+    float* lse_ptr = p.lse + b * p.lse_bstride + (long long)h * p.lse_hstride + qi;
+    float* og = (float*)p.out + b * p.o_bstride + (long long)qi * rs + (long long)h * D;
+    auto finish_block = [&](int s) __attribute__((always_inline)) {
+        const float lsum = xhalf_sum(l_i);
+        if (qvalid) {
+            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+            const float lse_b = lsum > 0.f ? (m_i + log2f(lsum)) * kLn2 : -INFINITY;
+            if (cp.blk[s].accumulate) {
+                const float la = *lse_ptr;
+                float lse_n, wa, wb;
+                merge_weights(la, lse_b, lse_n, wa, wb);
+#pragma unroll
+                for (int db = 0; db < G::NDB; ++db) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float4* dst = (float4*)(og + db * 32 + 8 * g + 4 * hh);
+                        const float4 oa = *dst;
+                        float4 r;
+                        r.x = merge_value(wa, oa.x, wb, o[db][4 * g + 0] * inv);
+                        r.y = merge_value(wa, oa.y, wb, o[db][4 * g + 1] * inv);
+                        r.z = merge_value(wa, oa.z, wb, o[db][4 * g + 2] * inv);
+                        r.w = merge_value(wa, oa.w, wb, o[db][4 * g + 3] * inv);
+                        *dst = r;
+                    }
+                }
+                if (hh == 0) *lse_ptr = lse_n;
+            } else {
+#pragma unroll
+                for (int db = 0; db < G::NDB; ++db) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float4 r = make_float4(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv,
+                                               o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                        *(float4*)(og + db * 32 + 8 * g + 4 * hh) = r;
+                    }
+                }
+                if (hh == 0) *lse_ptr = lse_b;
+            }
+        }
+        m_i = -INFINITY;
+        l_i = 0.f;
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) o[db] = f32x16{};
+    };
+    // blocks without a live tile for this workgroup: their (empty) partials
+    auto finish_empty_blocks = [&]() __attribute__((always_inline)) {
+        while (cs < nb && tab[cs] == 0) {
+            finish_block(cs);
+            ++cs;
+        }
+        if (cs < nb) enter(cs);
+    };
+    finish_empty_blocks();
+
+    // ---- prologue: tiles 0..2 in flight, tiles 0 and 1 resident
+    constexpr int PT = 2 * G::NI;
+    if (ntot > 0) issue_next(0);
+    if (ntot > 1) issue_next(1);
+    if (ntot > 2) {
+        issue_next(2);
+        wait_barrier<PT>();
+    } else {
+        wait_barrier<0>();
+    }
+
+    // One tile (global index g): as in attn_fwd_bf16_kernel, plus the scores
+    // of the tile when the wave skipped the tile before it, and the block's
+    // epilogue after its last tile.
+    f32x16 s0 = f32x16{}, s1 = f32x16{}, n0, n1;
+    bool have = false;   // the scores of tile g are in the current register set
+    auto step = [&](int g, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1) __attribute__((always_inline)) {
+        const bool more = g + 3 < ntot;
+        if (more) issue_next(g + 3);
+        const bool act = ci < c_nact;
+        if (act) {
+            if (!have) scores<D>(smem + (g % NSLOT) * G::SLOT, koff, qreg, c0, c1);
+            if (ci >= c_nfull) apply_mask(c0, c1, tile_mask(ci));
+            update_max<D>(c0, c1, o, m_i, l_i, sl2);
+            const float nm = (m_i == -INFINITY) ? 0.f : -m_i;
+            bf16x8 pb[4];
+            __builtin_amdgcn_s_setprio(1);
+            exp_and_next<D>(c0, c1, nm, sl2, l_i, pb, smem + ((g + 1) % NSLOT) * G::SLOT, koff, qreg, x0, x1);
+            accumulate_pv<D>(smem + (g % NSLOT) * G::SLOT + G::TILE, voff, pb, o);
+            __builtin_amdgcn_s_setprio(0);
+        }
+        have = act;
+        bool merged = false;
+        if (++ci == c_ntl) {
+            merged = cp.blk[cs].accumulate != 0;
+            finish_block(cs);
+            ++cs;
+            ci = 0;
+            finish_empty_blocks();
+        }
+        // After a merge the epilogue has waited for its own loads of the
+        // partial, so every older tile load is complete too; its stores may
+        // drain during the next tile (the next wait covers them).
+        if (!more) wait_barrier<0>();
+        else if (merged) lds_barrier();
+        else wait_barrier<PT>();
+    };
+    for (int g = 0; g < ntot; g += 2) {
+        step(g, s0, s1, n0, n1);
+        if (g + 1 < ntot) step(g + 1, n0, n1, s0, s1);
+    }
+}
+
 template <int D, bool ALIBI, bool WIN>
 hipError_t launch(const FwdParams& p, hipStream_t s) {
     using G = Geo<D>;
@@ -538,7 +865,28 @@ hipError_t launch(const FwdParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_chain(const ChainParams& c, hipStream_t s) {
+    using G = Geo<D>;
+    constexpr int LDS = G::LDS_BYTES + NW * 3 * kMaxChain * 4;
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = set_lds_limit((const void*)attn_fwd_bf16_chain_kernel<D>, LDS, lds_set); e != hipSuccess)
+        return e;
+    ChainParams q = c;
+    q.p.n_qtiles = (c.p.Tq + BM - 1) / BM;
+    const long long grid = (long long)q.p.n_qtiles * c.p.H * c.p.B;
+    hipLaunchKernelGGL(attn_fwd_bf16_chain_kernel<D>, dim3((unsigned)grid), dim3(NT), LDS, s, q);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_fwd_bf16_chain(const ChainParams& c, int d, hipStream_t s) {
+    if (c.nblk < 1 || c.nblk > kMaxChain || c.p.rope_q || c.p.rope_k || c.p.amask || c.p.alibi ||
+        c.p.win_left >= 0 || c.p.win_right >= 0)
+        return hipErrorInvalidValue;
+    return d == 128 ? launch_chain<128>(c, s) : launch_chain<64>(c, s);
+}
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s) {
     if (p.rope_q || p.rope_k) return hipErrorInvalidValue;   // queries and keys arrive rotated

@@ -324,3 +324,40 @@ def test_ring_share_with_key_padding(case):
         ro, rl = oracle.sdpa(np64(q), np64(k), np64(v), qpos, np.arange(T), causal=causal, kpm=kpm.numpy(),
                              rope_base=10000.0, dtype=dt_name(q))
         compare(out.cpu(), lse.cpu(), ro, rl, dt_name(q), f"rank{rank}")
+
+
+@pytest.mark.parametrize("zigzag,causal,kp,rope,d", [(True, True, 0.0, 10000.0, 128), (False, True, 0.2, 10000.0, 128),
+                                                    (True, False, 0.2, 0.0, 64), (False, False, 0.0, 500.0, 64)])
+def test_ring_share_equals_its_subcalls_bitwise(zigzag, causal, kp, rope, d):
+    """attn_ring_fwd runs each query block's sub-calls in one launch; its out
+    and lse equal, bit for bit, one attn_fwd call per sub-call of
+    attn_ring_plan (in plan order, each writing or merging its partial into a
+    float32 accumulator of its query block), then the cast, on every rank."""
+    P, B, H, T = 4, 1, 2, 1536
+    k = rnd((B, T, H, d), 9601, torch.bfloat16).to(DEV)
+    v = rnd((B, T, H, d), 9602, torch.bfloat16).to(DEV)
+    kpm = workloads.random_mask((B, T), 9603, kp).to(DEV) if kp else None
+    for rank in range(P):
+        q = rnd((B, T // P, H, d), 9610 + rank, torch.bfloat16).to(DEV)
+        out, lse = bosa.attn_ring_fwd(q, k, v, P=P, rank=rank, zigzag=zigzag, causal=causal, kpm=kpm, rope_base=rope)
+        plan = bosa.attn_ring_plan(T, P, rank, zigzag, causal)
+        note(f"ring = sub-calls: zigzag={zigzag} causal={causal} kpm={kp} rope={rope} d={d} rank={rank}: "
+             f"{len(plan)} sub-calls")
+        parts = {}
+        for e in plan:
+            r0, nr, k0, nk = e.q_row0, e.q_rows, e.kv_pos0, e.kv_rows
+            if r0 not in parts:
+                parts[r0] = (torch.empty((B, nr, H, d), dtype=torch.float32, device=DEV),
+                             torch.empty((B, H, nr), dtype=torch.float32, device=DEV))
+            acc, ls = parts[r0]
+            flags = bosa.ATTN_OUT_F32 | (bosa.ATTN_ACCUMULATE if e.accumulate else 0)
+            bosa.attn_fwd(q[:, r0:r0 + nr].contiguous(), k[:, k0:k0 + nk].contiguous(), v[:, k0:k0 + nk].contiguous(),
+                          acc, ls, q_off=e.q_pos0, kv_off=k0, causal=causal,
+                          kpm=None if kpm is None else kpm[:, k0:k0 + nk].contiguous(), rope_base=rope, flags=flags)
+        for r0, (acc, ls) in parts.items():
+            nr = acc.shape[1]
+            o16 = torch.empty((B, nr, H, d), dtype=torch.bfloat16, device=DEV)
+            bosa.attn_cast(acc, o16)
+            torch.cuda.synchronize()
+            assert torch.equal(out[:, r0:r0 + nr].cpu(), o16.cpu()), f"rank {rank} rows {r0}: out"
+            assert torch.equal(lse[:, :, r0:r0 + nr].cpu(), ls.cpu()), f"rank {rank} rows {r0}: lse"
