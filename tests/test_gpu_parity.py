@@ -361,3 +361,8 @@ def test_ring_share_equals_its_subcalls_bitwise(zigzag, causal, kp, rope, d):
             torch.cuda.synchronize()
             assert torch.equal(out[:, r0:r0 + nr].cpu(), o16.cpu()), f"rank {rank} rows {r0}: out"
             assert torch.equal(lse[:, :, r0:r0 + nr].cpu(), ls.cpu()), f"rank {rank} rows {r0}: lse"
+        # every tile visited and masked instead of skipped: the same bits
+        o2, l2 = bosa.attn_ring_fwd(q, k, v, P=P, rank=rank, zigzag=zigzag, causal=causal, kpm=kpm, rope_base=rope,
+                                    flags=bosa.ATTN_NO_TILE_SKIP)
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), o2.cpu()) and torch.equal(lse.cpu(), l2.cpu()), f"rank {rank}: NO_TILE_SKIP"
