@@ -577,14 +577,14 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
     // are the local queries, which every sub-call reads again (rotating them
     // in each sub-call's kernel would re-read the float32 cos/sin table, twice
     // the bytes of the queries, once per sub-call); the copies hold the same
-    // values the kernel's own rotation gives.
+    // values the kernel's own rotation gives.  The local queries' positions
+    // are positions of the keys, so one table over [0, T) serves both.
     const bool krot = rope && dtype == ATTN_BF16;
-    const size_t tab_q = rope ? align_up((size_t)Tl * (d / 2) * sizeof(float2)) : 0;
     const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(float2)) : 0;
     const size_t kbuf = krot ? align_up((size_t)B * T * H * d * 2) : 0;
     const size_t qbuf = krot ? align_up((size_t)B * Tl * H * d * 2) : 0;
     std::vector<size_t> lst_off(n_live, 0);
-    size_t total = tab_q + tab_k + kbuf + qbuf;
+    size_t total = tab_k + kbuf + qbuf;
     std::vector<Call> calls(n_live);
     const int rs = H * d;
     const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
@@ -620,35 +620,34 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
     hipError_t err = ws.alloc(total, s);
     if (err != hipSuccess) return hip_fail(err, "scratch allocation");
     char* wp = (char*)ws.ptr;
+    const float2* tab = (const float2*)wp;
+    char* krb = wp + tab_k;
+    char* qrb = krb + kbuf;
     if (rope) {
-        const double lb = std::log(rope_base);
-        // local rows: contiguous chunk(s) at their absolute positions
-        const int parts = zigzag ? 2 : 1;
-        const int c = Tl / parts;
-        for (int ph = 0; ph < parts && err == hipSuccess; ++ph) {
-            const long long pos0 = (long long)(ph == 0 ? rank : 2 * P - 1 - rank) * c;
-            err = launch_rope_table((float2*)wp + (size_t)ph * c * (d / 2), pos0, c, d, lb, s);
-        }
-        if (err == hipSuccess) err = launch_rope_table((float2*)(wp + tab_q), 0, T, d, lb, s);
+        err = launch_rope_table((float2*)wp, 0, T, d, std::log(rope_base), s);
         if (err != hipSuccess) return hip_fail(err, "rotary table launch");
         if (krot) {
-            err = launch_rope_copy_bf16(k, wp + tab_q + tab_k, (const float2*)(wp + tab_q), B, T, H, d, s);
+            // local rows [0, c) sit at rank * c, zigzag rows [c, 2c) at (2P - 1 - rank) * c
+            const int parts = zigzag ? 2 : 1;
+            const int c = Tl / parts;
+            err = launch_rope_copy_bf16(k, krb, tab, B, T, H, d, s);
             if (err == hipSuccess)
-                err = launch_rope_copy_bf16(q, wp + tab_q + tab_k + kbuf, (const float2*)wp, B, Tl, H, d, s);
+                err = launch_rope_copy_bf16(q, qrb, tab, B, Tl, H, d, c, (long long)rank * c,
+                                            (long long)(2 * P - 1 - rank) * c, s);
             if (err != hipSuccess) return hip_fail(err, "key / query rotation launch");
         }
     }
-    bool covered[2] = {false, false};
     for (int i = 0; i < n_live; ++i) {
         Call& c = calls[i];
         if (krot) {
-            c.k = (const uint16_t*)(wp + tab_q + tab_k) + (size_t)plan[i].kv_pos0 * rs;
-            c.q = (const uint16_t*)(wp + tab_q + tab_k + kbuf) + (size_t)plan[i].q_row0 * rs;
+            c.k = (const uint16_t*)krb + (size_t)plan[i].kv_pos0 * rs;
+            c.q = (const uint16_t*)qrb + (size_t)plan[i].q_row0 * rs;
         } else if (rope) {
-            c.rope_q = (const float2*)wp + (size_t)plan[i].q_row0 * (d / 2);
-            c.rope_k = (const float2*)(wp + tab_q) + (size_t)plan[i].kv_pos0 * (d / 2);
+            c.rope_q = tab + (size_t)plan[i].q_pos0 * (d / 2);
+            c.rope_k = tab + (size_t)plan[i].kv_pos0 * (d / 2);
         }
     }
+    bool covered[2] = {false, false};
     // bf16 without a window or ALiBi: a query block's sub-calls run in plan
     // order, several to a launch of the chained kernel, with the same
     // per-block partials and merges as one launch per sub-call.  A chain ends

@@ -227,6 +227,10 @@ hipError_t launch_rope_apply(void* x, const long long* pos, double log_base, int
                              int is_bf16, hipStream_t s);
 hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
                                  hipStream_t s);
+// The same with row t taking table row t + off0 for t < split, else
+// t - split + off1.
+hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
+                                 int split, long long off0, long long off1, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t s);
 // ld2[b][h][i] = (lse * log2 e or +inf when lse = -inf, sum_c dout * out) for bf16 dout, out.

@@ -162,19 +162,24 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(void* __restrict__ x, c
 }
 
 // dst = src with the rotary embedding of its position applied to every head
-// (bf16, [B][T][H][d] rows; tab[t] holds the (cos, sin) pairs of position t).
-// The attention kernel then streams already-rotated keys; the rotation is the
-// same float32 arithmetic as the fused query rotation, so results match it bit
-// for bit.  One thread per 16-byte granule (4 coordinate pairs).
+// (bf16, [B][T][H][d] rows).  Row t takes table row t + off0 for t < split,
+// else t - split + off1: a ring share's local queries are two runs of
+// positions, all of them positions of the keys, so one table of (cos, sin)
+// pairs over the keys' positions serves both.  The attention kernel then
+// streams already-rotated operands; the rotation is the same float32
+// arithmetic as rope_apply's, bit for bit.  One thread per 16-byte granule
+// (4 coordinate pairs).
 __global__ __launch_bounds__(256) void rope_copy_bf16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                              const float2* __restrict__ tab, long long n, int T,
-                                                             int H, int gpr) {
+                                                             int H, int gpr, int split, long long off0,
+                                                             long long off1) {
     const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n) return;
     const long long row = g / gpr;   // (b * T + t) * H + h
     const int c = (int)(g - row * gpr);
     const int t = (int)((row / H) % T);
-    const float4* tp = (const float4*)(tab + (long long)t * (4 * gpr) + 4 * c);
+    const long long tr = t < split ? off0 + t : off1 + (t - split);
+    const float4* tp = (const float4*)(tab + tr * (4 * gpr) + 4 * c);
     dst[g] = rope8_bf16(src[g], tp[0], tp[1]);
 }
 
@@ -250,12 +255,17 @@ hipError_t launch_rope_apply(void* x, const long long* pos, double log_base, int
 }
 
 hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
-                                 hipStream_t s) {
+                                 int split, long long off0, long long off1, hipStream_t s) {
     const long long n = (long long)B * T * H * (d / 8);
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(rope_copy_bf16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, (const uint4*)src, (uint4*)dst,
-                       tab, n, T, H, d / 8);
+                       tab, n, T, H, d / 8, split, off0, off1);
     return hipGetLastError();
+}
+
+hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
+                                 hipStream_t s) {
+    return launch_rope_copy_bf16(src, dst, tab, B, T, H, d, T, 0, 0, s);
 }
 
 hipError_t launch_fill_empty(void* out, int out_bf16, float* lse, int B, int H, int rows, int d, long long o_bstride,
