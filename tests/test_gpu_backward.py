@@ -237,3 +237,30 @@ def test_ring_backward_with_key_padding(zigzag, causal):
         ref = oracle.sdpa_backward(np64(q), np64(k), np64(v), np64(dout), qpos, np.arange(T), causal=causal,
                                    kpm=kpm.numpy(), rope_base=10000.0, dtype="bf16")
         compare_grads((dq.cpu(), dk.cpu(), dv.cpu()), ref, f"rank{rank}")
+
+
+def test_ring_backward_with_a_fully_padded_row():
+    """attn_ring_bwd where every key of batch row 1 is padded: that row's
+    queries saw no key (out = 0, lse = -inf), so its dq, dk and dv are zero;
+    row 0 against the oracle; zigzag, causal, RoPE, every rank of P = 4."""
+    P, B, H, T, d = 4, 2, 2, 1024, 128
+    kpm = workloads.random_mask((B, T), 9700, 0.2)
+    kpm[1, :] = 1
+    for rank in range(P):
+        qpos = oracle.local_query_positions(T, P, rank, True)
+        seed = 9710 + 10 * rank
+        q = rnd((B, T // P, H, d), seed)
+        k = rnd((B, T, H, d), seed + 1)
+        v = rnd((B, T, H, d), seed + 2)
+        dout = rnd((B, T // P, H, d), seed + 3)
+        note(f"ring backward fully padded row: rank={rank}")
+        qd, kd, vd, od, md = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), kpm.to(DEV)
+        out, lse = bosa.attn_ring_fwd(qd, kd, vd, P=P, rank=rank, zigzag=True, causal=True, kpm=md, rope_base=10000.0)
+        dq, dk, dv = bosa.attn_ring_bwd(qd, kd, vd, out, od, lse, P=P, rank=rank, zigzag=True, causal=True, kpm=md,
+                                        rope_base=10000.0)
+        torch.cuda.synchronize()
+        for g in (dq, dk, dv):
+            assert not torch.any(g[1].float().cpu() != 0), "gradient of the padded row"
+        ref = oracle.sdpa_backward(np64(q), np64(k), np64(v), np64(dout), qpos, np.arange(T), causal=True,
+                                   kpm=kpm.numpy(), rope_base=10000.0, dtype="bf16")
+        compare_grads((dq.cpu(), dk.cpu(), dv.cpu()), ref, f"rank{rank}")

@@ -366,3 +366,29 @@ def test_ring_share_equals_its_subcalls_bitwise(zigzag, causal, kp, rope, d):
                                     flags=bosa.ATTN_NO_TILE_SKIP)
         torch.cuda.synchronize()
         assert torch.equal(out.cpu(), o2.cpu()) and torch.equal(lse.cpu(), l2.cpu()), f"rank {rank}: NO_TILE_SKIP"
+
+
+@pytest.mark.parametrize("zigzag,causal,dtype", [(True, True, torch.bfloat16), (False, False, torch.bfloat16),
+                                                 (False, True, torch.float32)])
+def test_ring_share_with_a_fully_padded_row(zigzag, causal, dtype):
+    """attn_ring_fwd where every key of batch row 1 is padded: each of that
+    row's sub-calls has no live tile (the chained kernel finishes them as
+    empty partials), so its rows come out as the merge identity, out = 0 and
+    lse = -inf; row 0 (random holes) still matches the oracle, every rank."""
+    P, B, H, T, d = 4, 2, 2, 1024, 128
+    kpm = workloads.random_mask((B, T), 9600 + int(zigzag), 0.2)
+    kpm[1, :] = 1
+    for rank in range(P):
+        qpos = oracle.local_query_positions(T, P, rank, zigzag)
+        seed = 9610 + 10 * rank + int(zigzag)
+        q = rnd((B, T // P, H, d), seed, dtype)
+        k = rnd((B, T, H, d), seed + 1, dtype)
+        v = rnd((B, T, H, d), seed + 2, dtype)
+        note(f"ring fully padded row: zigzag={zigzag} causal={causal} {dtype} rank={rank}")
+        out, lse = bosa.attn_ring_fwd(q.to(DEV), k.to(DEV), v.to(DEV), P=P, rank=rank, zigzag=zigzag, causal=causal,
+                                      kpm=kpm.to(DEV), rope_base=10000.0)
+        torch.cuda.synchronize()
+        ro, rl = oracle.sdpa(np64(q), np64(k), np64(v), qpos, np.arange(T), causal=causal, kpm=kpm.numpy(),
+                             rope_base=10000.0, dtype=dt_name(q))
+        assert np.all(np.isneginf(rl[1])) and not np.any(ro[1])
+        compare(out.cpu(), lse.cpu(), ro, rl, dt_name(q), f"rank{rank}")
