@@ -34,10 +34,12 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -204,6 +206,67 @@ def cpu_model():
     return None
 
 
+class ClockSampler:
+    """The shader clock and the board power while a block runs: a thread reads
+    the driver's current sclk level (the line of pp_dpm_sclk marked '*') and
+    hwmon power1_input every `period` seconds.  Reading these files starts no
+    program and makes no GPU call.  With no such files (or more than one GPU's)
+    the summary is None."""
+
+    def __init__(self, period: float = 0.01):
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.sclk_file = cards[0] if len(cards) == 1 else None
+        pw = sorted(glob.glob(os.path.join(os.path.dirname(cards[0]), "hwmon", "hwmon*", "power1_input"))) \
+            if self.sclk_file else []
+        self.power_file = pw[0] if pw else None
+        self.period = period
+        self.mhz, self.watts = [], []
+        self._stop = threading.Event()
+        self._thread = None
+
+    def _read(self):
+        try:
+            with open(self.sclk_file) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        self.mhz.append(float(line.split(":", 1)[1].strip().split("Mhz")[0]))
+                        break
+            if self.power_file:
+                with open(self.power_file) as f:
+                    self.watts.append(int(f.read().strip()) / 1e6)
+        except (OSError, ValueError, IndexError):
+            pass
+
+    def _run(self):
+        while not self._stop.wait(self.period):
+            self._read()
+
+    def __enter__(self):
+        if self.sclk_file:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.mhz:
+            return None
+        m = np.asarray(self.mhz)
+        out = {"sclk_mhz": {"mean": float(m.mean()), "min": float(m.min()), "max": float(m.max()),
+                            "samples": int(m.size)},
+               "source": "pp_dpm_sclk current level, sampled every %g s over the timed steps and the "
+                         "per-launch timing" % self.period}
+        if self.watts:
+            p = np.asarray(self.watts)
+            out["power_w"] = {"mean": float(p.mean()), "max": float(p.max())}
+        return out
+
+
 def step_stats(step, n: int) -> dict:
     """Wall time of each of n further steps: one HIP event at every step
     boundary on the current stream (a separate pass, after the timed one)."""
@@ -296,21 +359,22 @@ def run_decode(args, w) -> dict:
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {args.steps} decode steps")
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    gbs = nbytes / args.steps / (ms * 1e-3) / 1e9
-    # the decode kernel alone, timed with events around each launch over K
-    # further steps (kept out of the step time above)
-    L2 = ln.cpu().to(torch.int64)
-    nbytes_k = sum(int((L2 + s + 1).sum()) for s in range(args.steps)) * w.H * w.d * 2 * esize
-    with bosa.KernelTimer(max_launches=args.steps + 16) as kt:
+    with ClockSampler() as clk:
+        start.record()
         for _ in range(args.steps):
             step()
+        end.record()
         torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        gbs = nbytes / args.steps / (ms * 1e-3) / 1e9
+        # the decode kernel alone, timed with events around each launch over K
+        # further steps (kept out of the step time above)
+        L2 = ln.cpu().to(torch.int64)
+        nbytes_k = sum(int((L2 + s + 1).sum()) for s in range(args.steps)) * w.H * w.d * 2 * esize
+        with bosa.KernelTimer(max_launches=args.steps + 16) as kt:
+            for _ in range(args.steps):
+                step()
+            torch.cuda.synchronize()
     kms = np.asarray(kt.ms, dtype=np.float64)
     achieved = nbytes_k / (kms.sum() * 1e-3) / 1e9 if kms.sum() > 0 else None
     stats = step_stats(step, args.steps)
@@ -361,6 +425,7 @@ def run_decode(args, w) -> dict:
                      "avg_launch_ms": float(kms.mean()) if len(kms) else None,
                      "bytes_per_launch": nbytes_k / max(len(kms), 1)},
         "cpu_baseline": cpu,
+        "clock": clk.summary(),
     }
 
 
@@ -488,19 +553,20 @@ def main() -> int:
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    # the attention kernels alone: HIP events around every launch, on the
-    # launch's stream, over K further steps (kept out of the step time above,
-    # where they would add a gap per launch)
-    with bosa.KernelTimer(max_launches=args.steps * launches + 16) as kt:
+    with ClockSampler() as clk:
+        start.record()
         for _ in range(args.steps):
             step()
+        end.record()
         torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        # the attention kernels alone: HIP events around every launch, on the
+        # launch's stream, over K further steps (kept out of the step time above,
+        # where they would add a gap per launch)
+        with bosa.KernelTimer(max_launches=args.steps * launches + 16) as kt:
+            for _ in range(args.steps):
+                step()
+            torch.cuda.synchronize()
     stats = step_stats(step, args.steps)
     tflops = flops / (ms * 1e-3) / 1e12
     kms = np.asarray(kt.ms, dtype=np.float64)
@@ -568,7 +634,12 @@ def main() -> int:
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "clock": clk.summary(),
     }
+    clock = line["clock"]
+    if clock and w.dtype == "bf16":
+        # the same MFMA rate per clock at the clock the work ran at
+        clock["bf16_peak_at_mean_sclk_tflops"] = peak * clock["sclk_mhz"]["mean"] / 2400.0
     print(json.dumps(line), flush=True)
     return 0
 
