@@ -111,8 +111,18 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int cc) {
     return __builtin_bit_cast(bf16x8, u);
 }
 
-// Workgroup renumbering for the eight XCDs (each receives a contiguous range).
-__device__ __forceinline__ int xcd_order(int bid) {
+// Workgroup renumbering for the eight XCDs: workgroup b runs on XCD b % 8,
+// and the result l gives the (batch row, head) pair l / nt and its tile
+// l % nt.  Each XCD receives whole pairs (their tiles share its L2): a
+// contiguous range of them, or, with `spread` (the pairs' work differs, as
+// with a key-padding length per batch row) and a pair count that is a
+// multiple of 8, the pairs round-robin, so that one batch row's pairs are
+// spread over all XCDs.
+__device__ __forceinline__ int xcd_order(int bid, int nt, bool spread) {
+    if (spread && (((int)gridDim.x / nt) & 7) == 0) {
+        const int k = bid >> 3;
+        return ((k / nt) * 8 + (bid & 7)) * nt + k % nt;
+    }
     const int full = (int)gridDim.x & ~7;
     return bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
 }
@@ -134,7 +144,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
-    int bid = xcd_order(blockIdx.x);
+    int bid = xcd_order(blockIdx.x, p.n_tiles, p.kpm != nullptr && p.B > 1);
     const int qt = p.n_tiles - 1 - bid % p.n_tiles;   // heaviest causal query tiles first
     bid /= p.n_tiles;
     const int h = bid % p.H, b = bid / p.H;
@@ -389,7 +399,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const int l32 = lane & 31, hh = lane >> 5;
     const bool roleA = w < 4;
     const int kb = w & 3;
-    int bid = xcd_order(blockIdx.x);
+    int bid = xcd_order(blockIdx.x, p.n_tiles, p.kpm != nullptr && p.B > 1);
     const int kt = bid % p.n_tiles;   // low key tiles see the most queries under causal order
     bid /= p.n_tiles;
     const int h = bid % p.H, b = bid / p.H;

@@ -202,6 +202,37 @@ __device__ __forceinline__ void accumulate_pv(const char* Vt, const uint32_t (&v
     }
 }
 
+// Query tile, batch row and head of this workgroup.  Workgroup b is
+// dispatched to XCD b % 8 (each XCD has its own L2), so the k-th workgroup of
+// XCD x is b = 8k + x.  Each XCD takes whole (batch row, head) pairs, so the
+// query tiles of one head share that XCD's L2 for K and V: a contiguous range
+// of pairs, or, when the pairs' work differs (`spread`: the batch rows have
+// their own key-padding lengths), pairs round-robin (pair 8j + x is its j-th),
+// so that the pairs of one batch row are spread over all XCDs instead of
+// filling some of them.  Within a pair the heaviest query tiles (most keys
+// under causal order) come first.  Round-robin needs a pair count that is a
+// multiple of 8.
+__device__ __forceinline__ void wg_tile(const FwdParams& p, bool spread, int& qt, int& b, int& h) {
+    const int nq = p.n_qtiles;
+    const int bid = blockIdx.x;
+    const int npairs = (int)gridDim.x / nq;
+    int bh, t;
+    if (spread && (npairs & 7) == 0) {
+        const int k = bid >> 3;
+        bh = (k / nq) * 8 + (bid & 7);
+        t = k % nq;
+    } else {
+        int l = bid;
+        const int full = (int)gridDim.x & ~7;
+        if (l < full) l = (l & 7) * (full >> 3) + (l >> 3);
+        bh = l / nq;
+        t = l % nq;
+    }
+    qt = nq - 1 - t;
+    h = bh % p.H;
+    b = bh / p.H;
+}
+
 template <int D, bool ALIBI, bool WIN>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p) {
     using G = Geo<D>;
@@ -212,20 +243,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // Workgroup b is dispatched to XCD b % 8 (each XCD has its own L2).  The
-    // logical order is renumbered so that every XCD receives a contiguous range
-    // of it: the query tiles of one head then share that XCD's L2 for K and V.
-    // Within the logical order the heaviest query tiles (most keys under causal
-    // order) come first.
-    int bid = blockIdx.x;
-    {
-        const int full = (int)gridDim.x & ~7;
-        if (bid < full) bid = (bid & 7) * (full >> 3) + (bid >> 3);
-    }
-    const int qt = p.n_qtiles - 1 - bid % p.n_qtiles;
-    bid /= p.n_qtiles;
-    const int h = bid % p.H;
-    const int b = bid / p.H;
+    int qt, b, h;
+    wg_tile(p, p.kpm != nullptr && p.B > 1, qt, b, h);
 
     const int rs = p.row_stride;
     const uint32_t rs2 = 2u * (uint32_t)rs;   // bytes between consecutive keys
@@ -545,16 +564,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // workgroup order: as in attn_fwd_bf16_kernel
-    int bid = blockIdx.x;
-    {
-        const int full = (int)gridDim.x & ~7;
-        if (bid < full) bid = (bid & 7) * (full >> 3) + (bid >> 3);
-    }
-    const int qt = p.n_qtiles - 1 - bid % p.n_qtiles;
-    bid /= p.n_qtiles;
-    const int h = bid % p.H;
-    const int b = bid / p.H;
+    int qt, b, h;
+    wg_tile(p, cp.blk[0].kpm != nullptr && p.B > 1, qt, b, h);
 
     const int rs = p.row_stride;
     const uint32_t rs2 = 2u * (uint32_t)rs;

@@ -18,7 +18,7 @@ import torch
 import blockwise_online_softmax_attn_amd as bosa
 import oracle
 import workloads
-from gpu_helpers import DEV, note, np64
+from gpu_helpers import DEV, compare, note, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -264,3 +264,28 @@ def test_ring_backward_with_a_fully_padded_row():
         ref = oracle.sdpa_backward(np64(q), np64(k), np64(v), np64(dout), qpos, np.arange(T), causal=True,
                                    kpm=kpm.numpy(), rope_base=10000.0, dtype="bf16")
         compare_grads((dq.cpu(), dk.cpu(), dv.cpu()), ref, f"rank{rank}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_batch_rows_with_different_padding(causal):
+    """Forward and backward with B*H a multiple of 8 and a key-padding mask
+    whose valid length differs per batch row (the workgroups then spread the
+    (batch row, head) pairs over the XCDs round-robin): B = 2, H = 4,
+    lengths 700 and 230 of 700 keys, against the oracle."""
+    B, H, T, d = 2, 4, 700, 128
+    kpm = torch.zeros((B, T), dtype=torch.uint8)
+    kpm[1, 230:] = 1
+    seed = 9800 + int(causal)
+    q, k, v, dout = (rnd((B, T, H, d), seed + i) for i in range(4))
+    note(f"batch rows with different padding: causal={causal}")
+    qd, kd, vd, od, md = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), kpm.to(DEV)
+    out, lse = bosa.attn_fwd(qd, kd, vd, causal=causal, kpm=md, rope_base=10000.0)
+    dq, dk, dv = bosa.attn_bwd(qd, kd, vd, out, od, lse, causal=causal, kpm=md, rope_base=10000.0,
+                               flags=bosa.ATTN_OUT_F32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(np64(q), np64(k), np64(v), causal=causal, kpm=kpm.numpy(), rope_base=10000.0,
+                              dtype="bf16")
+    compare(out.cpu(), lse.cpu(), ro, rl, "bf16", "forward")
+    ref = oracle.attention_backward(np64(q), np64(k), np64(v), np64(dout), causal=causal, kpm=kpm.numpy(),
+                                    rope_base=10000.0, dtype="bf16")
+    compare_grads((dq.cpu(), dk.cpu(), dv.cpu()), ref, "backward")
