@@ -19,6 +19,11 @@ roofline = the attention kernel alone: the same algorithmic FLOPs divided by
          MI355X dense bf16 MFMA peak (2516.6 TFLOP/s).
 cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample
          of the same workload (rank 0, one GPU only).
+clock  = the shader clock and board power sampled from sysfs over the timing.
+warmup = untimed steps before the timed ones: --warmup W runs exactly W; by
+         default at least 5 and at least 0.2 s of them, since the clock climbs
+         from idle over the first tens of milliseconds of load (on the encoder
+         workload five warm-up steps left the first timed steps 5-15% slow).
 
 --pass bwd times the backward of the same share instead (attn_ring_bwd, or
 attn_bwd for a single call): 8 d algorithmic FLOPs per allowed pair (dP, dV,
@@ -267,6 +272,26 @@ class ClockSampler:
         return out
 
 
+WARMUP_MIN_S = 0.2
+
+
+def warm_up(step, n) -> int:
+    """Run n untimed steps; with n None, at least 5 steps and at least
+    WARMUP_MIN_S seconds of them (the clock climbs from its idle level over
+    the first tens of milliseconds of load).  Returns the number run."""
+    if n is not None:
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        return n
+    done, t0 = 0, time.perf_counter()
+    while done < 5 or time.perf_counter() - t0 < WARMUP_MIN_S:
+        step()
+        torch.cuda.synchronize()
+        done += 1
+    return done
+
+
 def step_stats(step, n: int) -> dict:
     """Wall time of each of n further steps: one HIP event at every step
     boundary on the current stream (a separate pass, after the timed one)."""
@@ -350,9 +375,7 @@ def run_decode(args, w) -> dict:
         bosa.attn_kv_append(kn, vn, kc, vc, ln, rope_base=w.rope_base)
         bosa.attn_decode(q, kc, vc, ln, out=out, lse=lse, rope_base=w.rope_base)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.warmup = warm_up(step, args.warmup)
     L_start = ln.cpu().to(torch.int64)
     # the s-th timed step sees L_start + s + 1 slots per row
     nbytes = sum(int((L_start + s + 1).sum()) for s in range(args.steps)) * w.H * w.d * 2 * esize
@@ -485,7 +508,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 5 and at least %g s of them, which lets the "
+                         "shader clock ramp up from idle)" % WARMUP_MIN_S)
     ap.add_argument("--workload", type=int, default=4, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward share (default, the headline metric) or its backward")
@@ -537,7 +562,7 @@ def main() -> int:
     # backward dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q (the scores
     # the kernels recompute are not counted)
     flops = (8.0 if bwd else 4.0) * w.d * pairs
-    log(f"{pairs} allowed pairs/step = {flops:.4e} FLOPs; {launches} attention sub-calls/step; warmup {args.warmup}")
+    log(f"{pairs} allowed pairs/step = {flops:.4e} FLOPs; {launches} attention sub-calls/step")
     if args.copy_calibration_mib:
         # a plain copy of known size through the library's float32 copy kernel:
         # reads and writes copy_calibration_mib MiB once each
@@ -546,9 +571,7 @@ def main() -> int:
         bosa.attn_cast(src, dst)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.warmup = warm_up(step, args.warmup)
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {args.steps} steps")
