@@ -162,10 +162,12 @@ def make_step(w, plan, dev_inputs):
         def step():
             bosa.attn_ring_fwd(dq, dk, dv, P=w.ring_P, rank=w.ring_rank, zigzag=w.zigzag, causal=w.causal,
                                kpm=dkpm, rope_base=w.rope_base, out=out, lse=lse, acc=acc)
+        step.outputs = (out, lse)
         return step, len(plan)
 
     def step():
         bosa.attn_fwd(dq, dk, dv, out, lse, causal=w.causal, kpm=dkpm, rope_base=w.rope_base)
+    step.outputs = (out, lse)
     return step, 1
 
 
@@ -290,6 +292,44 @@ def warm_up(step, n) -> int:
         torch.cuda.synchronize()
         done += 1
     return done
+
+
+def graph_pass(step, n: int, outputs) -> dict:
+    """One step captured into a HIP graph (torch.cuda.CUDAGraph) and replayed:
+    each of three checked replays, with eager work between them, must give
+    the eager step's outputs bit for bit; then n replays are timed."""
+    try:
+        step()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outputs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for t in outputs:
+                t.fill_(0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(outputs, ref)):
+                return {"error": "a graph replay differs from the eager step"}
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(n):
+            g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        return {"ms_per_step": start.elapsed_time(end) / n, "steps": n, "replays_checked": 3}
+    except RuntimeError as e:   # capture refused by the runtime or the library
+        torch.cuda.synchronize()
+        return {"error": str(e)[:300]}
 
 
 def step_stats(step, n: int) -> dict:
@@ -517,6 +557,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured into a HIP graph (forward passes; reported as 'graph')")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (byte-counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -591,6 +633,14 @@ def main() -> int:
                 step()
             torch.cuda.synchronize()
     stats = step_stats(step, args.steps)
+    graph = None
+    if args.graph and not bwd:
+        graph = graph_pass(step, args.steps, step.outputs)
+        if "ms_per_step" in graph:
+            graph["value"] = flops / (graph["ms_per_step"] * 1e-3) / 1e12
+            log(f"graph replay: {graph['ms_per_step']:.4f} ms/step, {graph['value']:.1f} TFLOP/s")
+        else:
+            log(f"graph: {graph['error']}")
     tflops = flops / (ms * 1e-3) / 1e12
     kms = np.asarray(kt.ms, dtype=np.float64)
     kern_ms = float(kms.sum())
@@ -659,6 +709,8 @@ def main() -> int:
         "cpu_baseline": cpu,
         "clock": clk.summary(),
     }
+    if graph is not None:
+        line["graph"] = graph
     clock = line["clock"]
     if clock and w.dtype == "bf16":
         # the same MFMA rate per clock at the clock the work ran at
