@@ -18,27 +18,41 @@ __global__ void rope_table_kernel(float2* __restrict__ tab, long long pos0, int 
     tab[idx] = rope_cos_sin(pos0 + i, t, d, log_base);
 }
 
-// Classification of a key tile under the key-padding mask.
+// Classification of keys [k0, k1) under the key-padding mask (nonzero =
+// masked): any_ok = some key allowed, all_ok = every key allowed.  Whole
+// 16-byte granules are tested four bytes at a time when the row is aligned.
+__device__ __forceinline__ bool word_has_zero_byte(uint32_t v) { return ((v - 0x01010101u) & ~v & 0x80808080u) != 0; }
 __device__ __forceinline__ void classify(const uint8_t* row, int k0, int k1, bool& any_ok, bool& all_ok) {
     any_ok = false;
     all_ok = true;
-    for (int k = k0; k < k1; ++k) {
+    int k = k0;
+    if ((((uintptr_t)(row + k)) & 15) == 0) {
+        for (; k + 16 <= k1; k += 16) {
+            const uint4 u = *(const uint4*)(row + k);
+            any_ok |= word_has_zero_byte(u.x) | word_has_zero_byte(u.y) | word_has_zero_byte(u.z) |
+                      word_has_zero_byte(u.w);
+            all_ok &= (u.x | u.y | u.z | u.w) == 0;
+        }
+    }
+    for (; k < k1; ++k) {
         const bool ok = row[k] == 0;
         any_ok |= ok;
         all_ok &= ok;
     }
 }
 
-// One workgroup per batch row: list[0] = number of tiles with at least one
-// allowed key, list[1] = number of leading tiles with no masked key, followed
-// by the live tile indices in increasing order (top bit set when every key of
-// the tile is allowed).  Fully masked tiles are skipped by the attention
-// kernel without being read.
+// One workgroup (4 waves) per batch row: list[0] = number of tiles with at
+// least one allowed key, list[1] = number of leading tiles with no masked
+// key, followed by the live tile indices in increasing order (top bit set
+// when every key of the tile is allowed).  Fully masked tiles are skipped by
+// the attention kernel without being read.  Thread i classifies a run of
+// consecutive tiles; the runs' live counts are turned into write offsets by a
+// scan over the workgroup (lane shuffles within a wave, LDS across waves).
 __global__ __launch_bounds__(256) void kpm_tiles_kernel(const uint8_t* __restrict__ kpm, long long bstride, int Tkv,
                                                         int tile, int* __restrict__ list, int list_stride) {
-    __shared__ int counts[256];
+    __shared__ int wave_sum[4];
     __shared__ int first_unclean;
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint8_t* row = kpm + b * bstride;
     int* out = list + (long long)b * list_stride;
     const int ntk = (Tkv + tile - 1) / tile;
@@ -53,21 +67,27 @@ __global__ __launch_bounds__(256) void kpm_tiles_kernel(const uint8_t* __restric
         cnt += any_ok ? 1 : 0;
         if (!all_ok && unclean == ntk) unclean = t;
     }
-    counts[tid] = cnt;
     if (unclean < ntk) atomicMin(&first_unclean, unclean);
+    // inclusive scan of cnt within the wave, then across the four waves
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) wave_sum[wv] = inc;
     __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        before += i < wv ? wave_sum[i] : 0;
+        total += wave_sum[i];
+    }
     if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < 256; ++i) {
-            const int c = counts[i];
-            counts[i] = run;
-            run += c;
-        }
-        out[0] = run;
+        out[0] = total;
         out[1] = first_unclean;
     }
-    __syncthreads();
-    int pos = counts[tid];
+    int pos = before + inc - cnt;
     for (int t = t0; t < t1; ++t) {
         bool any_ok, all_ok;
         classify(row, t * tile, min((t + 1) * tile, Tkv), any_ok, all_ok);
