@@ -284,7 +284,13 @@ int attn_ring_plan(int T, int P, int rank, int zigzag, int causal, attn_ring_cal
  *             (may equal out when dtype is ATTN_F32).
  *  kpm        device uint8 (B, T) or NULL, over absolute key positions.
  *  Other arguments as attn_fwd.  The work is the sub-calls of attn_ring_plan,
- *  issued in order on `stream`, then one attn_cast of acc into out.
+ *  issued in order on `stream`, then one attn_cast of acc into out.  In bf16
+ *  (without window or ALiBi) up to four consecutive sub-calls of one query
+ *  block run in one kernel launch, with each sub-call's partial written or
+ *  merged exactly as by its own launch: out and lse are bit for bit those of
+ *  one attn_fwd call per sub-call.  With RoPE the call rotates every key
+ *  block and the local queries once into stream-ordered scratch (released on
+ *  `stream` when the call's work is done).
  */
 int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse, float* acc,
                   int B, int H, int T, int d, int P, int rank, int zigzag, int causal,
