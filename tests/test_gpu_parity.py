@@ -392,3 +392,28 @@ def test_ring_share_with_a_fully_padded_row(zigzag, causal, dtype):
                              rope_base=10000.0, dtype=dt_name(q))
         assert np.all(np.isneginf(rl[1])) and not np.any(ro[1])
         compare(out.cpu(), lse.cpu(), ro, rl, dt_name(q), f"rank{rank}")
+
+
+@pytest.mark.parametrize("zigzag", [True, False])
+def test_ring_share_batch_rows_with_different_padding(zigzag):
+    """attn_ring_fwd with B*H a multiple of 8 and batch rows padded to
+    different lengths (the chained kernel then spreads the (batch row, head)
+    pairs over the XCDs round-robin): B = 2, H = 4, P = 4, every rank,
+    against the oracle."""
+    P, B, H, T, d = 4, 2, 4, 1024, 128
+    kpm = torch.zeros((B, T), dtype=torch.uint8)
+    kpm[0, 900:] = 1
+    kpm[1, 333:] = 1
+    for rank in range(P):
+        qpos = oracle.local_query_positions(T, P, rank, zigzag)
+        seed = 9900 + 10 * rank + int(zigzag)
+        q = rnd((B, T // P, H, d), seed, torch.bfloat16)
+        k = rnd((B, T, H, d), seed + 1, torch.bfloat16)
+        v = rnd((B, T, H, d), seed + 2, torch.bfloat16)
+        note(f"ring share, uneven padding: zigzag={zigzag} rank={rank}")
+        out, lse = bosa.attn_ring_fwd(q.to(DEV), k.to(DEV), v.to(DEV), P=P, rank=rank, zigzag=zigzag, causal=True,
+                                      kpm=kpm.to(DEV), rope_base=10000.0)
+        torch.cuda.synchronize()
+        ro, rl = oracle.sdpa(np64(q), np64(k), np64(v), qpos, np.arange(T), causal=True, kpm=kpm.numpy(),
+                             rope_base=10000.0, dtype="bf16")
+        compare(out.cpu(), lse.cpu(), ro, rl, "bf16", f"rank{rank}")
