@@ -59,8 +59,13 @@ def compare(out, lse, ref_out, ref_lse, dtype: str, what: str = ""):
     if dtype == "f32" and fin.any():
         # a float32 lse is itself rounded to half a unit in the last place of
         # its magnitude; where distance penalties make |lse| large (ALiBi),
-        # 1e-5 falls below a few such units, so 4 of them are allowed
-        tol_l = max(tol_l, 4.0 * float(np.spacing(np.float32(np.abs(ref_lse[fin]).max()))))
+        # 1e-5 falls below a few such units, so 4 of them are allowed.  The
+        # scores behind it are float32 numbers of that magnitude too: half a
+        # unit of |score| in the exponent is a relative error of P, so out
+        # (a P-weighted mean of unit-variance v rows) gets the same 4 units.
+        unit = float(np.spacing(np.float32(np.abs(ref_lse[fin]).max())))
+        tol_l = max(tol_l, 4.0 * unit)
+        tol_o = max(tol_o, 4.0 * unit)
     eo = float(np.abs(o - ref_out).max()) if o.size else 0.0
     el = float(np.abs(l[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
     row_err = np.sqrt(((o - ref_out) ** 2).sum(-1)) + 1e-300
