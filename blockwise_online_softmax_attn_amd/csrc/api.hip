@@ -41,6 +41,7 @@ int hip_fail(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kTile = 64;   // key tile of the bf16 kernel (live-tile list granularity)
+constexpr int kChainRows = 256;   // query rows per workgroup of the chained bf16 kernel
 
 // Stream-ordered scratch: allocated on the call's stream, released on it after
 // the last kernel that uses it, so nothing outlives the call.
@@ -651,17 +652,25 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
     // bf16 without a window or ALiBi: a query block's sub-calls run in plan
     // order, several to a launch of the chained kernel, with the same
     // per-block partials and merges as one launch per sub-call.  A chain ends
-    // after kMaxChain blocks or after a block that causal order cuts through
-    // the query block (its workgroups then finish at different times, and a
-    // new launch lines them up again, so the workgroups of one head keep
-    // reading the same key tiles at about the same time).
+    // after kMaxChain blocks, and after a block that causal order cuts through
+    // the query block when the launch runs its workgroups in more than one
+    // round per CU: those workgroups finish that block at different times,
+    // and a new launch lines them up again, so the workgroups of one head keep
+    // reading the same key tiles at about the same time.  With a single round
+    // (the 8K share) there is no later round to fall out of step, and going
+    // on in the same launch was 4.7% faster there.
     const bool chain = dtype == ATTN_BF16 && wl < 0 && wr < 0 && !(var && var->alibi_slopes);
     if (chain) {
         for (int i = 0; i < n_live; ++i)
             if (kpm_list_bytes(calls[i]))
                 if (int rc = build_tile_list(calls[i], (int*)(wp + lst_off[i]), s)) return rc;
+        int dev = 0, n_cu = 0;
+        if ((err = hipGetDevice(&dev)) != hipSuccess ||
+            (err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+            return hip_fail(err, "device query");
         auto cut = [&](int i) {
-            return causal && plan[i].kv_pos0 + plan[i].kv_rows - 1 > plan[i].q_pos0;
+            const long long wgs = (long long)B * H * ((plan[i].q_rows + kChainRows - 1) / kChainRows);
+            return causal && wgs > n_cu && plan[i].kv_pos0 + plan[i].kv_rows - 1 > plan[i].q_pos0;
         };
         for (int ph = 0; ph < 2; ++ph) {
             std::vector<int> idx;
