@@ -642,38 +642,40 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 
 // dst = (accumulate ? dst : 0) + R(-pos) src per coordinate pair, pos from
 // the table row of the token (tab[t][pair] = cos, sin of +pos); tab == null:
-// no rotation.  One thread per pair.
+// no rotation.  One workgroup per token row (b, t), whose H * d values it
+// walks four at a time (two pairs per thread step); d is 64 or 128.
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restrict__ src, void* __restrict__ dst,
-                                                           const float2* __restrict__ tab, int B, int T, int H, int d,
+                                                           const float2* __restrict__ tab, int T, int H, int d,
                                                            long long src_bstride, long long dst_bstride, int accumulate) {
-    const long long pid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int b = (int)(blockIdx.x / (unsigned)T), t = (int)(blockIdx.x % (unsigned)T);
     const int half = d / 2;
-    const long long npairs = (long long)B * T * H * half;
-    if (pid >= npairs) return;
-    const int pr = (int)(pid % half);
-    long long r = pid / half;
-    const int h = (int)(r % H);
-    r /= H;
-    const int t = (int)(r % T), b = (int)(r / T);
-    const long long rowoff = (long long)t * H * d + (long long)h * d + 2 * pr;
-    const float2 x = *(const float2*)(src + b * src_bstride + rowoff);
-    float2 y = x;
-    if (tab) {
-        const float2 cs = tab[(long long)t * half + pr];
-        y = rot_pair(x.x, x.y, cs.x, -cs.y);
-    }
-    if (BF16) {
-        uint32_t* o = (uint32_t*)((uint16_t*)dst + b * dst_bstride + rowoff);
-        *o = pack_bf16x2(y.x, y.y);
-    } else {
-        float2* o = (float2*)((float*)dst + b * dst_bstride + rowoff);
-        if (accumulate) {
-            const float2 a = *o;
-            y.x += a.x;
-            y.y += a.y;
+    const int n4 = H * d / 4;
+    const float* sp = src + b * src_bstride + (long long)t * H * d;
+    const long long doff = b * dst_bstride + (long long)t * H * d;
+    const float4* tr = tab ? (const float4*)(tab + (long long)t * half) : nullptr;
+    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+        const float4 x = ((const float4*)sp)[i];
+        float2 y0 = make_float2(x.x, x.y), y1 = make_float2(x.z, x.w);
+        if (tr) {
+            const float4 cs = tr[(i & (d / 4 - 1))];   // pairs 2j, 2j+1 of the head's d/2
+            y0 = rot_pair(x.x, x.y, cs.x, -cs.y);
+            y1 = rot_pair(x.z, x.w, cs.z, -cs.w);
         }
-        *o = y;
+        if (BF16) {
+            ((uint2*)((uint16_t*)dst + doff))[i] = make_uint2(pack_bf16x2(y0.x, y0.y), pack_bf16x2(y1.x, y1.y));
+        } else {
+            float4* o = (float4*)((float*)dst + doff) + i;
+            float4 r = make_float4(y0.x, y0.y, y1.x, y1.y);
+            if (accumulate) {
+                const float4 a = *o;
+                r.x += a.x;
+                r.y += a.y;
+                r.z += a.z;
+                r.w += a.w;
+            }
+            *o = r;
+        }
     }
 }
 
@@ -737,14 +739,14 @@ hipError_t launch_bwd_delta(const void* dout, const void* out, const float* lse,
 hipError_t launch_bwd_finalize(const float* src, void* dst, const float2* tab, int B, int T, int H, int d,
                                long long src_bstride, long long dst_bstride, int dst_bf16, int accumulate,
                                hipStream_t s) {
-    const long long n = (long long)B * T * H * (d / 2);
-    if (n == 0) return hipSuccess;
+    const long long rows = (long long)B * T;
+    if (rows == 0 || H == 0) return hipSuccess;
     if (dst_bf16)
-        hipLaunchKernelGGL(bwd_finalize_kernel<true>, dim3(grid_for(n, 256)), dim3(256), 0, s, src, dst, tab, B, T, H,
-                           d, src_bstride, dst_bstride, 0);
+        hipLaunchKernelGGL(bwd_finalize_kernel<true>, dim3((unsigned)rows), dim3(256), 0, s, src, dst, tab, T, H, d,
+                           src_bstride, dst_bstride, 0);
     else
-        hipLaunchKernelGGL(bwd_finalize_kernel<false>, dim3(grid_for(n, 256)), dim3(256), 0, s, src, dst, tab, B, T,
-                           H, d, src_bstride, dst_bstride, accumulate);
+        hipLaunchKernelGGL(bwd_finalize_kernel<false>, dim3((unsigned)rows), dim3(256), 0, s, src, dst, tab, T, H, d,
+                           src_bstride, dst_bstride, accumulate);
     return hipGetLastError();
 }
 
