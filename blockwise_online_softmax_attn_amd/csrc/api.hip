@@ -4,8 +4,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -95,6 +97,19 @@ void drop_dead_subcalls(std::vector<attn_ring_call>& plan, int causal, long long
         live.push_back(e);
     }
     plan.swap(live);
+}
+
+// [0, T) minus the given row ranges, as sorted disjoint ranges.
+std::vector<std::pair<int, int>> complement_rows(std::vector<std::pair<int, int>> used, int T) {
+    std::sort(used.begin(), used.end());
+    std::vector<std::pair<int, int>> out;
+    int at = 0;
+    for (const auto& r : used) {
+        if (r.first > at) out.push_back({at, r.first});
+        at = std::max(at, r.first + r.second);
+    }
+    if (at < T) out.push_back({at, T});
+    return out;
 }
 
 struct Call {
@@ -222,11 +237,14 @@ struct BwdCall {
     long long q_off, kv_off;
     int causal;
     const uint8_t* kpm; const uint8_t* amask;
-    unsigned flags;
+    unsigned flags;            // ATTN_ACCUMULATE here: every gradient adds to what it holds
     long long q_bstride, kv_bstride, kpm_bstride, lse_bstride;
     int lse_hstride, amask_stride;
     long long win_left = -1, win_right = -1;
     const float* alibi = nullptr;
+    // ring sub-calls: the first to touch a gradient's rows writes them (the
+    // flags without ATTN_ACCUMULATE), later ones add
+    int write_dq = 0, write_dkdv = 0;
 };
 
 // Enqueue the dQ and dK/dV kernels of one sub-call; `list` is scratch of
@@ -256,7 +274,9 @@ int enqueue_bwd(const BwdCall& c, int* list, hipStream_t s) {
         p.kpm_list = list;
         p.kpm_list_stride = ntk + 2;
     }
+    p.flags = c.write_dq ? (c.flags & ~(unsigned)ATTN_ACCUMULATE) : c.flags;
     if (int rc = timed_launch([&] { return launch_bwd_dq(p, c.d, s); }, "backward dQ kernel launch", s)) return rc;
+    p.flags = c.write_dkdv ? (c.flags & ~(unsigned)ATTN_ACCUMULATE) : c.flags;
     return timed_launch([&] { return launch_bwd_dkdv(p, c.d, s); }, "backward dK/dV kernel launch", s);
 }
 
@@ -916,10 +936,45 @@ int attn_ring_bwd_ex(const void* q, const void* k, const void* v, const void* ou
     float* gk = (float*)wp; wp += align_up(nk * 4);
     float* gv = (float*)wp;
 
+    // The first sub-call that touches a query block's dq, or a key block's
+    // dk and dv, writes them; later ones add.  Key blocks of the plan are
+    // equal or disjoint row ranges; rows no sub-call touches are zeroed.
+    std::vector<int> write_dq(n_live, 0), write_kv(n_live, 0);
+    std::vector<std::pair<int, int>> kv_seen;   // (first row, rows)
+    bool q_seen[2] = {false, false}, disjoint = true;
+    for (int i = 0; i < n_live; ++i) {
+        const int ph = plan[i].q_row0 == 0 ? 0 : 1;
+        write_dq[i] = !q_seen[ph];
+        q_seen[ph] = true;
+        const int r0 = (int)plan[i].kv_pos0, nr = plan[i].kv_rows;
+        bool same = false;
+        for (const auto& r : kv_seen) {
+            if (r.first == r0 && r.second == nr) same = true;
+            else if (r0 < r.first + r.second && r.first < r0 + nr) disjoint = false;
+        }
+        write_kv[i] = !same;
+        if (!same) kv_seen.push_back({r0, nr});
+    }
     e = launch_bwd_delta(dout, out, lse, ld2, B, H, Tl, d, (long long)Tl * rs, (int)rs, (long long)H * Tl, Tl, s);
-    if (e == hipSuccess) e = launch_zero_f32(gq, (long long)nq, s);
-    if (e == hipSuccess) e = launch_zero_f32(gk, (long long)nk, s);
-    if (e == hipSuccess) e = launch_zero_f32(gv, (long long)nk, s);
+    if (!disjoint) {   // not the plan's layout: zero everything, every sub-call adds
+        std::fill(write_dq.begin(), write_dq.end(), 0);
+        std::fill(write_kv.begin(), write_kv.end(), 0);
+        if (e == hipSuccess) e = launch_zero_f32(gq, (long long)nq, s);
+        if (e == hipSuccess) e = launch_zero_f32(gk, (long long)nk, s);
+        if (e == hipSuccess) e = launch_zero_f32(gv, (long long)nk, s);
+    } else {
+        const int parts = zigzag ? 2 : 1, c = Tl / parts;
+        for (int ph = 0; ph < parts && e == hipSuccess; ++ph)
+            if (!q_seen[ph])
+                for (int b = 0; b < B && e == hipSuccess; ++b)
+                    e = launch_zero_f32(gq + ((size_t)b * Tl + (size_t)ph * c) * rs, (long long)c * rs, s);
+        for (const auto& r : complement_rows(kv_seen, T))
+            for (int b = 0; b < B && e == hipSuccess; ++b) {
+                const size_t off = ((size_t)b * T + r.first) * rs;
+                e = launch_zero_f32(gk + off, (long long)(r.second - r.first) * rs, s);
+                if (e == hipSuccess) e = launch_zero_f32(gv + off, (long long)(r.second - r.first) * rs, s);
+            }
+    }
     if (e != hipSuccess) return hip_fail(e, "setup launch");
     if (rope) {
         const double lb = std::log(rope_base);
@@ -954,6 +1009,8 @@ int attn_ring_bwd_ex(const void* q, const void* k, const void* v, const void* ou
         c.win_right = wr;
         c.alibi = var ? var->alibi_slopes : nullptr;
         c.flags = (flags & ATTN_NO_TILE_SKIP) | ATTN_ACCUMULATE;
+        c.write_dq = write_dq[i];
+        c.write_dkdv = write_kv[i];
         c.q_bstride = (long long)Tl * rs; c.kv_bstride = (long long)T * rs; c.kpm_bstride = T;
         c.lse_bstride = (long long)H * Tl; c.lse_hstride = Tl; c.amask_stride = 0;
         const size_t lb = kpm_list_bytes(c.kpm, dtype, flags, B, c.Tkv);
