@@ -226,3 +226,41 @@ def test_random_ring_share_bitwise_against_its_subcalls(case):
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), o16.view(torch.int16)), "out differs from the sub-calls'"
     assert torch.equal(lse, ls), "lse differs from the sub-calls'"
+
+
+N_RING_BWD = 20
+
+
+@pytest.mark.parametrize("case", range(N_RING_BWD))
+def test_random_ring_backward(case):
+    """attn_ring_bwd over random P (2, 3, 4, 8), layouts, head counts, key
+    padding and ranks (the first sub-call to touch a block's gradients writes
+    them, later ones add, untouched rows are zeroed) against the backward
+    oracle over the local rows and every key."""
+    rng = np.random.default_rng(80000 + case)
+    P = int(rng.choice([2, 3, 4, 8]))
+    zigzag = bool(rng.random() < 0.5)
+    c = int(rng.integers(8, 200))
+    T = (2 * P if zigzag else P) * c
+    B, H = int(rng.integers(1, 3)), int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    causal = bool(rng.random() < 0.7)
+    rank = int(rng.integers(0, P))
+    rope = float(rng.choice([0.0, 10000.0]))
+    kp = float(rng.choice([0.0, 0.0, 0.3]))
+    note(f"random ring backward {case}: P={P} zigzag={zigzag} T={T} B={B} H={H} d={d} causal={causal} rank={rank} "
+         f"rope={rope} kpm={kp}")
+    bf = torch.bfloat16
+    q, dout = _draw((B, T // P, H, d), 81000 + case, bf), _draw((B, T // P, H, d), 84000 + case, bf)
+    k, v = _draw((B, T, H, d), 82000 + case, bf), _draw((B, T, H, d), 83000 + case, bf)
+    kpm = _mask((B, T), 85000 + case, kp)
+    qd, kd, vd, od = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV)
+    md = None if kpm is None else kpm.to(DEV)
+    out, lse = bosa.attn_ring_fwd(qd, kd, vd, P=P, rank=rank, zigzag=zigzag, causal=causal, kpm=md, rope_base=rope)
+    grads = bosa.attn_ring_bwd(qd, kd, vd, out, od, lse, P=P, rank=rank, zigzag=zigzag, causal=causal, kpm=md,
+                               rope_base=rope)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa_backward(np64(q), np64(k), np64(v), np64(dout), oracle.local_query_positions(T, P, rank, zigzag),
+                               np.arange(T), causal=causal, kpm=None if kpm is None else kpm.numpy(), rope_base=rope,
+                               dtype="bf16")
+    compare_grads([g.cpu() for g in grads], ref, f"case {case}")
