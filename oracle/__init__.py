@@ -23,15 +23,14 @@ Every function states the passage of the source pages it follows:
 
 Pins: every function here is checked by ``tests/test_oracle_pins.py`` against
 facts the pages or mathematics fix (printed worked example, closed forms,
-invariants, library special cases, brute force).  One point is recorded as
-"parity unpinned": the RoPE frequency schedule theta_t = base^(-2t/d) is
-pinned only by its closed form and invariants, never against an external RoPE
-implementation (none is available offline).
+invariants, library special cases, brute force).  The RoPE pairing and
+frequency schedule (adjacent pairs, theta_t = base^(-2t/d), a reading of
+"Transformers and Attention" #4) are pinned against the interleaved rotary
+routine of the GPT-J model in the installed ``transformers`` package.
 """
 from .reference import (  # noqa: F401
     round_to_dtype,
     rope_rotate,
-    rope_rotate_f32,
     rope_frequencies,
     sdpa,
     sdpa_backward,

@@ -58,7 +58,8 @@ def rope_frequencies(d: int, base: float) -> np.ndarray:
     """theta_t = base^(-2t/d) for pair t = 0 .. d/2-1 (RoFormer's schedule;
     the digest entry #4 of "Transformers and Attention" only states that an
     even-dimensional vector is split into coordinate pairs, each rotated by a
-    positional angle).  Parity against an external RoPE: unpinned."""
+    positional angle).  Pinned against the interleaved rotary embedding of
+    the GPT-J model in the transformers package (base 10000)."""
     t = np.arange(d // 2, dtype=np.float64)
     return np.power(float(base), -2.0 * t / d)
 
@@ -84,49 +85,19 @@ def rope_rotate(x, pos, base: float) -> np.ndarray:
     return y
 
 
-def rope_rotate_f32(x, pos, base: float) -> np.ndarray:
-    """The rotation evaluated in float32, the precision in which the rounded
-    operands q' and k' are decided.
-
-    The pages do not say in what precision a rotated vector is formed before
-    it is stored in the input dtype.  Since that rounding is a quantisation
-    decision, it is taken in the kernels' precision: cos and sin of the
-    float64 angle pos * theta_t rounded to float32, and each output formed as
-    one fused multiply-add over a float32 product,
-        y0 = fma(x0, c, -fl32(x1 s)),   y1 = fma(x0, s, fl32(x1 c)).
-    The fused multiply-add is evaluated in float64 (x0 c is exact there) and
-    rounded to float32; this differs from a single rounding only when the
-    float64 value lies exactly on a float32 rounding midpoint.
-    Input values must be float32-representable.  Returns float64 arrays
-    holding float32 values.
-    """
-    x = np.asarray(x, dtype=np.float64)
-    d = x.shape[-1]
-    if d % 2:
-        raise ValueError("RoPE needs an even head dimension")
-    pos = np.asarray(pos, dtype=np.float64)
-    ang = pos[:, None] * rope_frequencies(d, base)[None, :]
-    c = np.cos(ang).astype(np.float32).astype(np.float64)[:, None, :]
-    s = np.sin(ang).astype(np.float32).astype(np.float64)[:, None, :]
-    x0 = x[..., 0::2]
-    x1 = x[..., 1::2]
-    f32 = lambda a: a.astype(np.float32).astype(np.float64)  # noqa: E731
-    y = np.empty_like(x)
-    y[..., 0::2] = f32(x0 * c - f32(x1 * s))
-    y[..., 1::2] = f32(x0 * s + f32(x1 * c))
-    return y
-
-
 # --------------------------------------------------------------------------
 # scaled dot-product attention, plain definition
 # --------------------------------------------------------------------------
 def _rotated(x, pos, base: float, dtype: str) -> np.ndarray:
-    """Rotated operand as the attention sees it: the float32 rotation rounded
-    to the input dtype, or (dtype "f64") the exact float64 rotation with no
-    rounding at all, for derivative checks."""
+    """Rotated operand as the attention sees it: the float64 rotation
+    (``rope_rotate``) rounded once to the input dtype, as if the rotation had
+    been applied to the stored tensors ("Transformers and Attention" #4:
+    coordinate pairs turned by a positional angle; #31: a low-precision
+    position collapses nearby positions, so the angle is formed in float64).
+    dtype "f64" keeps the exact rotation, for derivative checks."""
     if dtype == "f64":
         return rope_rotate(x, pos, base)
-    return round_to_dtype(rope_rotate_f32(x, pos, base), dtype)
+    return round_to_dtype(rope_rotate(x, pos, base), dtype)
 
 
 def _allowed(B, Tq, Tkv, q_pos, kv_pos, causal, kpm, attn_mask, window=(-1, -1)) -> np.ndarray:
@@ -178,9 +149,9 @@ def sdpa(q, k, v, q_pos, kv_pos, *, causal: bool = False, kpm=None, attn_mask=No
     "CP: Split Long Contexts Across GPUs", "Why attention needs information
     from other GPUs": t3 attends to t0..t3).
 
-    With rope_base > 0, q and k are first rotated (``rope_rotate_f32``) and
-    rounded to ``dtype``, as if the rotation had been applied to the stored
-    tensors.  Scores are scaled by 1/sqrt(d) (#15, #22).  Row softmax is the two-pass
+    With rope_base > 0, q and k are first rotated in float64 and rounded
+    once to ``dtype`` (``_rotated``), as if the rotation had been applied to
+    the stored tensors.  Scores are scaled by 1/sqrt(d) (#15, #22).  Row softmax is the two-pass
     safe form (brunomaga.github.io post, "Improving numerical stability"):
     m = max of the allowed scores, e = exp(s - m) on allowed entries and
     exactly 0 elsewhere, l = sum e, out = (e / l) v, lse = m + ln l (the
@@ -323,8 +294,8 @@ def kv_append(k_cache, v_cache, cache_len, k_new, v_new, *, rope_base: float = 0
 
     k_cache, v_cache: (B, Tcap, H, d); cache_len[B]: filled slots (slot j
     holds the token at position j); k_new, v_new: (B, H, d).  The new key is
-    stored rotated to its position cache_len[b] (``_rotated``: the float32
-    rotation rounded to ``dtype``), the value as given; cache_len[b] grows by
+    stored rotated to its position cache_len[b] (``_rotated``: the float64
+    rotation rounded once to ``dtype``), the value as given; cache_len[b] grows by
     one.  A full cache (cache_len[b] == Tcap) is left unchanged.  Returns new
     arrays (k_cache, v_cache, cache_len).
     """

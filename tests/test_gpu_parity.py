@@ -225,14 +225,15 @@ def test_fused_rope_matches_rope_apply_bitwise(dtype):
     bosa.rope_apply(kd, torch.arange(kv_off, kv_off + Tkv, device=DEV), 10000.0)
     o2, l2 = gpu_fwd(qd.cpu(), kd.cpu(), v, q_off=q_off, kv_off=kv_off, causal=True)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    # rope_apply against the oracle's float32 rotation rounded to the dtype: the
-    # same bits except where the two float64 sin/cos libraries land on opposite
-    # sides of a float32 rounding midpoint (then one ulp apart)
-    ref = oracle.round_to_dtype(oracle.rope_rotate_f32(np64(q), q_off + np.arange(Tq), 10000.0),
+    # rope_apply against the oracle's rotation (float64, rounded once to the
+    # dtype): the same bits except where the two float64 angle evaluations land
+    # on opposite sides of a rounding midpoint (then one unit apart)
+    ref = oracle.round_to_dtype(oracle.rope_rotate(np64(q), q_off + np.arange(Tq), 10000.0),
                                 "f32" if dtype == torch.float32 else "bf16")
     got = np64(qd.cpu())
     diff = got != ref
-    assert diff.mean() < 1e-4
+    note(f"rope_apply {dtype}: {int(diff.sum())} of {diff.size} elements differ from the oracle")
+    assert diff.mean() < 1e-5
     ulp = 2.0 ** -23 if dtype == torch.float32 else 2.0 ** -7
     assert np.all(np.abs(got - ref)[diff] <= np.abs(ref[diff]) * ulp)
 

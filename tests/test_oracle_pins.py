@@ -399,19 +399,61 @@ def workloads_bf16(shape, seed):
     return torch.from_numpy(_rand(shape, seed)).to(torch.float32).to(torch.bfloat16).double().numpy()
 
 
-def test_float32_rotation_is_the_rotation_to_float32_accuracy():
-    """The float32 evaluation agrees with the float64 rotation within its
-    error bound (a few float32 ulps of the pair norm), is the identity at
-    position 0, and keeps the turning sense.  Catches a sign, pairing or
-    operand-order mistake in the float32 path."""
+def test_rope_matches_gptj_interleaved_rotary():
+    """The pairing (adjacent coordinates 2t, 2t+1) and the frequency schedule
+    (theta_t = base^(-2t/d)), a reading of "Transformers and Attention" #4,
+    agree with an independent implementation: the interleaved rotary
+    embedding of the GPT-J model in the installed transformers package, which
+    forms its angles in float32 (hence the tolerance: about 2^-24 of an angle
+    of at most 255 rad).  A rotate-half pairing, a wrong exponent or a
+    reversed turning sense are off by O(1)."""
+    gptj = pytest.importorskip("transformers.models.gptj.modeling_gptj")
+    for d in (64, 128):
+        T, H = 256, 3
+        x = workloads_bf16((2, T, H, d), 71 + d)
+        sincos = gptj.create_sinusoidal_positions(T, d)             # (T, d): sin | cos, float32
+        sin, cos = torch.split(sincos.double(), d // 2, dim=-1)
+        pos = torch.arange(T)
+        ref = gptj.apply_rotary_pos_emb(torch.from_numpy(x), sin[pos][None].expand(2, T, d // 2),
+                                        cos[pos][None].expand(2, T, d // 2)).numpy()
+        got = oracle.rope_rotate(x, np.arange(T), 10000.0)
+        norm = np.abs(x).max()
+        assert np.abs(got - ref).max() <= 4e-5 * norm
+
+
+def test_rope_frequency_schedule_structure():
+    """The turning rates read back from rotated unit vectors (atan2, not the
+    schedule's formula) start at 1 rad per position, fall geometrically (a
+    constant ratio between neighbours) and pair up as theta_t *
+    theta_(d/2-t) = 1/base; together these fix theta_t = base^(-2t/d)."""
+    for d, base in [(64, 10000.0), (128, 10000.0), (128, 500000.0)]:
+        x = np.zeros((1, 1, 1, d))
+        x[..., 0::2] = 1.0
+        y = oracle.rope_rotate(x, np.array([1]), base)[0, 0, 0]
+        th = np.arctan2(y[1::2], y[0::2])                      # all rates are below pi
+        assert th[0] == pytest.approx(1.0, abs=1e-15)
+        ratios = th[1:] / th[:-1]
+        np.testing.assert_allclose(ratios, ratios[0], rtol=1e-12)
+        for t in range(1, d // 2):
+            assert th[t] * th[d // 2 - t] == pytest.approx(1.0 / base, rel=1e-12)
+
+
+def test_rotated_operand_is_the_float64_rotation_rounded_once():
+    """The rotated operand the attention definition uses is the float64
+    rotation rounded once to the input dtype (reading R1): identity at
+    position 0, bf16-representable values, and each within half a bf16 unit
+    of the exact rotation (checked against the unit of the value itself)."""
+    from oracle import reference as ref
     d, base = 128, 10000.0
     x = workloads_bf16((1, 50, 3, d), 70)
     pos = np.concatenate([[0, 1, 2], np.arange(131000, 131047)])
-    a = oracle.rope_rotate(x, pos, base)
-    b = oracle.rope_rotate_f32(x, pos, base)
-    norm = np.sqrt(x[..., 0::2] ** 2 + x[..., 1::2] ** 2).repeat(2, axis=-1)
-    assert np.all(np.abs(a - b) <= norm * 2 ** -21 + 1e-30)
-    np.testing.assert_array_equal(b[:, 0], x[:, 0])
-    assert np.all(b == b.astype(np.float32).astype(np.float64))
-    y = oracle.rope_rotate_f32(np.tile(np.array([1.0, 0.0]), (1, 1, 1, d // 2)), np.array([1]), base)[0, 0, 0]
-    assert y[1] == np.float32(np.sin(1.0))           # pair 0 turns by +1 rad
+    exact = oracle.rope_rotate(x, pos, base)
+    r = ref._rotated(x, pos, base, "bf16")
+    np.testing.assert_array_equal(r[:, 0], x[:, 0])
+    as_bf16 = torch.from_numpy(r).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(r, as_bf16)
+    nz = exact != 0
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(exact[nz]))) - 7)
+    assert np.all(np.abs(r[nz] - exact[nz]) <= ulp / 2)
+    r32 = ref._rotated(x, pos, base, "f32")
+    np.testing.assert_array_equal(r32, exact.astype(np.float32).astype(np.float64))
