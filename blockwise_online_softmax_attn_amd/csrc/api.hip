@@ -122,7 +122,7 @@ struct Call {
     // strides (elements)
     long long q_bstride, kv_bstride, o_bstride, kpm_bstride, lse_bstride;
     int lse_hstride, amask_stride;
-    const float2* rope_q; const float2* rope_k;
+    const double2* rope_q; const double2* rope_k;
     long long win_left = -1, win_right = -1;
     const float* alibi = nullptr;
 };
@@ -386,8 +386,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
     // the attention kernel reads (the same float32 rotation it would apply);
     // float32: the kernel rotates them on the fly.
     const bool krot = rope && dtype == ATTN_BF16;
-    const size_t tab_q = rope ? align_up((size_t)Tq * (d / 2) * sizeof(float2)) : 0;
-    const size_t tab_k = rope ? align_up((size_t)Tkv * (d / 2) * sizeof(float2)) : 0;
+    const size_t tab_q = rope ? align_up((size_t)Tq * (d / 2) * sizeof(double2)) : 0;
+    const size_t tab_k = rope ? align_up((size_t)Tkv * (d / 2) * sizeof(double2)) : 0;
     const size_t kbuf = krot ? align_up((size_t)B * Tkv * H * d * 2) : 0;
     const size_t qbuf = krot ? align_up((size_t)B * Tq * H * d * 2) : 0;
     const size_t lst = kpm_list_bytes(c);
@@ -397,10 +397,10 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
     char* wp = (char*)ws.ptr;
     if (rope) {
         const double lb = std::log(rope_base);
-        c.rope_q = (const float2*)wp;
-        c.rope_k = (const float2*)(wp + tab_q);
-        e = launch_rope_table((float2*)wp, q_off, Tq, d, lb, s);
-        if (e == hipSuccess) e = launch_rope_table((float2*)(wp + tab_q), kv_off, Tkv, d, lb, s);
+        c.rope_q = (const double2*)wp;
+        c.rope_k = (const double2*)(wp + tab_q);
+        e = launch_rope_table((double2*)wp, q_off, Tq, d, lb, s);
+        if (e == hipSuccess) e = launch_rope_table((double2*)(wp + tab_q), kv_off, Tkv, d, lb, s);
         if (e != hipSuccess) return hip_fail(e, "rotary table launch");
         if (krot) {
             void* kr = wp + tab_q + tab_k;
@@ -601,7 +601,7 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
     // values the kernel's own rotation gives.  The local queries' positions
     // are positions of the keys, so one table over [0, T) serves both.
     const bool krot = rope && dtype == ATTN_BF16;
-    const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(float2)) : 0;
+    const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(double2)) : 0;
     const size_t kbuf = krot ? align_up((size_t)B * T * H * d * 2) : 0;
     const size_t qbuf = krot ? align_up((size_t)B * Tl * H * d * 2) : 0;
     std::vector<size_t> lst_off(n_live, 0);
@@ -637,15 +637,25 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
         lst_off[i] = total;
         total += kpm_list_bytes(c);
     }
+    const bool chain = dtype == ATTN_BF16 && wl < 0 && wr < 0 && !(var && var->alibi_slopes);
+    // the chained executor's cut rule needs the CU count: queried before anything is enqueued
+    int n_cu = 0;
+    hipError_t err = hipSuccess;
+    if (chain) {
+        int dev = 0;
+        if ((err = hipGetDevice(&dev)) != hipSuccess ||
+            (err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+            return hip_fail(err, "device query");
+    }
     Scratch ws;
-    hipError_t err = ws.alloc(total, s);
+    err = ws.alloc(total, s);
     if (err != hipSuccess) return hip_fail(err, "scratch allocation");
     char* wp = (char*)ws.ptr;
-    const float2* tab = (const float2*)wp;
+    const double2* tab = (const double2*)wp;
     char* krb = wp + tab_k;
     char* qrb = krb + kbuf;
     if (rope) {
-        err = launch_rope_table((float2*)wp, 0, T, d, std::log(rope_base), s);
+        err = launch_rope_table((double2*)wp, 0, T, d, std::log(rope_base), s);
         if (err != hipSuccess) return hip_fail(err, "rotary table launch");
         if (krot) {
             // local rows [0, c) sit at rank * c, zigzag rows [c, 2c) at (2P - 1 - rank) * c
@@ -679,15 +689,10 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
     // reading the same key tiles at about the same time.  With a single round
     // (the 8K share) there is no later round to fall out of step, and going
     // on in the same launch was 4.7% faster there.
-    const bool chain = dtype == ATTN_BF16 && wl < 0 && wr < 0 && !(var && var->alibi_slopes);
     if (chain) {
         for (int i = 0; i < n_live; ++i)
             if (kpm_list_bytes(calls[i]))
                 if (int rc = build_tile_list(calls[i], (int*)(wp + lst_off[i]), s)) return rc;
-        int dev = 0, n_cu = 0;
-        if ((err = hipGetDevice(&dev)) != hipSuccess ||
-            (err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-            return hip_fail(err, "device query");
         auto cut = [&](int i) {
             const long long wgs = (long long)B * H * ((plan[i].q_rows + kChainRows - 1) / kChainRows);
             return causal && wgs > n_cu && plan[i].kv_pos0 + plan[i].kv_rows - 1 > plan[i].q_pos0;
@@ -803,8 +808,8 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
     // still be rotated back (dq, dk with RoPE) or cast (bf16 outputs)
     const bool dq_direct = f32 && !rope, dk_direct = dq_direct, dv_direct = dq_direct;
     const size_t ld_b = align_up((size_t)B * H * Tq * sizeof(float2));
-    const size_t tab_q = rope ? align_up((size_t)Tq * (d / 2) * sizeof(float2)) : 0;
-    const size_t tab_k = rope ? align_up((size_t)Tkv * (d / 2) * sizeof(float2)) : 0;
+    const size_t tab_q = rope ? align_up((size_t)Tq * (d / 2) * sizeof(double2)) : 0;
+    const size_t tab_k = rope ? align_up((size_t)Tkv * (d / 2) * sizeof(double2)) : 0;
     const size_t qr_b = rope ? align_up(nq * 2) : 0, kr_b = rope ? align_up(nk * 2) : 0;
     const size_t dq_b = dq_direct ? 0 : align_up(nq * 4), dk_b = dk_direct ? 0 : align_up(nk * 4);
     const size_t dv_b = dv_direct ? 0 : align_up(nk * 4);
@@ -815,9 +820,9 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
     char* wp = (char*)ws.ptr;
     float2* ld2 = (float2*)wp;
     wp += ld_b;
-    float2* tq = (float2*)wp;
+    double2* tq = (double2*)wp;
     wp += tab_q;
-    float2* tk = (float2*)wp;
+    double2* tk = (double2*)wp;
     wp += tab_k;
     void* qr = wp;
     wp += qr_b;
@@ -912,8 +917,8 @@ int attn_ring_bwd_ex(const void* q, const void* k, const void* v, const void* ou
     const long long rs = (long long)H * d;
     const size_t nq = (size_t)B * Tl * rs, nk = (size_t)B * T * rs;
     const size_t ld_b = align_up((size_t)B * H * Tl * sizeof(float2));
-    const size_t tab_q = rope ? align_up((size_t)Tl * (d / 2) * sizeof(float2)) : 0;
-    const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(float2)) : 0;
+    const size_t tab_q = rope ? align_up((size_t)Tl * (d / 2) * sizeof(double2)) : 0;
+    const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(double2)) : 0;
     const size_t qr_b = rope ? align_up(nq * 2) : 0, kr_b = rope ? align_up(nk * 2) : 0;
     const size_t g_b = align_up(nq * 4) + 2 * align_up(nk * 4);
     std::vector<size_t> lst_off(n_live, 0);
@@ -928,8 +933,8 @@ int attn_ring_bwd_ex(const void* q, const void* k, const void* v, const void* ou
     char* base = (char*)ws.ptr;
     char* wp = base;
     float2* ld2 = (float2*)wp; wp += ld_b;
-    float2* tq = (float2*)wp; wp += tab_q;
-    float2* tk = (float2*)wp; wp += tab_k;
+    double2* tq = (double2*)wp; wp += tab_q;
+    double2* tk = (double2*)wp; wp += tab_k;
     char* qr = wp; wp += qr_b;
     char* kr = wp; wp += kr_b;
     float* gq = (float*)wp; wp += align_up(nq * 4);

@@ -641,40 +641,47 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // dst = (accumulate ? dst : 0) + R(-pos) src per coordinate pair, pos from
-// the table row of the token (tab[t][pair] = cos, sin of +pos); tab == null:
-// no rotation.  One workgroup per token row (b, t), whose H * d values it
-// walks four at a time (two pairs per thread step); d is 64 or 128.
+// the table row of the token (tab[t][pair] = float64 cos, sin of +pos); the
+// rotation is formed in float64 and rounded once to the output dtype;
+// tab == null: no rotation.  Workgroups walk the token rows (b, t) in a grid
+// stride; each row's H * d values go four at a time (two pairs per thread
+// step); d is 64 or 128.
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restrict__ src, void* __restrict__ dst,
-                                                           const float2* __restrict__ tab, int T, int H, int d,
-                                                           long long src_bstride, long long dst_bstride, int accumulate) {
-    const int b = (int)(blockIdx.x / (unsigned)T), t = (int)(blockIdx.x % (unsigned)T);
-    const int half = d / 2;
+                                                           const double2* __restrict__ tab, long long rows, int T,
+                                                           int H, int d, long long src_bstride, long long dst_bstride,
+                                                           int accumulate) {
     const int n4 = H * d / 4;
-    const float* sp = src + b * src_bstride + (long long)t * H * d;
-    const long long doff = b * dst_bstride + (long long)t * H * d;
-    const float4* tr = tab ? (const float4*)(tab + (long long)t * half) : nullptr;
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-        const float4 x = ((const float4*)sp)[i];
-        float2 y0 = make_float2(x.x, x.y), y1 = make_float2(x.z, x.w);
-        if (tr) {
-            const float4 cs = tr[(i & (d / 4 - 1))];   // pairs 2j, 2j+1 of the head's d/2
-            y0 = rot_pair(x.x, x.y, cs.x, -cs.y);
-            y1 = rot_pair(x.z, x.w, cs.z, -cs.w);
-        }
-        if (BF16) {
-            ((uint2*)((uint16_t*)dst + doff))[i] = make_uint2(pack_bf16x2(y0.x, y0.y), pack_bf16x2(y1.x, y1.y));
-        } else {
-            float4* o = (float4*)((float*)dst + doff) + i;
-            float4 r = make_float4(y0.x, y0.y, y1.x, y1.y);
-            if (accumulate) {
-                const float4 a = *o;
-                r.x += a.x;
-                r.y += a.y;
-                r.z += a.z;
-                r.w += a.w;
+    for (long long row = blockIdx.x; row < rows; row += gridDim.x) {
+        const long long b = row / T;
+        const int t = (int)(row - b * T);
+        const float* sp = src + b * src_bstride + (long long)t * H * d;
+        const long long doff = b * dst_bstride + (long long)t * H * d;
+        const double2* tr = tab ? tab + (long long)t * (d / 2) : nullptr;
+        for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+            const float4 x = ((const float4*)sp)[i];
+            double2 y0 = make_double2(x.x, x.y), y1 = make_double2(x.z, x.w);
+            if (tr) {
+                const double2 ca = tr[2 * (i & (d / 4 - 1))], cb = tr[2 * (i & (d / 4 - 1)) + 1];
+                y0 = rot64(x.x, x.y, ca.x, -ca.y);
+                y1 = rot64(x.z, x.w, cb.x, -cb.y);
             }
-            *o = r;
+            if (BF16) {
+                ((uint2*)((uint16_t*)dst + doff))[i] =
+                    make_uint2(bf16_bits_rn(y0.x) | (bf16_bits_rn(y0.y) << 16),
+                               bf16_bits_rn(y1.x) | (bf16_bits_rn(y1.y) << 16));
+            } else {
+                float4* o = (float4*)((float*)dst + doff) + i;
+                float4 r = make_float4((float)y0.x, (float)y0.y, (float)y1.x, (float)y1.y);
+                if (accumulate) {
+                    const float4 a = *o;
+                    r.x += a.x;
+                    r.y += a.y;
+                    r.z += a.z;
+                    r.w += a.w;
+                }
+                *o = r;
+            }
         }
     }
 }
@@ -736,16 +743,18 @@ hipError_t launch_bwd_delta(const void* dout, const void* out, const float* lse,
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_finalize(const float* src, void* dst, const float2* tab, int B, int T, int H, int d,
+hipError_t launch_bwd_finalize(const float* src, void* dst, const double2* tab, int B, int T, int H, int d,
                                long long src_bstride, long long dst_bstride, int dst_bf16, int accumulate,
                                hipStream_t s) {
     const long long rows = (long long)B * T;
     if (rows == 0 || H == 0) return hipSuccess;
+    // at most 2^20 workgroups (2^28 work-items, far below the 2^32 limit); more rows go round the grid stride
+    const unsigned grid = (unsigned)(rows < (1LL << 20) ? rows : (1LL << 20));
     if (dst_bf16)
-        hipLaunchKernelGGL(bwd_finalize_kernel<true>, dim3((unsigned)rows), dim3(256), 0, s, src, dst, tab, T, H, d,
+        hipLaunchKernelGGL(bwd_finalize_kernel<true>, dim3(grid), dim3(256), 0, s, src, dst, tab, rows, T, H, d,
                            src_bstride, dst_bstride, 0);
     else
-        hipLaunchKernelGGL(bwd_finalize_kernel<false>, dim3((unsigned)rows), dim3(256), 0, s, src, dst, tab, T, H, d,
+        hipLaunchKernelGGL(bwd_finalize_kernel<false>, dim3(grid), dim3(256), 0, s, src, dst, tab, rows, T, H, d,
                            src_bstride, dst_bstride, accumulate);
     return hipGetLastError();
 }

@@ -37,30 +37,47 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------- RoPE
-// Angle of pair t at position pos: pos * base^(-2t/d), evaluated in float64 and
-// returned as float32 cos/sin.  Position magnitudes up to 2^20 lose nothing
-// here (the product is exact to ~1e-10 rad), unlike a float32 angle.
-__device__ __forceinline__ float2 rope_cos_sin(long long pos, int t, int d, double log_base) {
-    double theta = exp(-(2.0 * (double)t / (double)d) * log_base);
-    double a = (double)pos * theta;
+// cos and sin of the angle of pair t at position pos, pos * base^(-2t/d),
+// all in float64: at positions up to 2^20 the angle keeps ~1e-10 rad.
+__device__ __forceinline__ double2 rope_cs64(long long pos, int t, int d, double log_base) {
+    const double theta = exp(-(2.0 * (double)t / (double)d) * log_base);
     double s, c;
-    sincos(a, &s, &c);
-    return make_float2((float)c, (float)s);
+    sincos((double)pos * theta, &s, &c);
+    return make_double2(c, s);
 }
 
-// Rotate one coordinate pair (x0, x1) by (c, s) in float32:
-// (x0 c - x1 s, x0 s + x1 c), with fixed fused-multiply-add placement.
-__device__ __forceinline__ float2 rot_pair(float x0, float x1, float c, float s) {
-    return make_float2(fmaf(x0, c, -(x1 * s)), fmaf(x0, s, x1 * c));
+// The rotated pair (x0 c - x1 s, x0 s + x1 c) in float64.  With x0, x1 from
+// bf16 or float32 inputs this is within two float64 units of the exact
+// rotation by (c, s), so one rounding to the input dtype afterwards gives the
+// correctly rounded rotated value except within ~1e-16 of a rounding midpoint.
+__device__ __forceinline__ double2 rot64(double x0, double x1, double c, double s) {
+    return make_double2(fma(x0, c, -(x1 * s)), fma(x0, s, x1 * c));
 }
-__device__ __forceinline__ uint32_t rot_pair_bf16(uint32_t u, float c, float s) {
-    float2 y = rot_pair(bf16_lo(u), bf16_hi(u), c, s);
-    return pack_bf16x2(y.x, y.y);
+
+// float64 -> bf16 bit pattern, rounded once to nearest even: the value is
+// first narrowed to float32 rounding to odd (truncate, then set the last bit
+// when anything was dropped), which keeps the information a final
+// round-to-nearest-even to 8 significant bits needs, then rounded to bf16.
+__host__ __device__ __forceinline__ uint32_t bf16_bits_rn(double y) {
+    const float f = (float)y;                       // nearest
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    const double back = (double)f;
+    if (back != y) {
+        if (__builtin_fabs(back) > __builtin_fabs(y)) u -= 1u;   // it rounded away from zero: step back toward zero
+        u |= 1u;                                                  // sticky
+    }
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
-// 8 bf16 values (4 pairs) with their table entries (c0,s0,c1,s1), (c2,s2,c3,s3).
-__device__ __forceinline__ uint4 rope8_bf16(uint4 x, float4 a, float4 b) {
-    return make_uint4(rot_pair_bf16(x.x, a.x, a.y), rot_pair_bf16(x.y, a.z, a.w),
-                      rot_pair_bf16(x.z, b.x, b.y), rot_pair_bf16(x.w, b.z, b.w));
+
+// A packed bf16 pair rotated by (c, s): float64 arithmetic, one rounding each.
+__device__ __forceinline__ uint32_t rot_pair_bf16(uint32_t u, double c, double s) {
+    const double2 y = rot64((double)bf16_lo(u), (double)bf16_hi(u), c, s);
+    return bf16_bits_rn(y.x) | (bf16_bits_rn(y.y) << 16);
+}
+// A float32 pair rotated by (c, s): float64 arithmetic, one rounding each.
+__device__ __forceinline__ float2 rot_pair_f32(float x0, float x1, double c, double s) {
+    const double2 y = rot64((double)x0, (double)x1, c, s);
+    return make_float2((float)y.x, (float)y.y);
 }
 
 // ---------------------------------------------------------------- merge
@@ -95,8 +112,8 @@ struct FwdParams {
     float* lse;
     const uint8_t* kpm;        // row b at kpm + b * kpm_bstride, indexed by local key
     const uint8_t* amask;      // [Tq][amask_stride]
-    const float2* rope_q;      // [Tq][d/2] (cos, sin) or null
-    const float2* rope_k;      // [Tkv][d/2] or null (float32 kernel; the bf16 kernel takes rotated keys)
+    const double2* rope_q;     // [Tq][d/2] (cos, sin) or null
+    const double2* rope_k;     // [Tkv][d/2] or null (float32 kernel; the bf16 kernel takes rotated keys)
     const int* kpm_list;       // per batch: [count, leading clean tiles, entries...] of live key tiles, or null
     long long q_bstride, kv_bstride, o_bstride, kpm_bstride, lse_bstride;
     int row_stride;            // H * d
@@ -216,7 +233,7 @@ hipError_t launch_decode_merge(const DecodeParams& p, int d, int out_bf16, hipSt
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, int* cache_len, int B,
                             int H, int Tcap, int d, double log_base, int is_bf16, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s);
-hipError_t launch_rope_table(float2* tab, long long pos0, int n, int d, double log_base, hipStream_t s);
+hipError_t launch_rope_table(double2* tab, long long pos0, int n, int d, double log_base, hipStream_t s);
 hipError_t launch_kpm_tiles(const uint8_t* kpm, long long kpm_bstride, int B, int Tkv, int tile,
                             int* list, int list_stride, hipStream_t s);
 hipError_t launch_merge(float* oa, float* la, const void* ob, const float* lb, int B, int H, int Tq, int d,
@@ -225,11 +242,11 @@ hipError_t launch_merge(float* oa, float* la, const void* ob, const float* lb, i
 hipError_t launch_cast(const float* src, void* dst, long long n, int to_bf16, hipStream_t s);
 hipError_t launch_rope_apply(void* x, const long long* pos, double log_base, int B, int T, int H, int d,
                              int is_bf16, hipStream_t s);
-hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
+hipError_t launch_rope_copy_bf16(const void* src, void* dst, const double2* tab, int B, int T, int H, int d,
                                  hipStream_t s);
 // The same with row t taking table row t + off0 for t < split, else
 // t - split + off1.
-hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
+hipError_t launch_rope_copy_bf16(const void* src, void* dst, const double2* tab, int B, int T, int H, int d,
                                  int split, long long off0, long long off1, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t s);
@@ -239,7 +256,7 @@ hipError_t launch_bwd_delta(const void* dout, const void* out, const float* lse,
                             hipStream_t s);
 // dst (float32 or bf16, optionally += ) = src rotated back by -pos (tab: cos/sin of +pos, or null for no
 // rotation); src, dst (B, T, H, d) with batch strides in elements.
-hipError_t launch_bwd_finalize(const float* src, void* dst, const float2* tab, int B, int T, int H, int d,
+hipError_t launch_bwd_finalize(const float* src, void* dst, const double2* tab, int B, int T, int H, int d,
                                long long src_bstride, long long dst_bstride, int dst_bf16, int accumulate,
                                hipStream_t s);
 hipError_t launch_zero_f32(float* x, long long n, hipStream_t s);

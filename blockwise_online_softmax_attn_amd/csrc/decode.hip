@@ -91,14 +91,16 @@ __global__ __launch_bounds__(DT) void decode_chunk_kernel(const DecodeParams p) 
         if (p.log_base > 0.0) {
 #pragma unroll
             for (int e = 0; e < EPL; e += 2) {
-                const float2 cs = rope_cos_sin(pos, (sl * EPL + e) / 2, D, p.log_base);
-                float2 y = rot_pair(q[e], q[e + 1], cs.x, cs.y);
+                const double2 cs = rope_cs64(pos, (sl * EPL + e) / 2, D, p.log_base);
+                const double2 y = rot64((double)q[e], (double)q[e + 1], cs.x, cs.y);
                 if (sizeof(T) == 2) {
-                    const uint32_t r = pack_bf16x2(y.x, y.y);
-                    y = make_float2(bf16_lo(r), bf16_hi(r));
+                    const uint32_t r = bf16_bits_rn(y.x) | (bf16_bits_rn(y.y) << 16);
+                    q[e] = bf16_lo(r);
+                    q[e + 1] = bf16_hi(r);
+                } else {
+                    q[e] = (float)y.x;
+                    q[e + 1] = (float)y.y;
                 }
-                q[e] = y.x;
-                q[e + 1] = y.y;
             }
         }
     }
@@ -241,25 +243,23 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const void* __restrict__
     const long long dst = ((long long)b * Tcap + L) * row;
     for (long long i = 2 * threadIdx.x; i < row; i += 2 * blockDim.x) {
         const int t = (int)(i % d) / 2;   // coordinate pair within the head
-        float x0, x1;
         if (sizeof(T) == 2) {
-            const uint32_t u = *(const uint32_t*)((const uint16_t*)k_new + src + i);
-            x0 = bf16_lo(u);
-            x1 = bf16_hi(u);
-        } else {
-            x0 = ((const float*)k_new)[src + i];
-            x1 = ((const float*)k_new)[src + i + 1];
-        }
-        if (log_base > 0.0) {
-            const float2 cs = rope_cos_sin(L, t, d, log_base);
-            const float2 y = rot_pair(x0, x1, cs.x, cs.y);
-            x0 = y.x;
-            x1 = y.y;
-        }
-        if (sizeof(T) == 2) {
-            *(uint32_t*)((uint16_t*)k_cache + dst + i) = pack_bf16x2(x0, x1);
+            uint32_t u = *(const uint32_t*)((const uint16_t*)k_new + src + i);
+            if (log_base > 0.0) {
+                const double2 cs = rope_cs64(L, t, d, log_base);
+                u = rot_pair_bf16(u, cs.x, cs.y);
+            }
+            *(uint32_t*)((uint16_t*)k_cache + dst + i) = u;
             *(uint32_t*)((uint16_t*)v_cache + dst + i) = *(const uint32_t*)((const uint16_t*)v_new + src + i);
         } else {
+            float x0 = ((const float*)k_new)[src + i];
+            float x1 = ((const float*)k_new)[src + i + 1];
+            if (log_base > 0.0) {
+                const double2 cs = rope_cs64(L, t, d, log_base);
+                const float2 y = rot_pair_f32(x0, x1, cs.x, cs.y);
+                x0 = y.x;
+                x1 = y.y;
+            }
             ((float*)k_cache)[dst + i] = x0;
             ((float*)k_cache)[dst + i + 1] = x1;
             ((float*)v_cache)[dst + i] = ((const float*)v_new)[src + i];

@@ -9,13 +9,13 @@ namespace {
 
 inline unsigned grid_for(long long n, int block) { return (unsigned)((n + block - 1) / block); }
 
-// tab[i][t] = (cos, sin) of (pos0 + i) * base^(-2t/d), i < n, t < d/2.
-__global__ void rope_table_kernel(float2* __restrict__ tab, long long pos0, int n, int d, double log_base) {
+// tab[i][t] = (cos, sin) of (pos0 + i) * base^(-2t/d) in float64, i < n, t < d/2.
+__global__ void rope_table_kernel(double2* __restrict__ tab, long long pos0, int n, int d, double log_base) {
     const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const int half = d / 2;
     if (idx >= (long long)n * half) return;
     const int i = (int)(idx / half), t = (int)(idx % half);
-    tab[idx] = rope_cos_sin(pos0 + i, t, d, log_base);
+    tab[idx] = rope_cs64(pos0 + i, t, d, log_base);
 }
 
 // Classification of keys [k0, k1) under the key-padding mask (nonzero =
@@ -29,7 +29,7 @@ __device__ __forceinline__ void classify(const uint8_t* row, int k0, int k1, boo
     if ((((uintptr_t)(row + k)) & 15) == 0) {
         for (; k + 16 <= k1; k += 16) {
             const uint4 u = *(const uint4*)(row + k);
-            any_ok |= word_has_zero_byte(u.x) | word_has_zero_byte(u.y) | word_has_zero_byte(u.z) |
+            any_ok |= word_has_zero_byte(u.x) || word_has_zero_byte(u.y) || word_has_zero_byte(u.z) ||
                       word_has_zero_byte(u.w);
             all_ok &= (u.x | u.y | u.z | u.w) == 0;
         }
@@ -156,27 +156,28 @@ __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__
 }
 
 // Rotary embedding of one token (all heads of one batch item) per workgroup:
-// the token's d/2 cos/sin pairs are computed once in LDS.
+// the token's d/2 float64 (cos, sin) pairs are computed once in LDS; each pair
+// is rotated in float64 and rounded once to the tensor's dtype.
 template <bool BF16>
 __global__ __launch_bounds__(256) void rope_apply_kernel(void* __restrict__ x, const long long* __restrict__ pos,
                                                          int T, int H, int d, double log_base) {
-    __shared__ float2 cs[128];
+    __shared__ double2 cs[128];
     const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int half = d / 2;
     const long long ps = pos[i];
-    for (int t = tid; t < half; t += blockDim.x) cs[t] = rope_cos_sin(ps, t, d, log_base);
+    for (int t = tid; t < half; t += blockDim.x) cs[t] = rope_cs64(ps, t, d, log_base);
     __syncthreads();
     const long long base = ((long long)b * T + i) * (long long)H * d;
     const int npairs = H * half;
     for (int pi = tid; pi < npairs; pi += blockDim.x) {
-        const float2 c = cs[pi % half];
+        const double2 c = cs[pi % half];
         if (BF16) {
             uint32_t* pp = (uint32_t*)((uint16_t*)x + base) + pi;
             *pp = rot_pair_bf16(*pp, c.x, c.y);
         } else {
             float2* pp = (float2*)((float*)x + base) + pi;
             const float2 v = *pp;
-            *pp = rot_pair(v.x, v.y, c.x, c.y);
+            *pp = rot_pair_f32(v.x, v.y, c.x, c.y);
         }
     }
 }
@@ -186,21 +187,34 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(void* __restrict__ x, c
 // else t - split + off1: a ring share's local queries are two runs of
 // positions, all of them positions of the keys, so one table of (cos, sin)
 // pairs over the keys' positions serves both.  The attention kernel then
-// streams already-rotated operands; the rotation is the same float32
-// arithmetic as rope_apply's, bit for bit.  One thread per 16-byte granule
-// (4 coordinate pairs).
+// streams already-rotated operands; the arithmetic is rope_apply's (float64,
+// one rounding), bit for bit.  A thread owns one 16-byte granule column
+// (4 coordinate pairs) of one token in HPT heads, so each table entry it
+// reads serves HPT granules.
+template <int HPT>
 __global__ __launch_bounds__(256) void rope_copy_bf16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                                             const float2* __restrict__ tab, long long n, int T,
-                                                             int H, int gpr, int split, long long off0,
+                                                             const double2* __restrict__ tab, long long n_threads,
+                                                             int T, int H, int gpr, int split, long long off0,
                                                              long long off1) {
     const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= n) return;
-    const long long row = g / gpr;   // (b * T + t) * H + h
-    const int c = (int)(g - row * gpr);
-    const int t = (int)((row / H) % T);
+    if (g >= n_threads) return;
+    const int hs = H / HPT;                  // heads apart of this thread's granules
+    const int tpt = hs * gpr;                // threads per token
+    const long long tok = g / tpt;           // b * T + t
+    const int r = (int)(g - tok * tpt);
+    const int c = r % gpr, j = r / gpr;
+    const int t = (int)(tok % T);
     const long long tr = t < split ? off0 + t : off1 + (t - split);
-    const float4* tp = (const float4*)(tab + tr * (4 * gpr) + 4 * c);
-    dst[g] = rope8_bf16(src[g], tp[0], tp[1]);
+    const double2* tp = tab + tr * (4 * gpr) + 4 * c;
+    const double2 c0 = tp[0], c1 = tp[1], c2 = tp[2], c3 = tp[3];
+    const long long row0 = tok * H * gpr + c;
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+        const long long at = row0 + (long long)(j + k * hs) * gpr;
+        const uint4 x = src[at];
+        dst[at] = make_uint4(rot_pair_bf16(x.x, c0.x, c0.y), rot_pair_bf16(x.y, c1.x, c1.y),
+                             rot_pair_bf16(x.z, c2.x, c2.y), rot_pair_bf16(x.w, c3.x, c3.y));
+    }
 }
 
 // Rows [0, rows) become the merge identity: out = 0 (float32 or bf16), lse = -inf.
@@ -227,7 +241,7 @@ __global__ __launch_bounds__(256) void fill_empty_kernel(void* __restrict__ out,
 
 }  // namespace
 
-hipError_t launch_rope_table(float2* tab, long long pos0, int n, int d, double log_base, hipStream_t s) {
+hipError_t launch_rope_table(double2* tab, long long pos0, int n, int d, double log_base, hipStream_t s) {
     const long long total = (long long)n * (d / 2);
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, tab, pos0, n, d, log_base);
@@ -274,16 +288,22 @@ hipError_t launch_rope_apply(void* x, const long long* pos, double log_base, int
     return hipGetLastError();
 }
 
-hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
+hipError_t launch_rope_copy_bf16(const void* src, void* dst, const double2* tab, int B, int T, int H, int d,
                                  int split, long long off0, long long off1, hipStream_t s) {
-    const long long n = (long long)B * T * H * (d / 8);
+    const int gpr = d / 8;
+    const int hpt = (H % 4 == 0) ? 4 : 1;
+    const long long n = (long long)B * T * (H / hpt) * gpr;
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(rope_copy_bf16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, (const uint4*)src, (uint4*)dst,
-                       tab, n, T, H, d / 8, split, off0, off1);
+    if (hpt == 4)
+        hipLaunchKernelGGL(rope_copy_bf16_kernel<4>, dim3(grid_for(n, 256)), dim3(256), 0, s, (const uint4*)src,
+                           (uint4*)dst, tab, n, T, H, gpr, split, off0, off1);
+    else
+        hipLaunchKernelGGL(rope_copy_bf16_kernel<1>, dim3(grid_for(n, 256)), dim3(256), 0, s, (const uint4*)src,
+                           (uint4*)dst, tab, n, T, H, gpr, split, off0, off1);
     return hipGetLastError();
 }
 
-hipError_t launch_rope_copy_bf16(const void* src, void* dst, const float2* tab, int B, int T, int H, int d,
+hipError_t launch_rope_copy_bf16(const void* src, void* dst, const double2* tab, int B, int T, int H, int d,
                                  hipStream_t s) {
     return launch_rope_copy_bf16(src, dst, tab, B, T, H, d, T, 0, 0, s);
 }

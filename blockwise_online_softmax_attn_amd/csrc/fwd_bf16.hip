@@ -849,11 +849,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
             ci = 0;
             finish_empty_blocks();
         }
-        // After a merge the epilogue has waited for its own loads of the
-        // partial, so every older tile load is complete too; its stores may
-        // drain during the next tile (the next wait covers them).
+        // After a merge the epilogue of a wave with a valid row has waited
+        // for its own loads of the partial, so every older tile load of that
+        // wave is complete too; its stores may drain during the next tile (the
+        // next wait covers them).  A wave whose rows all lie past Tq skipped
+        // that epilogue, so it waits for its tile loads here (wvalid and
+        // merged are the same for every lane of the wave).
         if (!more) wait_barrier<0>();
-        else if (merged) lds_barrier();
+        else if (merged && wvalid) lds_barrier();
         else wait_barrier<PT>();
     };
     for (int g = 0; g < ntot; g += 2) {

@@ -50,9 +50,9 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(const FwdParams p) 
     for (int c = 0; c < HD; c += 4) {
         float4 x = qvalid ? *(const float4*)(qg + (long long)qi * rs + c0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
         if (qvalid && p.rope_q) {
-            const float4 cs = *(const float4*)(p.rope_q + (long long)qi * (D / 2) + (c0 + c) / 2);
-            const float2 y0 = rot_pair(x.x, x.y, cs.x, cs.y);
-            const float2 y1 = rot_pair(x.z, x.w, cs.z, cs.w);
+            const double2* cs = p.rope_q + (long long)qi * (D / 2) + (c0 + c) / 2;
+            const float2 y0 = rot_pair_f32(x.x, x.y, cs[0].x, cs[0].y);
+            const float2 y1 = rot_pair_f32(x.z, x.w, cs[1].x, cs[1].y);
             x = make_float4(y0.x, y0.y, y1.x, y1.y);
         }
         q[c] = x.x; q[c + 1] = x.y; q[c + 2] = x.z; q[c + 3] = x.w;
@@ -81,9 +81,9 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(const FwdParams p) 
                 kx = *(const float4*)(kg + (long long)key * rs + 4 * c4);
                 vx = *(const float4*)(vg + (long long)key * rs + 4 * c4);
                 if (p.rope_k) {
-                    const float4 cs = *(const float4*)(p.rope_k + (long long)key * (D / 2) + 2 * c4);
-                    const float2 y0 = rot_pair(kx.x, kx.y, cs.x, cs.y);
-                    const float2 y1 = rot_pair(kx.z, kx.w, cs.z, cs.w);
+                    const double2* cs = p.rope_k + (long long)key * (D / 2) + 2 * c4;
+                    const float2 y0 = rot_pair_f32(kx.x, kx.y, cs[0].x, cs[0].y);
+                    const float2 y1 = rot_pair_f32(kx.z, kx.w, cs[1].x, cs[1].y);
                     kx = make_float4(y0.x, y0.y, y1.x, y1.y);
                 }
             }

@@ -28,15 +28,23 @@
  *    (0, -inf) is the identity of attn_merge.
  *  - Ownership: every pointer is caller-owned device memory (except where a
  *    host pointer is stated).  The library keeps no device state between
- *    calls; attn_fwd with a rotary embedding allocates a small stream-ordered
- *    cos/sin table on `stream` and frees it on the same stream.
+ *    calls.  Some calls need device scratch: they allocate it stream-ordered
+ *    on `stream` (hipMallocAsync) before their first launch and free it on
+ *    the same stream after their last one (hipFreeAsync), so it lives only
+ *    as long as the call's work.  Each entry point below states its scratch
+ *    in bytes as a formula of its sizes ("Scratch:"); every term is rounded
+ *    up to a multiple of 256 bytes.  Entry points without a "Scratch:" line
+ *    allocate nothing.
  *  - Streams: every call only enqueues work on `stream` (NULL = the null
  *    stream) and returns; there is no host synchronisation inside.
- *  - Errors: arguments are validated on the host before any HIP call; a
- *    failing call returns a nonzero attn_status, enqueues nothing, and
- *    attn_last_error() describes the problem (thread-local string).  Launch
- *    failures return ATTN_ERR_HIP.  Faults during execution surface at the
- *    caller's next synchronisation.
+ *  - Errors: arguments are validated on the host before any HIP call; a call
+ *    that fails validation returns ATTN_ERR_INVALID_ARG or
+ *    ATTN_ERR_UNSUPPORTED, enqueues nothing, and attn_last_error() describes
+ *    the problem (thread-local string).  A failed scratch allocation (device
+ *    memory exhausted) or kernel launch returns ATTN_ERR_HIP; an allocation
+ *    failure happens before the call's first launch, a launch failure may
+ *    leave the call's earlier launches enqueued.  Faults during execution
+ *    surface at the caller's next synchronisation.
  */
 #ifndef BOSA_ATTN_H
 #define BOSA_ATTN_H
@@ -89,15 +97,21 @@ enum {
  *  causal     nonzero: key j is allowed for query i only if kv_off+j <= q_off+i.
  *  kpm        device uint8 (B, Tkv) or NULL.  attn_mask: device uint8 (Tq, Tkv) or NULL.
  *  rope_base  > 0: rotate adjacent coordinate pairs (2t, 2t+1) of q and k by
- *             pos * rope_base^(-2t/d) (the angle formed in float64, its cos
- *             and sin rounded to float32), in float32, and round the rotated
- *             values to `dtype` before the dot product.  0: no rotary
- *             embedding.  A float64 angle carries an absolute error that
- *             grows with the position: about 1e-4 rad near position 2^40,
- *             tenths of a radian near 2^52.
+ *             pos * rope_base^(-2t/d) (angle, cos, sin and rotation in
+ *             float64) and round the rotated values once, to nearest even,
+ *             to `dtype` before the dot product.  0: no rotary embedding.  A
+ *             float64 angle carries an absolute error that grows with the
+ *             position: about 1e-4 rad near position 2^40, tenths of a
+ *             radian near 2^52.
  *  dtype      ATTN_BF16 (bf16 MFMA, float32 accumulation and softmax) or
  *             ATTN_F32 (float32 throughout).
  *  flags      ATTN_ACCUMULATE | ATTN_OUT_F32 | ATTN_NO_TILE_SKIP.
+ * Scratch:    with rope_base > 0 and Tkv > 0, the float64 (cos, sin) tables
+ *             (Tq + Tkv) * (d/2) * 16; in bf16 also the rotated copies of k
+ *             and q, 2 * B * (Tkv + Tq) * H * d (the kernel streams
+ *             rotated operands).  In bf16 with kpm (without
+ *             ATTN_NO_TILE_SKIP) the live key-tile list,
+ *             4 * B * (ceil(Tkv / 64) + 2).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int Tq, int Tkv, int d,
@@ -133,6 +147,7 @@ typedef struct attn_variant {
  * Same arguments and conventions as attn_fwd, plus `var` (host pointer,
  * read during the call; NULL = attn_fwd).  Windows must be >= -1.  Tiles
  * outside every row's window are skipped like fully masked tiles.
+ * Scratch: as attn_fwd.
  */
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
                 int B, int H, int Tq, int Tkv, int d,
@@ -190,8 +205,9 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
  *               attn_fwd_ex; window_right has no effect (nothing after the
  *               query is filled).
  *  flags        0 or ATTN_OUT_F32.
- * The call allocates a stream-ordered scratch of B * H * chunks * (d + 1)
- * floats for the partial results and frees it on `stream`.
+ * Scratch: the chunks' partial results, 4 * B * H * n * d + 4 * B * H * n
+ * with n = the number of chunks, at most ceil(8192 / (B * H)): below
+ * 4 * (d + 1) * (8192 + B * H) in all.
  */
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_len,
                 void* out, float* lse, int B, int H, int Tcap, int d, double rope_base, int dtype,
@@ -223,8 +239,8 @@ int attn_merge(float* out_a, float* lse_a, const void* out_b, const float* lse_b
  * split into coordinate pairs, each rotated by a positional angle, so that a
  * rotated query and key interact through their position difference only.
  * Pair (2t, 2t+1) of token i is rotated by pos[i] * base^(-2t/d):
- * (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a), computed in float32
- * from float64-accurate cos/sin and rounded to `dtype`.
+ * (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a), computed in float64
+ * and rounded once, to nearest even, to `dtype`.
  *
  *  x          device (B, T, H, d) of dtype `dtype`, rotated in place.
  *  pos        device int64 [T]: absolute position of each token (shared over B and H).
@@ -289,8 +305,15 @@ int attn_ring_plan(int T, int P, int rank, int zigzag, int causal, attn_ring_cal
  *  block run in one kernel launch, with each sub-call's partial written or
  *  merged exactly as by its own launch: out and lse are bit for bit those of
  *  one attn_fwd call per sub-call.  With RoPE the call rotates every key
- *  block and the local queries once into stream-ordered scratch (released on
- *  `stream` when the call's work is done).
+ *  block and the local queries once into scratch copies.
+ * Scratch:    with rope_base > 0, the float64 (cos, sin) table over the T
+ *             positions, T * (d/2) * 16; in bf16 also the rotated keys and
+ *             local queries, 2 * B * (T + T/P) * H * d.  In bf16 with kpm
+ *             (without ATTN_NO_TILE_SKIP) one live key-tile list per
+ *             sub-call, 4 * B * (ceil(c / 64) + 2) each, c = the sub-call's
+ *             key rows (T/P, or T/(2P) under zigzag).  The 128K zigzag share
+ *             (B = 1, H = 32, d = 128, T = 131072, P = 8) with RoPE:
+ *             128 MiB + 1 GiB + 128 MiB.
  */
 int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse, float* acc,
                   int B, int H, int T, int d, int P, int rank, int zigzag, int causal,
@@ -338,8 +361,15 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
  *  flags         ATTN_ACCUMULATE | ATTN_OUT_F32 | ATTN_NO_TILE_SKIP.
  *  Rows with no allowed key contribute nothing; keys with kpm set get zero
  *  gradients.  Results are deterministic (every output element is written by
- *  one workgroup).  Scratch (rotated q and k, float32 gradients, the
- *  per-row (lse, delta)) is allocated and freed on `stream`.
+ *  one workgroup).
+ * Scratch:       the per-row (lse, delta) pairs, 8 * B * H * Tq; with
+ *                rope_base > 0 the float64 (cos, sin) tables
+ *                (Tq + Tkv) * (d/2) * 16 and the rotated q and k,
+ *                2 * B * (Tq + Tkv) * H * d; float32 gradients
+ *                4 * B * H * d * (Tq + 2 * Tkv) unless the call writes
+ *                float32 gradients without RoPE (then the kernels write
+ *                dq, dk, dv directly); with kpm (without ATTN_NO_TILE_SKIP)
+ *                the live key-tile list, 4 * B * (ceil(Tkv / 64) + 2).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
              const float* lse, void* dq, void* dk, void* dv,
@@ -376,6 +406,13 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
  *                contributions only (keys no local row sees get 0).
  *  flags         ATTN_OUT_F32 | ATTN_NO_TILE_SKIP.  Other arguments as
  *                attn_ring_fwd.
+ * Scratch:       the per-row (lse, delta) pairs, 8 * B * H * (T/P); the
+ *                float32 gradients of the share, 4 * B * H * d * (T/P + 2 T);
+ *                with rope_base > 0 the float64 (cos, sin) tables
+ *                (T/P + T) * (d/2) * 16 and the rotated q and k,
+ *                2 * B * (T/P + T) * H * d; with kpm (without
+ *                ATTN_NO_TILE_SKIP) one live key-tile list per sub-call as
+ *                for attn_ring_fwd.
  */
 int attn_ring_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv,

@@ -226,14 +226,16 @@ def test_fused_rope_matches_rope_apply_bitwise(dtype):
     o2, l2 = gpu_fwd(qd.cpu(), kd.cpu(), v, q_off=q_off, kv_off=kv_off, causal=True)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     # rope_apply against the oracle's rotation (float64, rounded once to the
-    # dtype): the same bits except where the two float64 angle evaluations land
-    # on opposite sides of a rounding midpoint (then one unit apart)
+    # dtype): the same bits except where the two float64 angle evaluations
+    # (about 1e-11 rad apart at positions near 1e5) land on opposite sides of
+    # a rounding midpoint, then one unit apart: a rate of about 1e-11 / 2^-24
+    # for float32, about 1e-11 / 2^-8 (none expected) for bf16
     ref = oracle.round_to_dtype(oracle.rope_rotate(np64(q), q_off + np.arange(Tq), 10000.0),
                                 "f32" if dtype == torch.float32 else "bf16")
     got = np64(qd.cpu())
     diff = got != ref
     note(f"rope_apply {dtype}: {int(diff.sum())} of {diff.size} elements differ from the oracle")
-    assert diff.mean() < 1e-5
+    assert diff.mean() < (2e-4 if dtype == torch.float32 else 1e-5)
     ulp = 2.0 ** -23 if dtype == torch.float32 else 2.0 ** -7
     assert np.all(np.abs(got - ref)[diff] <= np.abs(ref[diff]) * ulp)
 
@@ -334,11 +336,23 @@ def test_ring_share_equals_its_subcalls_bitwise(zigzag, causal, kp, rope, d):
     and lse equal, bit for bit, one attn_fwd call per sub-call of
     attn_ring_plan (in plan order, each writing or merging its partial into a
     float32 accumulator of its query block), then the cast, on every rank."""
-    P, B, H, T = 4, 1, 2, 1536
+    _ring_share_vs_subcalls(4, 1, 2, 1536, d, zigzag, causal, kp, rope, range(4))
+
+
+@pytest.mark.parametrize("zigzag,T", [(False, 18432), (True, 36864)])
+def test_ring_share_equals_its_subcalls_bitwise_above_one_round(zigzag, T):
+    """The same bit-for-bit check where a sub-call's launch has more
+    workgroups than the chip has CUs (16 heads x 18 query tiles = 288): there
+    a chain ends after the sub-call that causal order cuts through the query
+    block, so the cut path runs; ranks 0 and 3 of P = 4, key padding, RoPE."""
+    _ring_share_vs_subcalls(4, 1, 16, T, 128, zigzag, True, 0.1, 10000.0, (0, 3))
+
+
+def _ring_share_vs_subcalls(P, B, H, T, d, zigzag, causal, kp, rope, ranks):
     k = rnd((B, T, H, d), 9601, torch.bfloat16).to(DEV)
     v = rnd((B, T, H, d), 9602, torch.bfloat16).to(DEV)
     kpm = workloads.random_mask((B, T), 9603, kp).to(DEV) if kp else None
-    for rank in range(P):
+    for rank in ranks:
         q = rnd((B, T // P, H, d), 9610 + rank, torch.bfloat16).to(DEV)
         out, lse = bosa.attn_ring_fwd(q, k, v, P=P, rank=rank, zigzag=zigzag, causal=causal, kpm=kpm, rope_base=rope)
         plan = bosa.attn_ring_plan(T, P, rank, zigzag, causal)
