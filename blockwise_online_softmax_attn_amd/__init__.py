@@ -134,9 +134,11 @@ def attn_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tens
 def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_len: torch.Tensor,
                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, *, rope_base: float = 0.0,
                 window_left: int = -1, alibi_slopes: Optional[torch.Tensor] = None, flags: int = 0,
-                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                noalloc: bool = False, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """out (B, H, d), lse (B, H) of each row's newest query over its cache
-    (see attn_decode in attn.h)."""
+    (see attn_decode in attn.h).  noalloc selects attn_decode_noalloc (the
+    library allocates nothing; pass out and lse to allocate nothing here
+    either)."""
     load()
     B, Tcap, H, d = k_cache.shape
     if v_cache.shape != k_cache.shape or q.shape != (B, H, d):
@@ -153,7 +155,8 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, c
     if out.shape != (B, H, d) or lse.shape != (B, H):
         raise ValueError("out/lse shape mismatch")
     var, _keep = _variant((window_left, -1) if window_left >= 0 else None, alibi_slopes, H)
-    rc = load().attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+    fn = load().attn_decode_noalloc if noalloc else load().attn_decode
+    rc = fn(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                             _dev(cache_len, "cache_len", torch.int32), _dev(out, "out", out_dtype),
                             _dev(lse, "lse", torch.float32), B, H, Tcap, d, float(rope_base), _dtype_code(q),
                             int(flags), var, _stream(stream))

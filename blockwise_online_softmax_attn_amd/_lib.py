@@ -15,8 +15,8 @@ ATTN_ACCUMULATE, ATTN_OUT_F32, ATTN_NO_TILE_SKIP = 1, 2, 4
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan", "attn_ring_fwd",
-           "attn_ring_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_ring_bwd", "attn_ring_bwd_ex", "attn_kv_append", "attn_decode", "attn_profile_start",
-           "attn_profile_stop", "attn_last_error", "attn_version")
+           "attn_ring_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_ring_bwd", "attn_ring_bwd_ex", "attn_kv_append", "attn_decode",
+           "attn_decode_noalloc", "attn_profile_start", "attn_profile_stop", "attn_last_error", "attn_version")
 
 
 class RingCall(ctypes.Structure):
@@ -67,6 +67,7 @@ def load() -> ctypes.CDLL:
     lib.attn_ring_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, d, i, u, var, vp]
     lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, d, i, vp]
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, d, i, u, var, vp]
+    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, d, i, u, var, vp]
     lib.attn_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.rope_apply.argtypes = [vp, vp, d, i, i, i, i, i, vp]
     lib.attn_cast.argtypes = [vp, vp, ll, i, vp]
@@ -78,7 +79,7 @@ def load() -> ctypes.CDLL:
     lib.attn_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_float), i]
     for name in ("attn_fwd", "attn_fwd_ex", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan",
                  "attn_ring_fwd", "attn_ring_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_ring_bwd", "attn_ring_bwd_ex",
-                 "attn_kv_append", "attn_decode",
+                 "attn_kv_append", "attn_decode", "attn_decode_noalloc",
                  "attn_profile_start", "attn_profile_stop", "attn_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.attn_last_error.argtypes = []

@@ -436,9 +436,12 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "cache append launch");
 }
 
-int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_len, void* out, float* lse,
-                int B, int H, int Tcap, int d, double rope_base, int dtype, unsigned flags, const attn_variant* var,
-                attn_stream_t stream) {
+// attn_decode and attn_decode_noalloc: the same validation and kernels; the
+// chunk partials go to stream-ordered scratch, or (static_ws) to the
+// library's per-device static workspace.
+static int decode_call(const void* q, const void* k_cache, const void* v_cache, const int* cache_len, void* out,
+                       float* lse, int B, int H, int Tcap, int d, double rope_base, int dtype, unsigned flags,
+                       const attn_variant* var, attn_stream_t stream, bool static_ws) {
     g_err.clear();
     if (B < 0 || H < 0 || Tcap < 0) return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 0");
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", d);
@@ -458,6 +461,13 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     const long long CH = decode_chunk_size(Tcap, bh, d, bf16);
     const long long nch = Tcap > 0 ? (Tcap + CH - 1) / CH : 1;
     if (bh * nch >= (1LL << 31) || CH >= (1LL << 30)) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+    const size_t po = align_up((size_t)bh * nch * d * sizeof(float));
+    const size_t pl = align_up((size_t)bh * nch * sizeof(float));
+    if (static_ws && po + pl > kDecodeStaticBytes)
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "attn_decode_noalloc: the chunk partials of B*H=%lld rows need %zu bytes, more than the "
+                    "%zu-byte static workspace (about B*H <= %lld at d=%d)", bh, po + pl, kDecodeStaticBytes,
+                    (long long)(kDecodeStaticBytes / (4 * (size_t)(d + 1))) - 8192, d);
     DecodeParams p{};
     p.q = q; p.k = k_cache; p.v = v_cache; p.cache_len = cache_len; p.out = out; p.lse = lse;
     p.alibi = var ? var->alibi_slopes : nullptr;
@@ -467,18 +477,36 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     p.sqrt_d = (float)std::sqrt((double)d);
     hipStream_t s = (hipStream_t)stream;
-    const size_t po = align_up((size_t)bh * nch * d * sizeof(float));
-    const size_t pl = align_up((size_t)bh * nch * sizeof(float));
     Scratch ws;
-    hipError_t e = ws.alloc(po + pl, s);
-    if (e != hipSuccess) return hip_fail(e, "scratch allocation");
-    p.part_o = (float*)ws.ptr;
-    p.part_lse = (float*)((char*)ws.ptr + po);
+    void* wsp = nullptr;
+    hipError_t e;
+    if (static_ws) {
+        if ((e = decode_static_workspace(&wsp)) != hipSuccess) return hip_fail(e, "static workspace lookup");
+    } else {
+        if ((e = ws.alloc(po + pl, s)) != hipSuccess) return hip_fail(e, "scratch allocation");
+        wsp = ws.ptr;
+    }
+    p.part_o = (float*)wsp;
+    p.part_lse = (float*)((char*)wsp + po);
     if (Tcap > 0)
         if (int rc = timed_launch([&] { return launch_decode_chunks(p, d, bf16, s); }, "decode kernel launch", s))
             return rc;
     e = launch_decode_merge(p, d, bf16 && !(flags & ATTN_OUT_F32), s);
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "decode merge launch");
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_len, void* out, float* lse,
+                int B, int H, int Tcap, int d, double rope_base, int dtype, unsigned flags, const attn_variant* var,
+                attn_stream_t stream) {
+    return decode_call(q, k_cache, v_cache, cache_len, out, lse, B, H, Tcap, d, rope_base, dtype, flags, var, stream,
+                       false);
+}
+
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* cache_len, void* out,
+                        float* lse, int B, int H, int Tcap, int d, double rope_base, int dtype, unsigned flags,
+                        const attn_variant* var, attn_stream_t stream) {
+    return decode_call(q, k_cache, v_cache, cache_len, out, lse, B, H, Tcap, d, rope_base, dtype, flags, var, stream,
+                       true);
 }
 
 int attn_merge(float* out_a, float* lse_a, const void* out_b, const float* lse_b, int B, int H, int Tq, int d,

@@ -229,6 +229,11 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_fwd_bf16_chain(const ChainParams& c, int d, hipStream_t s);
 long long decode_chunk_size(long long Tcap, long long bh, int d, int is_bf16);
 hipError_t launch_decode_chunks(const DecodeParams& p, int d, int is_bf16, hipStream_t s);
+// The per-device static workspace of attn_decode_noalloc (kDecodeStaticBytes
+// bytes): its device address on the current device (looked up on the first
+// call per device, no allocation).
+constexpr size_t kDecodeStaticBytes = size_t(16) << 20;
+hipError_t decode_static_workspace(void** ptr);
 hipError_t launch_decode_merge(const DecodeParams& p, int d, int out_bf16, hipStream_t s);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, int* cache_len, int B,
                             int H, int Tcap, int d, double log_base, int is_bf16, hipStream_t s);

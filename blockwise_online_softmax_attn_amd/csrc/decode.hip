@@ -284,6 +284,32 @@ hipError_t launch_chunks_a(const DecodeParams& p, hipStream_t s) {
 
 }  // namespace
 
+// Workspace of attn_decode_noalloc: the chunk partials of a call live here
+// instead of in stream-ordered scratch.  One copy per device, kept for the
+// life of the process; every call on a device uses (and overwrites) it.
+static __device__ __align__(256) unsigned char scratch[kDecodeStaticBytes];
+
+hipError_t decode_static_workspace(void** ptr) {
+    // Device address of `scratch` on the current device, looked up once per
+    // device.  In host code `scratch` names a host-side stand-in, so only the
+    // address returned here may be handed to kernels.
+    constexpr int kMaxDev = 64;
+    static std::atomic<void*> addr[kMaxDev];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    void* a = addr[dev].load(std::memory_order_acquire);
+    if (!a) {
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!a) return hipErrorInvalidSymbol;
+        addr[dev].store(a, std::memory_order_release);
+    }
+    *ptr = a;
+    return hipSuccess;
+}
+
 long long decode_chunk_size(long long Tcap, long long bh, int d, int is_bf16) {
     const int epl = is_bf16 ? 8 : 4;
     const long long gran = (64 / (d / epl)) * DW * DU;   // keys one workgroup iteration covers

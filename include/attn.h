@@ -214,6 +214,25 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
                 unsigned flags, const attn_variant* var, attn_stream_t stream);
 
 /*
+ * attn_decode_noalloc -- attn_decode that allocates nothing, for callers that
+ * cannot allocate device memory during the call: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results and kernels as attn_decode (bit for bit).  The
+ * chunk partials go to a static workspace of 16 MiB that the library holds on
+ * every device it runs on until the process ends (its address is looked up on
+ * the first call on a device).  A call whose partials need more
+ * (4 * B * H * n * (d + 1) bytes with n chunks as for attn_decode; about
+ * B * H > 24000 at d = 128) returns ATTN_ERR_UNSUPPORTED and enqueues
+ * nothing.  Every call on one device shares that device's workspace: calls
+ * that may overlap on one device (different streams without ordering, or
+ * several host threads) race and must be serialised by the caller.
+ */
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* cache_len,
+                        void* out, float* lse, int B, int H, int Tcap, int d, double rope_base, int dtype,
+                        unsigned flags, const attn_variant* var, attn_stream_t stream);
+
+/*
  * attn_merge -- (out_a, lse_a) <- (out_a, lse_a) (+) (out_b, lse_b), in place.
  *
  * The pages call an accumulate step after every ring step without defining

@@ -87,6 +87,22 @@ def test_other_entry_points_reject_bad_arguments():
     assert lib.attn_ring_plan(8, 2, 2, 0, 1, None, 0) < 0                               # rank out of range
 
 
+def test_decode_noalloc_checks_its_workspace_before_any_hip_call():
+    """attn_decode_noalloc validates like attn_decode and rejects partials
+    larger than its static workspace on the host (no GPU is touched here)."""
+    lib = bosa.load()
+    p = 1 << 20
+    # 40000 rows of partials at d = 128: about 20 MB, over the 16 MiB workspace
+    assert lib.attn_decode_noalloc(p, p, p, p, p, p, 1, 40000, 1, 128, 0.0, _lib.ATTN_BF16, 0, None,
+                                   None) == _lib.ATTN_ERR_UNSUPPORTED
+    assert b"static workspace" in lib.attn_last_error()
+    assert lib.attn_decode_noalloc(p, p, p, p, p, p, 1, 4, 16, 96, 0.0, _lib.ATTN_BF16, 0, None,
+                                   None) == _lib.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_decode_noalloc(None, p, p, p, p, p, 1, 4, 16, 128, 0.0, _lib.ATTN_BF16, 0, None,
+                                   None) == _lib.ATTN_ERR_INVALID_ARG
+    assert lib.attn_decode_noalloc(p, p, p, p, p, p, 0, 4, 16, 128, 0.0, _lib.ATTN_BF16, 0, None, None) == 0
+
+
 def _pairs_of_plan(plan, T, P, rank, zigzag, causal):
     """(query position, key position) pairs the plan evaluates."""
     qpos = oracle.local_query_positions(T, P, rank, zigzag)
