@@ -33,6 +33,11 @@ and dK/dV kernels of one sub-call together as one launch.
 step_ms  = median, min and max wall time of single steps, from one HIP event
          at each step boundary over K more steps (a third pass; value and
          ms_per_step come from the first, which has no events inside it).
+targets = the default run (workload 4, forward) also times workloads 2 (the
+         8K ring share) and 3 (the encoder), the other configurations of the
+         >= 50 % of peak target, by the same method, each in a child process
+         started before this one initialises the GPU: step and kernel-only
+         TFLOP/s with their fractions of the peak.  --no-targets skips them.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -391,6 +396,67 @@ def cpu_baseline(w, host_inputs, rows: int, heads: int, dout=None):
     }
 
 
+def time_steps(step, launches: int, flops: float, steps: int, per_launch: int = 1):
+    """Time `steps` steps (HIP events on the current stream around them all),
+    then the attention kernels alone (HIP events the library records around
+    every launch on the launch's stream, over `steps` further steps, so they
+    add no gaps to the step time), then per-step wall times (a third pass).
+    Returns ms per step, step TFLOP/s, kernel-only TFLOP/s, the per-launch
+    times, the per-step statistics and the clock sampler."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {steps} steps")
+    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        start.record()
+        for _ in range(steps):
+            step()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        with bosa.KernelTimer(max_launches=steps * launches * per_launch + 16) as kt:
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+    stats = step_stats(step, steps)
+    kms = np.asarray(kt.ms, dtype=np.float64)
+    kern_ms = float(kms.sum())
+    achieved = flops * steps / (kern_ms * 1e-3) / 1e12 if kern_ms > 0 else None
+    return ms, flops / (ms * 1e-3) / 1e12, achieved, kms, stats, clk
+
+
+# the other forward workloads of the >= 50 % of peak target, timed by the
+# default run with the same method and reported under "targets"
+TARGET_WORKLOADS = (2, 3)
+
+
+def target_lines(args) -> dict:
+    """Forward workloads 2 and 3, each timed by this script in a child process
+    of its own (fresh device state, as a separate run would see it), started
+    before this process touches the GPU.  Returns a summary per workload."""
+    import subprocess
+    out = {}
+    for wi in TARGET_WORKLOADS:
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", str(wi), "--steps", str(args.steps),
+               "--no-cpu-baseline", "--no-targets"]
+        log(f"target workload {wi}: {' '.join(cmd[1:])}")
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+        lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+        if r.returncode != 0 or not lines:
+            out[f"workload{wi}"] = {"error": f"exit status {r.returncode}"}
+            continue
+        t = json.loads(lines[-1])
+        ro = t["roofline"]
+        out[f"workload{wi}"] = {
+            "workload": t["config"]["workload"], "steps": t["steps"], "warmup": t["warmup"],
+            "ms_per_step": t["ms_per_step"], "step_ms": t["step_ms"], "value": t["value"], "unit": t["unit"],
+            "frac": t["value"] / PEAK_BF16_TFLOPS,
+            "kernel": {"name": ro["kernel"], "achieved": ro["achieved"], "frac": ro["frac"],
+                       "launches_per_step": t["config"]["attention_launches_per_step"],
+                       "avg_launch_ms": ro["avg_launch_ms"]},
+            "algorithmic_flops_per_step": t["config"]["algorithmic_flops_per_step"], "clock": t["clock"]}
+    return out
+
+
 # ---------------------------------------------------------------- decoding
 def run_decode(args, w) -> dict:
     """One decoding step per iteration over a static cache of w.T slots per
@@ -555,6 +621,8 @@ def main() -> int:
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward share (default, the headline metric) or its backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-targets", action="store_true",
+                    help="skip the extra forward workloads (2 and 3) the default run times in child processes")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--graph", action="store_true",
@@ -575,6 +643,11 @@ def main() -> int:
               "on that GPU); runs on more than one GPU are not part of this build. Use --gpus 1.",
               file=sys.stderr)
         return 2
+    # the default run also times workloads 2 and 3, in child processes started
+    # before this process initialises the GPU
+    targets = None
+    if args.which == "fwd" and args.workload == 4 and not args.no_targets:
+        targets = target_lines(args)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
@@ -614,25 +687,8 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
     args.warmup = warm_up(step, args.warmup)
-
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    with ClockSampler() as clk:
-        start.record()
-        for _ in range(args.steps):
-            step()
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / args.steps
-        # the attention kernels alone: HIP events around every launch, on the
-        # launch's stream, over K further steps (kept out of the step time above,
-        # where they would add a gap per launch)
-        with bosa.KernelTimer(max_launches=args.steps * launches + 16) as kt:
-            for _ in range(args.steps):
-                step()
-            torch.cuda.synchronize()
-    stats = step_stats(step, args.steps)
+    per_launch = 2 if bwd else 1
+    ms, tflops, achieved, kms, stats, clk = time_steps(step, launches, flops, args.steps, per_launch)
     graph = None
     if args.graph and not bwd:
         graph = graph_pass(step, args.steps, step.outputs)
@@ -641,14 +697,8 @@ def main() -> int:
             log(f"graph replay: {graph['ms_per_step']:.4f} ms/step, {graph['value']:.1f} TFLOP/s")
         else:
             log(f"graph: {graph['error']}")
-    tflops = flops / (ms * 1e-3) / 1e12
-    kms = np.asarray(kt.ms, dtype=np.float64)
     kern_ms = float(kms.sum())
-    # one attention launch of the backward is the dQ kernel and the dK/dV
-    # kernel of one sub-call (timed in that order)
-    per_launch = 2 if bwd else 1
     n_launch = len(kms) // per_launch
-    achieved = flops * args.steps / (kern_ms * 1e-3) / 1e12 if kern_ms > 0 else None
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     log(f"{ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of peak); kernel-only "
         f"{achieved:.1f} TFLOP/s over {n_launch} launches (avg {kern_ms / max(n_launch, 1):.4f} ms)")
@@ -711,6 +761,8 @@ def main() -> int:
     }
     if graph is not None:
         line["graph"] = graph
+    if targets is not None:
+        line["targets"] = targets
     clock = line["clock"]
     if clock and w.dtype == "bf16":
         # the same MFMA rate per clock at the clock the work ran at

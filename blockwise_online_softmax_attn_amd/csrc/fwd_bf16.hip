@@ -33,6 +33,8 @@
 // then S_{i+1} = K_{i+1} Q^T on the matrix cores interleaved with the
 // exponentials of S_i on the vector ALU; then O += V_i P_i; wait for tile
 // i + 2 and synchronise the workgroup.
+#include <type_traits>
+
 #include "tile_io.h"
 
 namespace bosa {
@@ -49,6 +51,9 @@ constexpr int NSLOT = 4;   // LDS tile slots (tiles i .. i + 3)
 // rounding for any reference.
 constexpr float kTau = 8.f;
 
+template <int N>
+using IC = std::integral_constant<int, N>;
+
 template <int D>
 struct Geo {
     static constexpr int NC = D / 16;                // 16-wide d chunks of Q K^T
@@ -57,8 +62,16 @@ struct Geo {
     static constexpr int ROW = 2 * D;                // bytes per K/V row in LDS
     static constexpr int RP = 256 / ROW;             // rows per 256-byte bank window
     static constexpr int TILE = BN * ROW;            // bytes per K or V tile
-    static constexpr int SLOT = 2 * TILE;            // K tile, then V tile
+    static constexpr int SLOT = 2 * TILE;            // one K and one V tile
     static constexpr int LDS_BYTES = NSLOT * SLOT;
+    // The K tiles of the NSLOT slots come first, then the V tiles: with the
+    // slot a compile-time constant (the tile loop is unrolled NSLOT times) a
+    // K operand read is (lane offset) + immediate, and V reads use lane
+    // offsets that already include VBASE, so no per-tile address add is
+    // needed (ds_read immediates reach 65535 bytes).
+    static constexpr int VBASE = NSLOT * TILE;
+    static constexpr int kt(int s) { return s * TILE; }          // K tile of slot s
+    static constexpr int vt(int s) { return s * TILE; }          // V tile of slot s, relative to VBASE
     static constexpr int NBLK = TILE / 1024;         // 1 KB load blocks per tile and tensor
     static constexpr int NI = NBLK / NW;             // load blocks per wave per tile and tensor
     static constexpr int RPB = 1024 / ROW;           // rows per load block
@@ -96,24 +109,25 @@ __device__ __forceinline__ void update_max(const f32x16& s0, const f32x16& s1, f
     }
 }
 
-// S^T of one tile: keys [0, 32) into s0 and [32, 64) into s1.  Kt = K tile
-// in LDS; koff = per-lane operand offsets (granule c of this lane's key row).
+// S^T of one tile: keys [0, 32) into s0 and [32, 64) into s1.  Kt = offset
+// of the K tile in LDS (a constant after inlining); koff = per-lane LDS
+// addresses of the operands (granule c of this lane's key row in slot 0).
 template <int D>
-__device__ __forceinline__ void scores(const char* Kt, const uint32_t (&koff)[Geo<D>::NC],
+__device__ __forceinline__ void scores(uint32_t Kt, const uint32_t (&koff)[Geo<D>::NC],
                                        const bf16x8 (&qreg)[Geo<D>::NC], f32x16& s0, f32x16& s1) {
     using G = Geo<D>;
     bf16x8 ka0[G::NC], ka1[G::NC];
-    ka0[0] = *(const bf16x8*)(Kt + koff[0]);
-    ka1[0] = *(const bf16x8*)(Kt + koff[0] + 32 * G::ROW);
-    ka0[1] = *(const bf16x8*)(Kt + koff[1]);
-    ka1[1] = *(const bf16x8*)(Kt + koff[1] + 32 * G::ROW);
+    ka0[0] = lds_b128(koff[0] + Kt);
+    ka1[0] = lds_b128(koff[0] + Kt + 32 * G::ROW);
+    ka0[1] = lds_b128(koff[1] + Kt);
+    ka1[1] = lds_b128(koff[1] + Kt + 32 * G::ROW);
     s0 = f32x16{};
     s1 = f32x16{};
 #pragma unroll
     for (int c = 0; c < G::NC; ++c) {
         if (c + 2 < G::NC) {
-            ka0[c + 2] = *(const bf16x8*)(Kt + koff[c + 2]);
-            ka1[c + 2] = *(const bf16x8*)(Kt + koff[c + 2] + 32 * G::ROW);
+            ka0[c + 2] = lds_b128(koff[c + 2] + Kt);
+            ka1[c + 2] = lds_b128(koff[c + 2] + Kt + 32 * G::ROW);
         }
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[c], qreg[c], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1[c], qreg[c], s1, 0, 0, 0);
@@ -124,35 +138,35 @@ __device__ __forceinline__ void scores(const char* Kt, const uint32_t (&koff)[Ge
 // operands) interleaved with the scores of the next tile.
 template <int D>
 __device__ __forceinline__ void exp_and_next(f32x16& s0, f32x16& s1, float nm, float sl2, float& l_i, bf16x8 (&pb)[4],
-                                             const char* Kn, const uint32_t (&koff)[Geo<D>::NC],
+                                             uint32_t Kn, const uint32_t (&koff)[Geo<D>::NC],
                                              const bf16x8 (&qreg)[Geo<D>::NC], f32x16& n0, f32x16& n1) {
     using G = Geo<D>;
     constexpr int PER = 16 / G::NC;   // registers of s0 (and of s1) per chunk of the next tile
     bf16x8 ka0[G::NC], ka1[G::NC];
-    ka0[0] = *(const bf16x8*)(Kn + koff[0]);
-    ka1[0] = *(const bf16x8*)(Kn + koff[0] + 32 * G::ROW);
-    ka0[1] = *(const bf16x8*)(Kn + koff[1]);
-    ka1[1] = *(const bf16x8*)(Kn + koff[1] + 32 * G::ROW);
+    ka0[0] = lds_b128(koff[0] + Kn);
+    ka1[0] = lds_b128(koff[0] + Kn + 32 * G::ROW);
+    ka0[1] = lds_b128(koff[1] + Kn);
+    ka1[1] = lds_b128(koff[1] + Kn + 32 * G::ROW);
     n0 = f32x16{};
     n1 = f32x16{};
-    float rs0 = 0.f, rs1 = 0.f;
+    float rs0, rs1;   // start from the first probability (no add of 0)
 #pragma unroll
     for (int c = 0; c < G::NC; ++c) {
         if (c + 2 < G::NC) {
-            ka0[c + 2] = *(const bf16x8*)(Kn + koff[c + 2]);
-            ka1[c + 2] = *(const bf16x8*)(Kn + koff[c + 2] + 32 * G::ROW);
+            ka0[c + 2] = lds_b128(koff[c + 2] + Kn);
+            ka1[c + 2] = lds_b128(koff[c + 2] + Kn + 32 * G::ROW);
         }
         n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[c], qreg[c], n0, 0, 0, 0);
 #pragma unroll
         for (int r = c * PER; r < c * PER + PER; ++r) {
             s0[r] = hw_exp2(fmaf(s0[r], sl2, nm));
-            rs0 += s0[r];
+            rs0 = r == 0 ? s0[r] : rs0 + s0[r];
         }
         n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1[c], qreg[c], n1, 0, 0, 0);
 #pragma unroll
         for (int r = c * PER; r < c * PER + PER; ++r) {
             s1[r] = hw_exp2(fmaf(s1[r], sl2, nm));
-            rs1 += s1[r];
+            rs1 = r == 0 ? s1[r] : rs1 + s1[r];
         }
         // keep the chunks in program order: the exponentials stay interleaved
         // with the matrix instructions instead of being hoisted ahead of them
@@ -176,17 +190,18 @@ __device__ __forceinline__ void exp_and_next(f32x16& s0, f32x16& s1, float nm, f
     }
 }
 
-// O^T += V^T P^T for one tile; Vt = V tile in LDS, voff = per-lane offsets of
-// the transposed reads for each 32-row d block.
+// O^T += V^T P^T for one tile; Vt = offset of the V tile in LDS (a constant
+// after inlining), voff = per-lane LDS addresses of the transposed reads for
+// each 32-row d block (slot 0).
 template <int D>
-__device__ __forceinline__ void accumulate_pv(const char* Vt, const uint32_t (&voff)[Geo<D>::NDB], const bf16x8 (&pb)[4],
+__device__ __forceinline__ void accumulate_pv(uint32_t Vt, const uint32_t (&voff)[Geo<D>::NDB], const bf16x8 (&pb)[4],
                                               f32x16 (&o)[Geo<D>::NDB]) {
     using G = Geo<D>;
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     auto v_load = [&](int db, int kc) -> bf16x8 {
-        const char* p0 = Vt + voff[db] + (16 * kc) * G::ROW;
-        const s16x4 r0 = tr_read(p0);
-        const s16x4 r1 = tr_read(p0 + 8 * G::ROW);
+        const uint32_t p0 = voff[db] + Vt + (16 * kc) * G::ROW;
+        const s16x4 r0 = lds_tr16(p0);
+        const s16x4 r1 = lds_tr16(p0 + 8 * G::ROW);
         const s16x8 a = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
         return __builtin_bit_cast(bf16x8, a);
     };
@@ -370,9 +385,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
 
     // ---- per-lane constants
     // LDS operand offsets (bytes within a tile)
+    // LDS byte address of the dynamic shared memory, folded into the per-lane
+    // operand addresses once
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
     uint32_t koff[G::NC];
 #pragma unroll
-    for (int c = 0; c < G::NC; ++c) koff[c] = l32 * G::ROW + 16 * ((2 * c + hh) ^ G::hk(l32));
+    for (int c = 0; c < G::NC; ++c) koff[c] = lds0 + l32 * G::ROW + 16 * ((2 * c + hh) ^ G::hk(l32));
     uint32_t voff[G::NDB];
     {
         const int jj = lane & 15, grp = lane >> 4;
@@ -381,7 +399,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db) {
             const int g = 4 * db + 2 * (grp & 1) + ((jj & 3) >> 1);
-            voff[db] = r0 * G::ROW + 16 * (g ^ hv) + 8 * (jj & 1);
+            voff[db] = lds0 + G::VBASE + r0 * G::ROW + 16 * (g ^ hv) + 8 * (jj & 1);
         }
     }
     // Tile loads: this wave moves load blocks w*NI .. w*NI+NI-1 of the K and V
@@ -395,18 +413,21 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
         dk[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ G::hk(row));
         dv[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ G::hv(row));
     }
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
     auto issue = [&](int i) {
         const int key0 = tile_at(i) * BN;
         // bytes up to the end of the tile's last key row; keys >= Tkv read as zeros
         const uint32_t nb = (uint32_t)min(Tkv - 1 - key0, BN - 1) * rs2 + 2u * D;
         const u32x4 rk = buffer_rsrc(kg + (long long)key0 * rs2, nb);
         const u32x4 rv = buffer_rsrc(vg + (long long)key0 * rs2, nb);
-        const uint32_t base = lds0 + (uint32_t)(i % NSLOT) * G::SLOT + (uint32_t)(w * G::NI) * 1024u;
+        // opaque per call: the per-slot bases are then formed here with scalar
+        // adds instead of being kept live (in spilled scalar registers) across the loop
+        uint32_t lw = lds0 + (uint32_t)(w * G::NI) * 1024u;
+        asm volatile("" : "+s"(lw));
+        const uint32_t base = lw + (uint32_t)(i % NSLOT) * G::TILE;
 #pragma unroll
         for (int n = 0; n < G::NI; ++n) load_lds16(dk[n], rk, base + 1024u * n);
 #pragma unroll
-        for (int n = 0; n < G::NI; ++n) load_lds16(dv[n], rv, base + G::TILE + 1024u * n);
+        for (int n = 0; n < G::NI; ++n) load_lds16(dv[n], rv, base + G::VBASE + 1024u * n);
     };
     const uint8_t* kpm_row = p.kpm ? p.kpm + b * p.kpm_bstride : nullptr;
     const uint8_t* am_row = (p.amask && qvalid) ? p.amask + (long long)qi * p.amask_stride : nullptr;
@@ -448,12 +469,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     } else {
         wait_barrier<0>();
     }
-    if (n_act > 0 && w_first == 0) scores<D>(smem, koff, qreg, s0, s1);
+    if (n_act > 0 && w_first == 0) scores<D>(G::kt(0), koff, qreg, s0, s1);
 
     // One tile: softmax of the scores in (c0, c1), scores of the next tile
     // into (x0, x1), O += V P.  Called with the two register sets swapped on
-    // alternate tiles, so no copy of the scores is needed.
-    auto step = [&](int i, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1) {
+    // alternate tiles, so no copy of the scores is needed; S = i % NSLOT is
+    // the tile's slot, a compile-time constant.
+    auto step = [&](auto S, int i, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1) {
+        constexpr int sl = decltype(S)::value, sn = (sl + 1) % NSLOT;
         const bool more = i + 3 < ntiles;
         if (more) issue(i + 3);
         if (i >= w_first && i < n_act) {
@@ -467,13 +490,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
             // not use them (last tile, or no allowed key for its rows): the
             // slot is always readable, and one code path keeps the registers
             // in budget.
-            exp_and_next<D>(c0, c1, nm, sl2, l_i, pb, smem + ((i + 1) % NSLOT) * G::SLOT, koff, qreg, x0, x1);
-            accumulate_pv<D>(smem + (i % NSLOT) * G::SLOT + G::TILE, voff, pb, o);
+            exp_and_next<D>(c0, c1, nm, sl2, l_i, pb, G::kt(sn), koff, qreg, x0, x1);
+            accumulate_pv<D>(G::vt(sl), voff, pb, o);
             __builtin_amdgcn_s_setprio(0);
         } else if constexpr (WIN) {
             if (i + 1 == w_first && w_first < n_act) {
                 // first tile of a wave whose window starts later: its scores only
-                scores<D>(smem + ((i + 1) % NSLOT) * G::SLOT, koff, qreg, x0, x1);
+                scores<D>(G::kt(sn), koff, qreg, x0, x1);
             }
         }
         // tile i + 2 resident for every wave; tile i + 3 may stay in flight
@@ -481,9 +504,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
         else wait_barrier<0>();
     };
     f32x16 n0, n1;
-    for (int i = 0; i < ntiles; i += 2) {
-        step(i, s0, s1, n0, n1);
-        if (i + 1 < ntiles) step(i + 1, n0, n1, s0, s1);
+    for (int i = 0; i < ntiles; i += NSLOT) {
+        static_assert(NSLOT == 4, "the loop below is unrolled once per slot");
+        step(IC<0>{}, i, s0, s1, n0, n1);
+        if (i + 1 < ntiles) step(IC<1>{}, i + 1, n0, n1, s0, s1);
+        if (i + 2 < ntiles) step(IC<2>{}, i + 2, s0, s1, n0, n1);
+        if (i + 3 < ntiles) step(IC<3>{}, i + 3, n0, n1, s0, s1);
     }
 
     // ---- epilogue: out = O / l, lse = ln(sum exp(scores)); optional merge into a partial
@@ -653,9 +679,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the table is written before it is read
 
     // ---- per-lane constants (as in attn_fwd_bf16_kernel)
+    // LDS byte address of the dynamic shared memory, folded into the per-lane
+    // operand addresses once
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
     uint32_t koff[G::NC];
 #pragma unroll
-    for (int c = 0; c < G::NC; ++c) koff[c] = l32 * G::ROW + 16 * ((2 * c + hh) ^ G::hk(l32));
+    for (int c = 0; c < G::NC; ++c) koff[c] = lds0 + l32 * G::ROW + 16 * ((2 * c + hh) ^ G::hk(l32));
     uint32_t voff[G::NDB];
     {
         const int jj = lane & 15, grp = lane >> 4;
@@ -664,7 +693,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db) {
             const int g = 4 * db + 2 * (grp & 1) + ((jj & 3) >> 1);
-            voff[db] = r0 * G::ROW + 16 * (g ^ hv) + 8 * (jj & 1);
+            voff[db] = lds0 + G::VBASE + r0 * G::ROW + 16 * (g ^ hv) + 8 * (jj & 1);
         }
     }
     uint32_t dk[G::NI], dv[G::NI];
@@ -676,7 +705,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
         dk[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ G::hk(row));
         dv[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(pos ^ G::hv(row));
     }
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
 
     // ---- load cursor: block ls, list position li of the next tile to load,
     // and that block's addressing (read from the kernel arguments and the
@@ -707,11 +735,15 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
         const uint32_t nbytes = (uint32_t)min(l_Tkv - 1 - key0, BN - 1) * rs2 + 2u * D;
         const u32x4 rk = buffer_rsrc(l_kg + (long long)key0 * rs2, nbytes);
         const u32x4 rv = buffer_rsrc(l_vg + (long long)key0 * rs2, nbytes);
-        const uint32_t base = lds0 + (uint32_t)(g % NSLOT) * G::SLOT + (uint32_t)(w * G::NI) * 1024u;
+        // opaque per call: the per-slot bases are then formed here with scalar
+        // adds instead of being kept live (in spilled scalar registers) across the loop
+        uint32_t lw = lds0 + (uint32_t)(w * G::NI) * 1024u;
+        asm volatile("" : "+s"(lw));
+        const uint32_t base = lw + (uint32_t)(g % NSLOT) * G::TILE;
 #pragma unroll
         for (int n = 0; n < G::NI; ++n) load_lds16(dk[n], rk, base + 1024u * n);
 #pragma unroll
-        for (int n = 0; n < G::NI; ++n) load_lds16(dv[n], rv, base + G::TILE + 1024u * n);
+        for (int n = 0; n < G::NI; ++n) load_lds16(dv[n], rv, base + G::VBASE + 1024u * n);
         if (++li >= l_ntl) load_skip();
     };
 
@@ -825,19 +857,20 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
     // epilogue after its last tile.
     f32x16 s0 = f32x16{}, s1 = f32x16{}, n0, n1;
     bool have = false;   // the scores of tile g are in the current register set
-    auto step = [&](int g, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1) __attribute__((always_inline)) {
+    auto step = [&](auto S, int g, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value, sn = (sl + 1) % NSLOT;   // slots of tiles g and g + 1
         const bool more = g + 3 < ntot;
         if (more) issue_next(g + 3);
         const bool act = ci < c_nact;
         if (act) {
-            if (!have) scores<D>(smem + (g % NSLOT) * G::SLOT, koff, qreg, c0, c1);
+            if (!have) scores<D>(G::kt(sl), koff, qreg, c0, c1);
             if (ci >= c_nfull) apply_mask(c0, c1, tile_mask(ci));
             update_max<D>(c0, c1, o, m_i, l_i, sl2);
             const float nm = (m_i == -INFINITY) ? 0.f : -m_i;
             bf16x8 pb[4];
             __builtin_amdgcn_s_setprio(1);
-            exp_and_next<D>(c0, c1, nm, sl2, l_i, pb, smem + ((g + 1) % NSLOT) * G::SLOT, koff, qreg, x0, x1);
-            accumulate_pv<D>(smem + (g % NSLOT) * G::SLOT + G::TILE, voff, pb, o);
+            exp_and_next<D>(c0, c1, nm, sl2, l_i, pb, G::kt(sn), koff, qreg, x0, x1);
+            accumulate_pv<D>(G::vt(sl), voff, pb, o);
             __builtin_amdgcn_s_setprio(0);
         }
         have = act;
@@ -859,9 +892,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
         else if (merged && wvalid) lds_barrier();
         else wait_barrier<PT>();
     };
-    for (int g = 0; g < ntot; g += 2) {
-        step(g, s0, s1, n0, n1);
-        if (g + 1 < ntot) step(g + 1, n0, n1, s0, s1);
+    for (int g = 0; g < ntot; g += NSLOT) {
+        static_assert(NSLOT == 4, "the loop below is unrolled once per slot");
+        step(IC<0>{}, g, s0, s1, n0, n1);
+        if (g + 1 < ntot) step(IC<1>{}, g + 1, n0, n1, s0, s1);
+        if (g + 2 < ntot) step(IC<2>{}, g + 2, s0, s1, n0, n1);
+        if (g + 3 < ntot) step(IC<3>{}, g + 3, n0, n1, s0, s1);
     }
 }
 

@@ -22,7 +22,7 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 // NaN-propagating maximum (v_maximum3_f32): unlike fmaxf it needs no operand
 // canonicalisation.  Scores are finite or -inf (excluded keys), where the two agree.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-__device__ __forceinline__ float max3(float a, float b, float c) { return vmax(a, vmax(b, c)); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -61,6 +61,16 @@ __device__ __forceinline__ void wait_barrier() {
 
 __device__ __forceinline__ s16x4 tr_read(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// LDS reads at an absolute LDS byte address.  A loop-invariant per-lane
+// address plus a compile-time constant becomes one ds_read with the constant
+// in its immediate offset (no address arithmetic per read).
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) bf16x8*)(size_t)addr;
+}
+__device__ __forceinline__ s16x4 lds_tr16(uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(size_t)addr);
 }
 
 
