@@ -29,10 +29,12 @@
 // the MFMA operand reads are free of LDS bank conflicts without padding.
 //
 // Schedule per tile i: issue the loads of tile i + 3; mask (only tiles that
-// are not entirely allowed) and row max of S_i; rescale if the max moved;
-// then S_{i+1} = K_{i+1} Q^T on the matrix cores interleaved with the
-// exponentials of S_i on the vector ALU; then O += V_i P_i; wait for tile
-// i + 2 and synchronise the workgroup.
+// are not entirely allowed); S_{i+1} = K_{i+1} Q^T on the matrix cores
+// interleaved with the exponentials of S_i against the row's reference max
+// on the vector ALU, and a check of the probabilities' sums (rarely out of
+// range: then the tile's scores are formed again and its row max moves the
+// reference); then O += V_i P_i; wait for tile i + 2 and synchronise the
+// workgroup.
 #include <type_traits>
 
 #include "tile_io.h"
@@ -45,11 +47,20 @@ constexpr int NW = 8;      // waves per workgroup, 32 query rows each
 constexpr int BM = 32 * NW;
 constexpr int NT = 64 * NW;
 constexpr int NSLOT = 4;   // LDS tile slots (tiles i .. i + 3)
-// Lazy rescale: the reference max of a row moves only when a tile's row max
-// exceeds it by more than this (log2 units), so probabilities stay <= 2^8
-// and the O/l rescale is almost never executed.  The result is the same up to
-// rounding for any reference.
-constexpr float kTau = 8.f;
+// Reference max of a row (log2 units): the row max of the tile with the
+// row's first allowed keys, then moved only when the probabilities leave the
+// range below (those tiles are processed again), so the other tiles take no
+// row max.  (0 until then.)
+// Bounds on a lane's probabilities against its row's reference max (log2
+// units).  A lane's tile sum (32 probabilities) above kSumMax means some
+// probability exceeded 2^16: the row's scores rose by more than 16 over the
+// reference, which must then move up.  A running sum below kSumMin means
+// every probability so far is below 2^-100, where float32 would soon lose
+// them to underflow: the reference moves down to the row max.  Between the
+// two, any reference gives the same result up to rounding.
+constexpr float kSumMax = 0x1p21f;
+constexpr float kSumMin = 0x1p-100f;
+
 
 template <int N>
 using IC = std::integral_constant<int, N>;
@@ -85,23 +96,39 @@ struct Geo {
     static __device__ __forceinline__ int hv(int r) { return 4 * ((r / RP) % (GPR / 4)); }
 };
 
-// Row max of the tile (scaled, log2 units) and the lazy move of the reference
-// max m_i with the matching rescale of O and l.
+// Pass 1 of a tile whose probabilities left their range on some lane, or
+// that holds a row's first allowed keys: set or move the reference max m_i
+// (log2 units) of each row that needs it, from row totals (the two
+// half-waves of a row keep one reference):
+//  - to the tile's row max mx for a row with nothing accumulated yet, so its
+//    largest probability is exactly 1 before its bf16 rounding;
+//  - up to mx when a probability exceeds 2^16 (mx > m_i + 16; every earlier
+//    probability was <= 2^16, so mx is the running max);
+//  - down when the row's running sum plus the tile's largest probability is
+//    still below kSumMin: to the larger of mx and the largest probability
+//    already accumulated (at most l above the reference).
+// Rows with no allowed key in the tile, and all other rows, keep their
+// reference, so a tile that changes no reference gives the same bits in
+// either pass, and fully masked tiles never change the state.
 template <int D>
-__device__ __forceinline__ void update_max(const f32x16& s0, const f32x16& s1, f32x16 (&o)[Geo<D>::NDB], float& m_i,
-                                           float& l_i, float sl2) {
-    // two independent chains of v_maximum3_f32
+__device__ __forceinline__ void remax(const f32x16& s0, const f32x16& s1, f32x16 (&o)[Geo<D>::NDB], float& m_i,
+                                      float& l_i, float sl2) {
     float ma = max3(s0[0], s0[1], s0[2]), mb = max3(s1[0], s1[1], s1[2]);
 #pragma unroll
     for (int r = 3; r < 15; r += 2) {
         ma = max3(ma, s0[r], s0[r + 1]);
         mb = max3(mb, s1[r], s1[r + 1]);
     }
-    float mx = max3(ma, mb, vmax(s0[15], s1[15]));
-    mx = xhalf_max(mx) * sl2;
-    if (__ballot(mx > m_i + kTau)) {
-        const float mnew = fmaxf(m_i, mx);
-        const float a = (mnew == -INFINITY) ? 1.f : hw_exp2(m_i - mnew);
+    const float mx = xhalf_max(max3(ma, mb, vmax(s0[15], s1[15]))) * sl2;
+    const float lrow = xhalf_sum(l_i);
+    float mnew = m_i;
+    if (mx > m_i + 16.f || (lrow == 0.f && mx > -INFINITY)) {
+        mnew = mx;
+    } else if (mx > -INFINITY && lrow + hw_exp2(mx - m_i) < kSumMin) {
+        mnew = fmaxf(mx, lrow > 0.f ? m_i + log2f(lrow) : -INFINITY);
+    }
+    if (mnew != m_i) {
+        const float a = l_i > 0.f ? hw_exp2(m_i - mnew) : 1.f;
         l_i *= a;
 #pragma unroll
         for (int db = 0; db < Geo<D>::NDB; ++db) o[db] *= a;
@@ -134,12 +161,13 @@ __device__ __forceinline__ void scores(uint32_t Kt, const uint32_t (&koff)[Geo<D
     }
 }
 
-// Probabilities of the current tile (in place, then packed to the bf16 P^T
-// operands) interleaved with the scores of the next tile.
+// Probabilities of the current tile, p = exp2(s sl2 + nm), in place of the
+// scores in s0, s1, with this lane's sum of them in rs, interleaved with the
+// scores of the next tile (K tile at LDS offset Kn into n0, n1).
 template <int D>
-__device__ __forceinline__ void exp_and_next(f32x16& s0, f32x16& s1, float nm, float sl2, float& l_i, bf16x8 (&pb)[4],
-                                             uint32_t Kn, const uint32_t (&koff)[Geo<D>::NC],
-                                             const bf16x8 (&qreg)[Geo<D>::NC], f32x16& n0, f32x16& n1) {
+__device__ __forceinline__ void exp_and_next(f32x16& s0, f32x16& s1, float nm, float sl2, float& rs, uint32_t Kn,
+                                             const uint32_t (&koff)[Geo<D>::NC], const bf16x8 (&qreg)[Geo<D>::NC],
+                                             f32x16& n0, f32x16& n1) {
     using G = Geo<D>;
     constexpr int PER = 16 / G::NC;   // registers of s0 (and of s1) per chunk of the next tile
     bf16x8 ka0[G::NC], ka1[G::NC];
@@ -172,8 +200,12 @@ __device__ __forceinline__ void exp_and_next(f32x16& s0, f32x16& s1, float nm, f
         // with the matrix instructions instead of being hoisted ahead of them
         __builtin_amdgcn_sched_barrier(0);
     }
-    l_i += rs0 + rs1;
-    // P^T operands: chunk (kb, cc) = accumulator registers 8cc .. 8cc+7
+    rs = rs0 + rs1;
+}
+
+// The probabilities in s0, s1 as the bf16 P^T operands: chunk (kb, cc) =
+// accumulator registers 8cc .. 8cc+7.
+__device__ __forceinline__ void pack_p(const f32x16& s0, const f32x16& s1, bf16x8 (&pb)[4]) {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
         uint4 u0, u1;
@@ -188,6 +220,30 @@ __device__ __forceinline__ void exp_and_next(f32x16& s0, f32x16& s1, float nm, f
         pb[cc] = __builtin_bit_cast(bf16x8, u0);
         pb[2 + cc] = __builtin_bit_cast(bf16x8, u1);
     }
+}
+
+// One tile's softmax update after its (masked) scores are in c0, c1.  Pass 0
+// takes no row max: the probabilities are formed against the reference max
+// and checked (tile sum <= kSumMax, running sum >= kSumMin, something
+// accumulated before).  Returns true when some lane fails (or a sum is not
+// finite): the caller then runs pass 1
+// on the same tile with its scores recomputed, where remax moves the
+// reference before the probabilities are formed again; pass 1 always ends
+// the tile.  On return the probabilities are in c0, c1 (their sum added to
+// l_i) and the next tile's scores (K at LDS offset Kn) in x0, x1.
+template <int D>
+__device__ __forceinline__ bool softmax_tile(int pass, f32x16& c0, f32x16& c1, f32x16 (&o)[Geo<D>::NDB], float& m_i,
+                                             float& l_i, float sl2, uint32_t Kn, const uint32_t (&koff)[Geo<D>::NC],
+                                             const bf16x8 (&qreg)[Geo<D>::NC], f32x16& x0, f32x16& x1) {
+    if (pass) remax<D>(c0, c1, o, m_i, l_i, sl2);
+    float rs;
+    exp_and_next<D>(c0, c1, -m_i, sl2, rs, Kn, koff, qreg, x0, x1);
+    const float l_new = l_i + rs;
+    // out of range, or nothing accumulated yet (a row's first allowed keys,
+    // or scores so far below the reference that they all vanished): pass 1
+    if (pass == 0 && __ballot(!(rs <= kSumMax && l_i > 0.f && l_new >= kSumMin))) return true;
+    l_i = l_new;
+    return false;
 }
 
 // O^T += V^T P^T for one tile; Vt = offset of the V tile in LDS (a constant
@@ -452,7 +508,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
         return mk;
     };
 
-    float m_i = -INFINITY;   // reference max of scaled scores (log2 units)
+    float m_i = 0.f;         // reference max of scaled scores (log2 units)
     float l_i = 0.f;         // running denominator (this half-wave's keys)
     f32x16 o[G::NDB];
 #pragma unroll
@@ -480,17 +536,24 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
         const bool more = i + 3 < ntiles;
         if (more) issue(i + 3);
         if (i >= w_first && i < n_act) {
-            if (!full_at(i)) apply_mask(c0, c1, tile_mask(i));
-            if (ALIBI) add_alibi(c0, c1, (float)((long long)qi + delta - (long long)tile_at(i) * BN - 4 * hh), ab);
-            update_max<D>(c0, c1, o, m_i, l_i, sl2);
-            const float nm = (m_i == -INFINITY) ? 0.f : -m_i;
-            bf16x8 pb[4];
+            auto mask_tile = [&]() __attribute__((always_inline)) {
+                if (!full_at(i)) apply_mask(c0, c1, tile_mask(i));
+                if (ALIBI) add_alibi(c0, c1, (float)((long long)qi + delta - (long long)tile_at(i) * BN - 4 * hh), ab);
+            };
+            mask_tile();
             __builtin_amdgcn_s_setprio(1);
             // The scores of tile i + 1 are computed even when this wave will
             // not use them (last tile, or no allowed key for its rows): the
             // slot is always readable, and one code path keeps the registers
             // in budget.
-            exp_and_next<D>(c0, c1, nm, sl2, l_i, pb, G::kt(sn), koff, qreg, x0, x1);
+            if (softmax_tile<D>(0, c0, c1, o, m_i, l_i, sl2, G::kt(sn), koff, qreg, x0, x1)) {
+                // pass 1 (rare): the scores again, from the K tile still in LDS
+                scores<D>(G::kt(sl), koff, qreg, c0, c1);
+                mask_tile();
+                softmax_tile<D>(1, c0, c1, o, m_i, l_i, sl2, G::kt(sn), koff, qreg, x0, x1);
+            }
+            bf16x8 pb[4];
+            pack_p(c0, c1, pb);
             accumulate_pv<D>(G::vt(sl), voff, pb, o);
             __builtin_amdgcn_s_setprio(0);
         } else if constexpr (WIN) {
@@ -780,7 +843,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
         return mk;
     };
 
-    float m_i = -INFINITY;
+    float m_i = 0.f;   // reference max (log2 units)
     float l_i = 0.f;
     f32x16 o[G::NDB];
 #pragma unroll
@@ -826,7 +889,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
                 if (hh == 0) *lse_ptr = lse_b;
             }
         }
-        m_i = -INFINITY;
+        m_i = 0.f;
         l_i = 0.f;
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db) o[db] = f32x16{};
@@ -865,11 +928,15 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
         if (act) {
             if (!have) scores<D>(G::kt(sl), koff, qreg, c0, c1);
             if (ci >= c_nfull) apply_mask(c0, c1, tile_mask(ci));
-            update_max<D>(c0, c1, o, m_i, l_i, sl2);
-            const float nm = (m_i == -INFINITY) ? 0.f : -m_i;
-            bf16x8 pb[4];
             __builtin_amdgcn_s_setprio(1);
-            exp_and_next<D>(c0, c1, nm, sl2, l_i, pb, G::kt(sn), koff, qreg, x0, x1);
+            if (softmax_tile<D>(0, c0, c1, o, m_i, l_i, sl2, G::kt(sn), koff, qreg, x0, x1)) {
+                // pass 1 (rare): the scores again, from the K tile still in LDS
+                scores<D>(G::kt(sl), koff, qreg, c0, c1);
+                if (ci >= c_nfull) apply_mask(c0, c1, tile_mask(ci));
+                softmax_tile<D>(1, c0, c1, o, m_i, l_i, sl2, G::kt(sn), koff, qreg, x0, x1);
+            }
+            bf16x8 pb[4];
+            pack_p(c0, c1, pb);
             accumulate_pv<D>(G::vt(sl), voff, pb, o);
             __builtin_amdgcn_s_setprio(0);
         }
