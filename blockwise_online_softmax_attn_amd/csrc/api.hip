@@ -290,6 +290,22 @@ int check_sizes(int B, int H, int Tq, int Tkv, int d) {
     return ATTN_OK;
 }
 
+}  // namespace
+
+// Slots per decoding chunk: enough chunks to fill the chip for any batch
+// (about 8192 (row, head, chunk) workgroups), each chunk at least four
+// workgroup iterations long.
+long long bosa::decode_chunk_size(long long Tcap, long long bh, int d, int is_bf16) {
+    const int epl = is_bf16 ? 8 : 4;   // elements per 16-byte load
+    const long long gran = (64 / (d / epl)) * kDecodeWaves * kDecodeUnroll;   // keys one iteration covers
+    const long long nch = (8192 + bh - 1) / bh;
+    long long CH = Tcap > 0 ? (Tcap + nch - 1) / nch : gran;
+    CH = (CH + gran - 1) / gran * gran;
+    return CH < 4 * gran ? 4 * gran : CH;
+}
+
+namespace {
+
 // The bf16 kernel addresses one 64-key tile of a head with 32-bit byte
 // offsets: 64 rows of H * d bf16 values must stay below 4 GiB.
 int check_bf16_rows(int dtype, int H, int d) {

@@ -227,7 +227,12 @@ struct DecodeParams {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_fwd_bf16_chain(const ChainParams& c, int d, hipStream_t s);
-long long decode_chunk_size(long long Tcap, long long bh, int d, int is_bf16);
+// Decoding splits each row's slots into chunks of a multiple of the keys one
+// workgroup iteration covers: (64 lanes / lanes per key row) key groups per
+// wave x kDecodeWaves waves x kDecodeUnroll keys per group.
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeUnroll = 4;
+long long decode_chunk_size(long long Tcap, long long bh, int d, int is_bf16);   // host code (api.hip)
 hipError_t launch_decode_chunks(const DecodeParams& p, int d, int is_bf16, hipStream_t s);
 // The per-device static workspace of attn_decode_noalloc (kDecodeStaticBytes
 // bytes): its device address on the current device (looked up on the first

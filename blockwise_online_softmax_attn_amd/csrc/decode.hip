@@ -24,9 +24,9 @@
 namespace bosa {
 namespace {
 
-constexpr int DW = 4;        // waves per decode workgroup
-constexpr int DT = 64 * DW;  // threads
-constexpr int DU = 4;        // keys per group per iteration
+constexpr int DW = kDecodeWaves;    // waves per decode workgroup
+constexpr int DT = 64 * DW;         // threads
+constexpr int DU = kDecodeUnroll;   // keys per group per iteration
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 template <typename T>
@@ -308,16 +308,6 @@ hipError_t decode_static_workspace(void** ptr) {
     }
     *ptr = a;
     return hipSuccess;
-}
-
-long long decode_chunk_size(long long Tcap, long long bh, int d, int is_bf16) {
-    const int epl = is_bf16 ? 8 : 4;
-    const long long gran = (64 / (d / epl)) * DW * DU;   // keys one workgroup iteration covers
-    // enough workgroups to fill the chip for any batch, at least 4 iterations each
-    const long long nch = (8192 + bh - 1) / bh;
-    long long CH = Tcap > 0 ? (Tcap + nch - 1) / nch : gran;
-    CH = (CH + gran - 1) / gran * gran;
-    return CH < 4 * gran ? 4 * gran : CH;
 }
 
 hipError_t launch_decode_chunks(const DecodeParams& p, int d, int is_bf16, hipStream_t s) {
