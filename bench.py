@@ -38,6 +38,15 @@ targets = the default run (workload 4, forward) also times workloads 2 (the
          >= 50 % of peak target, by the same method, each in a child process
          started before this one initialises the GPU: step and kernel-only
          TFLOP/s with their fractions of the peak.  --no-targets skips them.
+mfma_sustained = the default run also runs the matrix-core rate probe
+         (probe/mfma_rate, built with the library) first: a stream of
+         independent bf16 MFMAs with no memory traffic, held for a few
+         seconds, once with standard-normal and once with zero operands.  Under
+         sustained load the board holds its power cap by lowering the shader
+         clock, so this is the rate a kernel doing nothing but matrix work
+         sustains on this board; the attention kernel's rate is also given as
+         a fraction of it.  The roofline's peak stays the published one.
+         --no-yardstick skips it.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -457,6 +466,21 @@ def target_lines(args) -> dict:
     return out
 
 
+def mfma_yardstick() -> dict:
+    """The sustained matrix-core rate probe, run as a child process before
+    this process initialises the GPU."""
+    import subprocess
+    from blockwise_online_softmax_attn_amd import _build
+    if not os.path.exists(_build.PROBE):
+        return {"error": "probe not built (run __graft_entry__.build())"}
+    log(f"matrix-core rate probe: {_build.PROBE}")
+    r = subprocess.run([_build.PROBE], stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    if r.returncode != 0 or not lines:
+        return {"error": f"exit status {r.returncode}: {r.stderr.strip()[-200:]}"}
+    return json.loads(lines[-1])
+
+
 # ---------------------------------------------------------------- decoding
 def run_decode(args, w) -> dict:
     """One decoding step per iteration over a static cache of w.T slots per
@@ -623,6 +647,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-targets", action="store_true",
                     help="skip the extra forward workloads (2 and 3) the default run times in child processes")
+    ap.add_argument("--no-yardstick", action="store_true",
+                    help="skip the sustained matrix-core rate probe the default run starts with")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--graph", action="store_true",
@@ -646,6 +672,9 @@ def main() -> int:
     # the default run also times workloads 2 and 3, in child processes started
     # before this process initialises the GPU
     targets = None
+    yardstick = None
+    if args.which == "fwd" and args.workload == 4 and not args.no_yardstick:
+        yardstick = mfma_yardstick()
     if args.which == "fwd" and args.workload == 4 and not args.no_targets:
         targets = target_lines(args)
     if not torch.cuda.is_available():
@@ -763,6 +792,11 @@ def main() -> int:
         line["graph"] = graph
     if targets is not None:
         line["targets"] = targets
+    if yardstick is not None:
+        rate = yardstick.get("normal_operands_tflops")
+        if rate and achieved:
+            yardstick["kernel_frac_of_normal_operand_rate"] = achieved / rate
+        line["mfma_sustained"] = yardstick
     clock = line["clock"]
     if clock and w.dtype == "bf16":
         # the same MFMA rate per clock at the clock the work ran at

@@ -1,4 +1,6 @@
-"""Build libattn.so (gfx950) from csrc/*.hip with hipcc.
+"""Build libattn.so (gfx950) from csrc/*.hip with hipcc, and the matrix-core
+rate probe (probe/mfma_rate.hip, a stand-alone program bench.py runs as a
+yardstick) next to its source.
 
 Every call recompiles.  Objects go to <repo>/_build/, the shared library to
 this package directory, where the ctypes binding loads it.
@@ -15,6 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "libattn.so")
+PROBE_SRC = os.path.join(PKG, "probe", "mfma_rate.hip")
+PROBE = os.path.join(PKG, "probe", "mfma_rate")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = "gfx950"
@@ -45,15 +49,18 @@ def build(verbose: bool = False) -> str:
     for f in srcs:
         obj = os.path.join(BUILD, f[:-4] + ".o")
         jobs.append((obj, [HIPCC, *CFLAGS, "-c", os.path.join(SRC, f), "-o", obj]))
+    jobs.append((PROBE + ".tmp", [HIPCC, *CFLAGS, "-o", PROBE + ".tmp", PROBE_SRC]))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         for (obj, cmd), warn in zip(jobs, ex.map(lambda j: _run(j[1]), jobs)):
             if verbose and warn.strip():
                 print(warn, file=sys.stderr)
+    shutil.move(PROBE + ".tmp", PROBE)
+    jobs.pop()
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in jobs]])
     shutil.move(tmp, LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE}")
     return LIB
 
 
