@@ -379,15 +379,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
 // (w >= 4) computes dP = dO V^T, dS = P (dP - delta) and dK^T += Q^T dS,
 // taking P (float32) from wave A through LDS.  Each wave holds one operand
 // (K or V) and one accumulator (dV^T or dK^T), so two waves fit per SIMD;
-// waves w and w + 4 share a SIMD, one of each role.
+// waves w and w + 4 share a SIMD, one of each role.  Wave B runs one query
+// tile behind wave A: in loop step t, A works on tile t and B on tile t - 1,
+// whose P A wrote in step t - 1 (two exchange buffers, by tile parity), so the
+// one workgroup barrier that ends a step both publishes P and frees the tile
+// slot B has finished with.
 template <int D, bool VAR>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     using G = BG<D>;
     constexpr int NW = 8, BK = 128, BQ = 32, NSL = 6;
     constexpr int QTILE = BQ * G::ROW;           // bytes of one 32-row tile
-    constexpr int LDO = 2 * QTILE;               // (lse2, delta) of the tile after the two copies
+    constexpr int LDO = 2 * QTILE;               // lse2[32] then delta[32] of the tile after the two copies
     constexpr int SLOT = 2 * QTILE + 256;        // Q | dO | 32 x float2
-    constexpr int XCH = NSL * SLOT;              // P exchange after the slots: 4 blocks x 4 KB
+    constexpr int XCH = NSL * SLOT;              // P exchange after the slots: 2 buffers x 4 blocks x 4 KB
     constexpr int NBLK = QTILE / 1024;           // 1 KB blocks per copy
     constexpr int PW = 2 * NBLK / NW;            // blocks per wave per tile (all in one copy)
     constexpr int PT = PW + 1;                   // loads per wave per tile
@@ -483,28 +487,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
         for (int n = 0; n < PW; ++n) load_lds16(dofs[n], r, base + 1024u * n);
         // (lse2, delta) of the 32 rows: 64 floats, 8 per wave
         const u32x4 rl = buffer_rsrc(ldg + qa, (uint32_t)min(Tq - qa, BQ) * 8u);
-        if (lane < 8) load_lds4((uint32_t)(8 * w + lane) * 4u, rl, slot + LDO + 32u * w);
+        // (rows of ld2 are float2 (lse2, delta); waves 0-3 move the lse2 of
+        // rows 8w .. 8w + 7, waves 4-7 the delta of rows 8(w - 4) ..)
+        if (lane < 8) load_lds4((uint32_t)(8 * (8 * (w & 3) + lane) + 4 * (w >> 2)), rl, slot + LDO + 32u * w);
     };
-    // P exchange block of this key block: [register group j][lane][4 floats]
-    float4* xch = (float4*)(smem + XCH + 4096 * kb) + lane;
+    // P exchange block of this key block in buffer par: [register group j][lane][4 floats]
+    auto xch_of = [&](int par) -> float4* { return (float4*)(smem + XCH + 16384 * par + 4096 * kb) + lane; };
 
     f32x16 acc[G::NDB];   // dV^T (wave A) or dK^T (wave B); lane = key
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) acc[db] = f32x16{};
 
     const int ntl = t_end - t0;
-    // tiles t + 1 .. t + NSL - 1 are loaded while tile t is processed
-    for (int i = 0; i < NSL - 1 && i < ntl; ++i) issue(t0 + i);
-    wait_tiles<PT, NSL - 2>(min(NSL - 2, ntl - 1));
-    for (int t = t0; t < t_end; ++t) {
-        if (t + NSL - 1 < t_end) issue(t + NSL - 1);
-        const bool act = wactive && t >= tw0 && t < tw_end;   // the same for both waves of a key block
-        const char* St = smem + slot_of(t) * SLOT;
-        const float4* lp = (const float4*)(St + LDO);
+    // Tile t is read by wave A in step t and by wave B in step t + 1; tiles
+    // t + 1 .. t + NSL - 2 are loaded during step t, into the slot of tile
+    // t - 2, which B finished with in step t - 1.
+    for (int i = 0; i < NSL - 2 && i < ntl; ++i) issue(t0 + i);
+    wait_tiles<PT, NSL - 3>(min(NSL - 3, ntl - 1));
+    for (int t = t0; ntl > 0 && t <= t_end; ++t) {
+        if (t + NSL - 2 < t_end) issue(t + NSL - 2);
+        const int tt = roleA ? t : t - 1;   // this wave's tile
+        const bool act = wactive && tt >= tw0 && tt < tw_end;   // for tile tt, the same for both waves of a key block
+        const char* St = smem + slot_of(max(tt, 0)) * SLOT;
+        float4* xch = xch_of(tt & 1);
+        // lse2 (wave A) or delta (wave B) of this lane's query rows 8 j + 4 hh .. + 3
+        const float4* lp = (const float4*)(St + LDO + (roleA ? 0 : 128));
         f32x16 x = f32x16{};   // S (wave A) or dP (wave B): lane = key, register r = query 8 (r/4) + 4 hh + r%4
         constexpr int NJ = 2 * G::NDB;
         bf16x8 ta[NJ];         // transposed operand of the second product (dO^T or Q^T)
-        float4 la[4], lc[4];   // (lse2, delta) pairs of this lane's query rows
+        float4 lr[4];          // lse2 (wave A) or delta (wave B) of rows 8 j + 4 hh + (0 .. 3)
         if (act) {
             // every LDS operand of this tile is requested before the first
             // matrix instruction, so the reads overlap the products
@@ -515,8 +526,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
             for (int c = 0; c < G::NC; ++c) ra[c] = *(const bf16x8*)(rows + roff[c]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                la[j] = lp[4 * j + 2 * hh];
-                lc[j] = lp[4 * j + 2 * hh + 1];
+                lr[j] = lp[2 * j + hh];
             }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) ta[j] = tr_operand<D>(trt, toff[j % G::NDB], j / G::NDB);
@@ -526,13 +536,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
             if (roleA) {
                 if (VAR && p.alibi) {
                     // penalty ab |pos_q - pos_k| on every score of the tile
-                    const float base = (float)((long long)t * BQ + 4 * hh + delta - kj);
+                    const float base = (float)((long long)tt * BQ + 4 * hh + delta - kj);
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         x[r] = fmaf(fabsf(base + (float)(8 * (r >> 2) + (r & 3))), ab, x[r]);
                 }
-                if (t < tf || t >= tf_hi || t >= tail) {
-                    const int qa = t * BQ;
+                if (tt < tf || tt >= tf_hi || tt >= tail) {
+                    const int qa = tt * BQ;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int qi = qa + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -547,25 +557,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
                 // P = exp2(s sl2 - lse2) with the row's lse2
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    x[4 * j + 0] = hw_exp2(fmaf(x[4 * j + 0], sl2, -la[j].x));
-                    x[4 * j + 1] = hw_exp2(fmaf(x[4 * j + 1], sl2, -la[j].z));
-                    x[4 * j + 2] = hw_exp2(fmaf(x[4 * j + 2], sl2, -lc[j].x));
-                    x[4 * j + 3] = hw_exp2(fmaf(x[4 * j + 3], sl2, -lc[j].z));
+                    x[4 * j + 0] = hw_exp2(fmaf(x[4 * j + 0], sl2, -lr[j].x));
+                    x[4 * j + 1] = hw_exp2(fmaf(x[4 * j + 1], sl2, -lr[j].y));
+                    x[4 * j + 2] = hw_exp2(fmaf(x[4 * j + 2], sl2, -lr[j].z));
+                    x[4 * j + 3] = hw_exp2(fmaf(x[4 * j + 3], sl2, -lr[j].w));
                     xch[64 * j] = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
                 }
             }
         }
-        lds_barrier();   // P of every key block is in LDS
         if (act) {
             if (!roleA) {
                 // dS = P (dP - delta)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float4 pr = xch[64 * j];
-                    x[4 * j + 0] = pr.x * (x[4 * j + 0] - la[j].y);
-                    x[4 * j + 1] = pr.y * (x[4 * j + 1] - la[j].w);
-                    x[4 * j + 2] = pr.z * (x[4 * j + 2] - lc[j].y);
-                    x[4 * j + 3] = pr.w * (x[4 * j + 3] - lc[j].w);
+                    x[4 * j + 0] = pr.x * (x[4 * j + 0] - lr[j].x);
+                    x[4 * j + 1] = pr.y * (x[4 * j + 1] - lr[j].y);
+                    x[4 * j + 2] = pr.z * (x[4 * j + 2] - lr[j].z);
+                    x[4 * j + 3] = pr.w * (x[4 * j + 3] - lr[j].w);
                 }
             }
             // dV^T += dO^T P (wave A) or dK^T += Q^T dS (wave B)
@@ -574,7 +583,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
             for (int j = 0; j < NJ; ++j)
                 acc[j % G::NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[j], xb[j / G::NDB], acc[j % G::NDB], 0, 0, 0);
         }
-        wait_tiles<PT, NSL - 2>(min(t + NSL - 1, t_end - 1) - (t + 1));
+        // tile t + 1 resident for A's next step (B's, tile t, already is); the
+        // barrier also publishes this step's P
+        wait_tiles<PT, NSL - 3>(min(t + NSL - 2, t_end - 1) - (t + 1));
     }
 
     if (!kvalid) return;
@@ -708,7 +719,7 @@ hipError_t launch_dq(const BwdParams& p, hipStream_t s) {
 
 template <int D, bool VAR>
 hipError_t launch_dkdv(const BwdParams& p, hipStream_t s) {
-    constexpr int BK = 128, LDS = 6 * (2 * 32 * 2 * D + 256) + 4 * 4096;
+    constexpr int BK = 128, LDS = 6 * (2 * 32 * 2 * D + 256) + 2 * 4 * 4096;
     static std::atomic<uint64_t> lds_set{0};
     if (hipError_t e = set_lds_limit((const void*)bwd_dkdv_kernel<D, VAR>, LDS, lds_set); e != hipSuccess) return e;
     BwdParams q = p;
