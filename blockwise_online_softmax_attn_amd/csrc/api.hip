@@ -724,15 +724,17 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
     }
     bool covered[2] = {false, false};
     // bf16 without a window or ALiBi: a query block's sub-calls run in plan
-    // order, several to a launch of the chained kernel, with the same
-    // per-block partials and merges as one launch per sub-call.  A chain ends
-    // after kMaxChain blocks, and after a block that causal order cuts through
-    // the query block when the launch runs its workgroups in more than one
-    // round per CU: those workgroups finish that block at different times,
-    // and a new launch lines them up again, so the workgroups of one head keep
-    // reading the same key tiles at about the same time.  With a single round
-    // (the 8K share) there is no later round to fall out of step, and going
-    // on in the same launch was 4.7% faster there.
+    // order, several to a launch of the chained kernel, which carries each
+    // row's softmax state across the sub-calls of the launch and writes or
+    // merges one partial per launch; the query block's last launch writes the
+    // final bf16 output itself (no cast pass).  A chain ends after kMaxChain
+    // blocks, and after a block that causal order cuts through the query
+    // block when the launch runs its workgroups in more than one round per
+    // CU: those workgroups finish that block at different times, and a new
+    // launch lines them up again, so the workgroups of one head keep reading
+    // the same key tiles at about the same time.  With a single round (the 8K
+    // share) there is no later round to fall out of step, and going on in the
+    // same launch was 4.7% faster there.
     if (chain) {
         for (int i = 0; i < n_live; ++i)
             if (kpm_list_bytes(calls[i]))
@@ -753,6 +755,8 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
                 }
                 ChainParams cpm{};
                 cpm.p = fwd_params(calls[idx[j0]]);
+                if (j0 + n1 == idx.size())   // the query block's last launch
+                    cpm.out_bf16 = (uint16_t*)out + (size_t)plan[idx[j0]].q_row0 * rs;
                 cpm.nblk = (int)n1;
                 for (int j = 0; j < cpm.nblk; ++j) {
                     const Call& c = calls[idx[j0 + j]];
@@ -779,15 +783,22 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
             covered[plan[i].q_row0 == 0 ? 0 : 1] = true;
         }
     }
-    // rows no sub-call reached (not possible with a causal diagonal, kept for safety)
+    // rows no sub-call reached (not possible with a causal diagonal, kept for
+    // safety): the empty result, in out directly on the chained path (whose
+    // launches wrote the rest of out), else in acc before the cast
     const int parts = zigzag ? 2 : 1;
     for (int ph = 0; ph < parts; ++ph) {
         if (covered[ph]) continue;
         const int c = Tl / parts;
-        err = launch_fill_empty(acc + (size_t)ph * c * rs, 0, lse + (size_t)ph * c, B, H, c, d, (long long)Tl * rs, rs,
-                                (long long)H * Tl, Tl, s);
+        if (chain)
+            err = launch_fill_empty((uint16_t*)out + (size_t)ph * c * rs, 1, lse + (size_t)ph * c, B, H, c, d,
+                                    (long long)Tl * rs, rs, (long long)H * Tl, Tl, s);
+        else
+            err = launch_fill_empty(acc + (size_t)ph * c * rs, 0, lse + (size_t)ph * c, B, H, c, d, (long long)Tl * rs,
+                                    rs, (long long)H * Tl, Tl, s);
         if (err != hipSuccess) return hip_fail(err, "fill launch");
     }
+    if (chain) return ATTN_OK;
     const long long nel = (long long)B * Tl * rs;
     if (dtype == ATTN_F32 && (void*)acc == out) return ATTN_OK;
     err = launch_cast(acc, out, nel, dtype == ATTN_BF16, s);

@@ -148,10 +148,13 @@ struct ChainBlock {
                                // ceil(Tkv / 64) + 2 entries per batch row), or null
     long long kv_off;          // absolute position of the block's first key
     int Tkv;                   // keys in the block
-    int accumulate;            // 0: write the block's partial; 1: merge it into out / lse
+    int accumulate;            // the first block: 0 = the launch writes its partial, 1 = merges it into
+                               // out / lse (later blocks of a launch continue the same softmax state)
 };
 struct ChainParams {
-    FwdParams p;               // q (rotated), out (float32), lse, strides, B, H, Tq, q_off, causal, flags
+    FwdParams p;               // q (rotated), out (float32 accumulator), lse, strides, B, H, Tq, q_off, causal, flags
+    uint16_t* out_bf16;        // null, or the final bf16 output (the layout of out): the launch merges and
+                               // writes there instead of into out
     int nblk;
     ChainBlock blk[kMaxChain];
 };

@@ -637,11 +637,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
 // one launch.  Each workgroup keeps its 256 query rows (Q in registers) and
 // runs the tile pipeline of attn_fwd_bf16_kernel over the concatenation of
 // every block's live tiles, so the loads of a block's first tiles overlap the
-// last tiles of the block before; after a block's last tile each wave writes
-// that block's partial (out, lse) or merges it into the float32 partial (the
-// same epilogue as one launch per block), then starts the next block from an
-// empty state.  The results are those of one attn_fwd_bf16_kernel launch per
-// block, bit for bit.  No window, ALiBi or attention mask.
+// last tiles of the block before.  The rows' softmax state runs on across the
+// blocks (each block keeps its own positions, causal bound and key padding),
+// so the launch's blocks act as one key sequence: after the last tile each
+// wave writes that partial (out, lse) to the float32 accumulator, or merges
+// it into the partial a previous launch left there, or, for the last launch
+// of the query block, merges and writes the final output in bf16.  No window,
+// ALiBi or attention mask.
 template <int D>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainParams cp) {
     using G = Geo<D>;
@@ -849,60 +851,50 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) o[db] = f32x16{};
 
-    // partial of block s from (m_i, l_i, o), then the empty state
+    // the launch's partial from (m_i, l_i, o): written to the float32
+    // accumulator (the query block's first launch), merged into it, or merged
+    // and written as the final bf16 output (cp.out_bf16, same layout)
     float* lse_ptr = p.lse + b * p.lse_bstride + (long long)h * p.lse_hstride + qi;
-    float* og = (float*)p.out + b * p.o_bstride + (long long)qi * rs + (long long)h * D;
-    auto finish_block = [&](int s) __attribute__((always_inline)) {
+    const long long orow = b * p.o_bstride + (long long)qi * rs + (long long)h * D;
+    auto finish_chain = [&]() __attribute__((always_inline)) {
         const float lsum = xhalf_sum(l_i);
-        if (qvalid) {
-            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-            const float lse_b = lsum > 0.f ? (m_i + log2f(lsum)) * kLn2 : -INFINITY;
-            if (cp.blk[s].accumulate) {
-                const float la = *lse_ptr;
-                float lse_n, wa, wb;
-                merge_weights(la, lse_b, lse_n, wa, wb);
+        if (!qvalid) return;
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        const float lse_b = lsum > 0.f ? (m_i + log2f(lsum)) * kLn2 : -INFINITY;
+        const bool acc_in = cp.blk[0].accumulate != 0;
+        float* og = (float*)p.out + orow;
+        uint16_t* ob = cp.out_bf16 ? cp.out_bf16 + orow : nullptr;
+        float lse_n = lse_b, wa = 0.f, wb = 1.f;
+        if (acc_in) merge_weights(*lse_ptr, lse_b, lse_n, wa, wb);
 #pragma unroll
-                for (int db = 0; db < G::NDB; ++db) {
+        for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float4* dst = (float4*)(og + db * 32 + 8 * g + 4 * hh);
-                        const float4 oa = *dst;
-                        float4 r;
-                        r.x = merge_value(wa, oa.x, wb, o[db][4 * g + 0] * inv);
-                        r.y = merge_value(wa, oa.y, wb, o[db][4 * g + 1] * inv);
-                        r.z = merge_value(wa, oa.z, wb, o[db][4 * g + 2] * inv);
-                        r.w = merge_value(wa, oa.w, wb, o[db][4 * g + 3] * inv);
-                        *dst = r;
-                    }
+            for (int g = 0; g < 4; ++g) {
+                const int c = db * 32 + 8 * g + 4 * hh;
+                float4 r = make_float4(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                                       o[db][4 * g + 3] * inv);
+                if (acc_in) {
+                    const float4 oa = *(const float4*)(og + c);
+                    r.x = merge_value(wa, oa.x, wb, r.x);
+                    r.y = merge_value(wa, oa.y, wb, r.y);
+                    r.z = merge_value(wa, oa.z, wb, r.z);
+                    r.w = merge_value(wa, oa.w, wb, r.w);
                 }
-                if (hh == 0) *lse_ptr = lse_n;
-            } else {
-#pragma unroll
-                for (int db = 0; db < G::NDB; ++db) {
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float4 r = make_float4(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv,
-                                               o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                        *(float4*)(og + db * 32 + 8 * g + 4 * hh) = r;
-                    }
+                if (ob) {
+                    *(uint2*)(ob + c) = make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
+                } else {
+                    *(float4*)(og + c) = r;
                 }
-                if (hh == 0) *lse_ptr = lse_b;
             }
         }
-        m_i = 0.f;
-        l_i = 0.f;
-#pragma unroll
-        for (int db = 0; db < G::NDB; ++db) o[db] = f32x16{};
+        if (hh == 0) *lse_ptr = lse_n;
     };
-    // blocks without a live tile for this workgroup: their (empty) partials
-    auto finish_empty_blocks = [&]() __attribute__((always_inline)) {
-        while (cs < nb && tab[cs] == 0) {
-            finish_block(cs);
-            ++cs;
-        }
+    // past blocks without a live tile for this workgroup
+    auto skip_empty_blocks = [&]() __attribute__((always_inline)) {
+        while (cs < nb && tab[cs] == 0) ++cs;
         if (cs < nb) enter(cs);
     };
-    finish_empty_blocks();
+    skip_empty_blocks();
 
     // ---- prologue: tiles 0..2 in flight, tiles 0 and 1 resident
     constexpr int PT = 2 * G::NI;
@@ -916,8 +908,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
     }
 
     // One tile (global index g): as in attn_fwd_bf16_kernel, plus the scores
-    // of the tile when the wave skipped the tile before it, and the block's
-    // epilogue after its last tile.
+    // of the tile when the wave skipped the tile before it, and the move to
+    // the next block after a block's last tile.
     f32x16 s0 = f32x16{}, s1 = f32x16{}, n0, n1;
     bool have = false;   // the scores of tile g are in the current register set
     auto step = [&](auto S, int g, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1) __attribute__((always_inline)) {
@@ -941,22 +933,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
             __builtin_amdgcn_s_setprio(0);
         }
         have = act;
-        bool merged = false;
         if (++ci == c_ntl) {
-            merged = cp.blk[cs].accumulate != 0;
-            finish_block(cs);
             ++cs;
             ci = 0;
-            finish_empty_blocks();
+            skip_empty_blocks();
         }
-        // After a merge the epilogue of a wave with a valid row has waited
-        // for its own loads of the partial, so every older tile load of that
-        // wave is complete too; its stores may drain during the next tile (the
-        // next wait covers them).  A wave whose rows all lie past Tq skipped
-        // that epilogue, so it waits for its tile loads here (wvalid and
-        // merged are the same for every lane of the wave).
         if (!more) wait_barrier<0>();
-        else if (merged && wvalid) lds_barrier();
         else wait_barrier<PT>();
     };
     for (int g = 0; g < ntot; g += NSLOT) {
@@ -966,6 +948,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
         if (g + 2 < ntot) step(IC<2>{}, g + 2, s0, s1, n0, n1);
         if (g + 3 < ntot) step(IC<3>{}, g + 3, n0, n1, s0, s1);
     }
+    finish_chain();
 }
 
 template <int D, bool ALIBI, bool WIN>

@@ -319,12 +319,15 @@ int attn_ring_plan(int T, int P, int rank, int zigzag, int causal, attn_ring_cal
  *             (may equal out when dtype is ATTN_F32).
  *  kpm        device uint8 (B, T) or NULL, over absolute key positions.
  *  Other arguments as attn_fwd.  The work is the sub-calls of attn_ring_plan,
- *  issued in order on `stream`, then one attn_cast of acc into out.  In bf16
- *  (without window or ALiBi) up to four consecutive sub-calls of one query
- *  block run in one kernel launch, with each sub-call's partial written or
- *  merged exactly as by its own launch: out and lse are bit for bit those of
- *  one attn_fwd call per sub-call.  With RoPE the call rotates every key
- *  block and the local queries once into scratch copies.
+ *  issued in order on `stream`, each writing or merging its partial into acc,
+ *  then one attn_cast of acc into out.  In bf16 (without window or ALiBi) up
+ *  to four consecutive sub-calls of one query block run in one kernel launch
+ *  that carries each row's softmax state across them (so they act as one key
+ *  sequence in ring order) and writes or merges one partial per launch; the
+ *  last launch of a query block writes out directly.  out and lse then equal
+ *  one attn_fwd call per launch over that launch's keys in ring order, and
+ *  one attn_fwd call per sub-call up to rounding.  With RoPE the call rotates
+ *  every key block and the local queries once into scratch copies.
  * Scratch:    with rope_base > 0, the float64 (cos, sin) table over the T
  *             positions, T * (d/2) * 16; in bf16 also the rotated keys and
  *             local queries, 2 * B * (T + T/P) * H * d.  In bf16 with kpm

@@ -74,3 +74,90 @@ def compare(out, lse, ref_out, ref_lse, dtype: str, what: str = ""):
     assert eo <= tol_o, f"{what}: out error {eo} > {tol_o}"
     assert el <= tol_l, f"{what}: lse error {el} > {tol_l}"
     return eo, el
+
+
+CHAIN_MAX = 4      # sub-calls per launch of the chained ring executor
+CHAIN_ROWS = 256   # query rows per workgroup of that launch
+
+
+def ring_chains(plan, B, H, causal, n_cu):
+    """The launches of the chained ring executor (bf16, no window or ALiBi):
+    per query block, its sub-calls in plan order, at most CHAIN_MAX to a
+    launch, and a launch also ends after a sub-call that causal order cuts
+    through the query block when the launch has more workgroups than the
+    device has CUs.  Returns lists of plan entries."""
+    chains = []
+    for ph in (0, 1):
+        sub = [e for e in plan if (0 if e.q_row0 == 0 else 1) == ph]
+        cur = []
+        for e in sub:
+            cur.append(e)
+            wgs = B * H * -(-e.q_rows // CHAIN_ROWS)
+            cut = causal and wgs > n_cu and e.kv_pos0 + e.kv_rows - 1 > e.q_pos0
+            if len(cur) == CHAIN_MAX or cut:
+                chains.append(cur)
+                cur = []
+        if cur:
+            chains.append(cur)
+    return chains
+
+
+def chained_ring_reference(q, k, v, kpm, P, rank, zigzag, causal, rope):
+    """What attn_ring_fwd's chained executor computes, rebuilt from plain
+    attn_fwd calls: each launch's blocks act as one key sequence, so each
+    launch becomes one attn_fwd over its blocks' keys concatenated in ring
+    order, each block padded to whole 64-key tiles with excluded zero keys
+    (as the executor's tiles are), with causal order as an attention mask over
+    absolute positions and the rotations applied beforehand by rope_apply;
+    launches after a query block's first merge into its float32 partial, then
+    one cast.  Equal to the executor bit for bit (the tile sequence and every
+    tile's arithmetic are the same; fully masked tiles that one side skips
+    change no bit)."""
+    B, Tl, H, d = q.shape
+    T = k.shape[1]
+    plan = bosa.attn_ring_plan(T, P, rank, zigzag, causal)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    kpos = torch.arange(T, device=DEV)
+    qpos = torch.from_numpy(oracle.local_query_positions(T, P, rank, zigzag)).to(DEV)
+    qr, kr = q.clone(), k.clone()
+    if rope > 0:
+        bosa.rope_apply(qr, qpos, rope)
+        bosa.rope_apply(kr, kpos, rope)
+    acc = torch.zeros((B, Tl, H, d), dtype=torch.float32, device=DEV)
+    lse = torch.full((B, H, Tl), float("-inf"), device=DEV)
+    parts = {}
+    for chain in ring_chains(plan, B, H, causal, n_cu):
+        r0, nr = chain[0].q_row0, chain[0].q_rows
+        widths = [-(-e.kv_rows // 64) * 64 for e in chain]
+        n = sum(widths)
+        kc = torch.zeros((B, n, H, d), dtype=k.dtype, device=DEV)
+        vc = torch.zeros((B, n, H, d), dtype=v.dtype, device=DEV)
+        am = torch.ones((nr, n), dtype=torch.uint8, device=DEV)   # padding keys: excluded
+        kpc = None if kpm is None else torch.ones((B, n), dtype=torch.uint8, device=DEV)
+        c0 = 0
+        for e, wdt in zip(chain, widths):
+            sl = slice(e.kv_pos0, e.kv_pos0 + e.kv_rows)
+            kc[:, c0:c0 + e.kv_rows] = kr[:, sl]
+            vc[:, c0:c0 + e.kv_rows] = v[:, sl]
+            keys = kpos[sl]
+            if causal:
+                am[:, c0:c0 + e.kv_rows] = (keys[None, :] > qpos[r0:r0 + nr, None]).to(torch.uint8)
+            else:
+                am[:, c0:c0 + e.kv_rows] = 0
+            if kpm is not None:
+                kpc[:, c0:c0 + e.kv_rows] = kpm[:, sl]
+            c0 += wdt
+        if r0 not in parts:
+            parts[r0] = (torch.empty((B, nr, H, d), dtype=torch.float32, device=DEV),
+                         torch.empty((B, H, nr), dtype=torch.float32, device=DEV))
+        a, la = parts[r0]
+        flags = bosa.ATTN_OUT_F32 | (bosa.ATTN_ACCUMULATE if chain[0].accumulate else 0)
+        bosa.attn_fwd(qr[:, r0:r0 + nr].contiguous(), kc, vc, a, la, causal=False, kpm=kpc,
+                      attn_mask=am.contiguous(), flags=flags)
+    for r0, (a, la) in parts.items():
+        acc[:, r0:r0 + a.shape[1]] = a
+        lse[:, :, r0:r0 + a.shape[1]] = la
+    out = torch.empty((B, Tl, H, d), dtype=torch.bfloat16, device=DEV)
+    bosa.attn_cast(acc, out)
+    torch.cuda.synchronize()
+    return out, lse

@@ -164,6 +164,7 @@ hipError_t launch_fwd_bf16_chain(const ChainParams& c, int d, hipStream_t) {
     CHECK(c.nblk >= 1 && c.nblk <= kMaxChain, "chain of %d blocks", c.nblk);
     rows(p.q, p.B, p.Tq, p.H, d, p.q_bstride, p.row_stride, 2, false);
     rows(p.out, p.B, p.Tq, p.H, d, p.o_bstride, p.row_stride, 4, true);
+    if (c.out_bf16) rows(c.out_bf16, p.B, p.Tq, p.H, d, p.o_bstride, p.row_stride, 2, true);
     lse_rows(p.lse, p.B, p.H, p.Tq, p.lse_bstride, p.lse_hstride, true);
     for (int s = 0; s < c.nblk; ++s) {
         const ChainBlock& k = c.blk[s];

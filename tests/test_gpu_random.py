@@ -14,7 +14,7 @@ import torch
 import blockwise_online_softmax_attn_amd as bosa
 import oracle
 import workloads
-from gpu_helpers import DEV, compare, note, np64
+from gpu_helpers import DEV, chained_ring_reference, compare, note, np64
 from test_gpu_backward import compare_grads
 
 pytestmark = pytest.mark.gpu
@@ -175,11 +175,12 @@ N_CHAIN = 40
 
 @pytest.mark.parametrize("case", range(N_CHAIN))
 def test_random_ring_share_bitwise_against_its_subcalls(case):
-    """attn_ring_fwd (bf16: sub-calls chained up to four to a launch) against
-    one attn_fwd call per sub-call of attn_ring_plan in plan order, writing
-    or merging into a float32 accumulator, then the cast: out and lse bit for
-    bit, over random P (2, 3, 4, 8), layouts, head counts, key padding and
-    ranks."""
+    """attn_ring_fwd (bf16: sub-calls chained up to four to a launch, the
+    softmax state carried across them) against one attn_fwd call per launch
+    over that launch's keys in ring order (causal order as an attention mask,
+    rotations applied beforehand), merging into a float32 accumulator, then
+    the cast: out and lse bit for bit, over random P (2, 3, 4, 8), layouts,
+    head counts, key padding and ranks."""
     rng = np.random.default_rng(50000 + case)
     P = int(rng.choice([2, 3, 4, 8]))
     zigzag = bool(rng.random() < 0.5)
@@ -204,28 +205,9 @@ def test_random_ring_share_bitwise_against_its_subcalls(case):
             kpm[int(rng.integers(0, B)), int(rng.integers(0, T)):] = 1
         kpm = kpm.to(DEV)
     out, lse = bosa.attn_ring_fwd(q, k, v, P=P, rank=rank, zigzag=zigzag, causal=causal, kpm=kpm, rope_base=rope)
-    Tl = T // P
-    acc = torch.zeros((B, Tl, H, d), dtype=torch.float32, device=DEV)
-    ls = torch.full((B, H, Tl), float("-inf"), device=DEV)
-    parts = {}
-    for e in bosa.attn_ring_plan(T, P, rank, zigzag, causal):
-        r0, nr, k0, nk = e.q_row0, e.q_rows, e.kv_pos0, e.kv_rows
-        if r0 not in parts:
-            parts[r0] = (torch.empty((B, nr, H, d), dtype=torch.float32, device=DEV),
-                         torch.empty((B, H, nr), dtype=torch.float32, device=DEV))
-        a, la = parts[r0]
-        bosa.attn_fwd(q[:, r0:r0 + nr].contiguous(), k[:, k0:k0 + nk].contiguous(), v[:, k0:k0 + nk].contiguous(),
-                      a, la, q_off=e.q_pos0, kv_off=k0, causal=causal,
-                      kpm=None if kpm is None else kpm[:, k0:k0 + nk].contiguous(), rope_base=rope,
-                      flags=bosa.ATTN_OUT_F32 | (bosa.ATTN_ACCUMULATE if e.accumulate else 0))
-    for r0, (a, la) in parts.items():
-        acc[:, r0:r0 + a.shape[1]] = a
-        ls[:, :, r0:r0 + a.shape[1]] = la
-    o16 = torch.empty((B, Tl, H, d), dtype=bf, device=DEV)
-    bosa.attn_cast(acc, o16)
-    torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), o16.view(torch.int16)), "out differs from the sub-calls'"
-    assert torch.equal(lse, ls), "lse differs from the sub-calls'"
+    ro, rl = chained_ring_reference(q, k, v, kpm, P, rank, zigzag, causal, rope)
+    assert torch.equal(out.view(torch.int16), ro.view(torch.int16)), "out differs from the chained launches'"
+    assert torch.equal(lse, rl), "lse differs from the chained launches'"
 
 
 N_RING_BWD = 20
