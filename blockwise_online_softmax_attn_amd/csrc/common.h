@@ -139,7 +139,7 @@ struct FwdParams {
 // float32 out / lse of FwdParams exactly as by one attn_fwd launch per block.
 // At most kMaxChain blocks per launch: measured on the 128K share, chains of
 // 4 were 0.7% faster than one launch per block and chains of 16 6% slower.
-constexpr int kMaxChain = 4;
+constexpr int kMaxChain = 16;
 struct ChainBlock {
     const void* k;             // (rotated) keys and values of the block: row 0 = the block's first key,
     const void* v;             // batch stride and row stride those of FwdParams

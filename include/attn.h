@@ -321,7 +321,7 @@ int attn_ring_plan(int T, int P, int rank, int zigzag, int causal, attn_ring_cal
  *  Other arguments as attn_fwd.  The work is the sub-calls of attn_ring_plan,
  *  issued in order on `stream`, each writing or merging its partial into acc,
  *  then one attn_cast of acc into out.  In bf16 (without window or ALiBi) up
- *  to four consecutive sub-calls of one query block run in one kernel launch
+ *  to sixteen consecutive sub-calls of one query block run in one kernel launch
  *  that carries each row's softmax state across them (so they act as one key
  *  sequence in ring order) and writes or merges one partial per launch; the
  *  last launch of a query block writes out directly.  out and lse then equal

@@ -76,7 +76,7 @@ def compare(out, lse, ref_out, ref_lse, dtype: str, what: str = ""):
     return eo, el
 
 
-CHAIN_MAX = 4      # sub-calls per launch of the chained ring executor
+CHAIN_MAX = 16     # sub-calls per launch of the chained ring executor
 CHAIN_ROWS = 256   # query rows per workgroup of that launch
 
 
