@@ -398,12 +398,13 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
     }
     hipStream_t s = (hipStream_t)stream;
     const bool rope = rope_base > 0.0 && Tkv > 0;
-    // bf16: the queries and the keys are rotated once into scratch copies that
-    // the attention kernel reads (the same float32 rotation it would apply);
-    // float32: the kernel rotates them on the fly.
+    // bf16: the queries and the keys are rotated once, in one launch that
+    // computes its own (cos, sin) values, into scratch copies that the
+    // attention kernel reads; float32: the kernel rotates them on the fly from
+    // float64 (cos, sin) tables.
     const bool krot = rope && dtype == ATTN_BF16;
-    const size_t tab_q = rope ? align_up((size_t)Tq * (d / 2) * sizeof(double2)) : 0;
-    const size_t tab_k = rope ? align_up((size_t)Tkv * (d / 2) * sizeof(double2)) : 0;
+    const size_t tab_q = rope && !krot ? align_up((size_t)Tq * (d / 2) * sizeof(double2)) : 0;
+    const size_t tab_k = rope && !krot ? align_up((size_t)Tkv * (d / 2) * sizeof(double2)) : 0;
     const size_t kbuf = krot ? align_up((size_t)B * Tkv * H * d * 2) : 0;
     const size_t qbuf = krot ? align_up((size_t)B * Tq * H * d * 2) : 0;
     const size_t lst = kpm_list_bytes(c);
@@ -411,24 +412,21 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
     hipError_t e = ws.alloc(tab_q + tab_k + kbuf + qbuf + lst, s);
     if (e != hipSuccess) return hip_fail(e, "scratch allocation");
     char* wp = (char*)ws.ptr;
-    if (rope) {
+    if (krot) {
+        void* kr = wp;
+        void* qr = wp + kbuf;
+        e = launch_rope_rotate_bf16(rope_job(k, kr, B, Tkv, H, d, Tkv, kv_off, 0),
+                                    rope_job(q, qr, B, Tq, H, d, Tq, q_off, 0), H, d, std::log(rope_base), s);
+        if (e != hipSuccess) return hip_fail(e, "key / query rotation launch");
+        c.k = kr;
+        c.q = qr;
+    } else if (rope) {
         const double lb = std::log(rope_base);
         c.rope_q = (const double2*)wp;
         c.rope_k = (const double2*)(wp + tab_q);
         e = launch_rope_table((double2*)wp, q_off, Tq, d, lb, s);
         if (e == hipSuccess) e = launch_rope_table((double2*)(wp + tab_q), kv_off, Tkv, d, lb, s);
         if (e != hipSuccess) return hip_fail(e, "rotary table launch");
-        if (krot) {
-            void* kr = wp + tab_q + tab_k;
-            void* qr = wp + tab_q + tab_k + kbuf;
-            e = launch_rope_copy_bf16(k, kr, c.rope_k, B, Tkv, H, d, s);
-            if (e == hipSuccess) e = launch_rope_copy_bf16(q, qr, c.rope_q, B, Tq, H, d, s);
-            if (e != hipSuccess) return hip_fail(e, "key / query rotation launch");
-            c.k = kr;
-            c.q = qr;
-            c.rope_k = nullptr;
-            c.rope_q = nullptr;
-        }
     }
     return enqueue(c, lst ? (int*)(wp + tab_q + tab_k + kbuf + qbuf) : nullptr, s);
 }
@@ -640,12 +638,13 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
     // bf16: every key block is rotated once (at its absolute positions) into
     // a scratch copy, as the block's owner would before passing it on, and so
     // are the local queries, which every sub-call reads again (rotating them
-    // in each sub-call's kernel would re-read the float32 cos/sin table, twice
-    // the bytes of the queries, once per sub-call); the copies hold the same
-    // values the kernel's own rotation gives.  The local queries' positions
-    // are positions of the keys, so one table over [0, T) serves both.
+    // in each sub-call's kernel would re-read cos/sin values several times the
+    // bytes of the queries, once per sub-call); one launch rotates both and
+    // computes its own (cos, sin) values.  float32: the kernel rotates on the
+    // fly from one table over [0, T) (the local queries' positions are
+    // positions of the keys).
     const bool krot = rope && dtype == ATTN_BF16;
-    const size_t tab_k = rope ? align_up((size_t)T * (d / 2) * sizeof(double2)) : 0;
+    const size_t tab_k = rope && !krot ? align_up((size_t)T * (d / 2) * sizeof(double2)) : 0;
     const size_t kbuf = krot ? align_up((size_t)B * T * H * d * 2) : 0;
     const size_t qbuf = krot ? align_up((size_t)B * Tl * H * d * 2) : 0;
     std::vector<size_t> lst_off(n_live, 0);
@@ -698,19 +697,19 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
     const double2* tab = (const double2*)wp;
     char* krb = wp + tab_k;
     char* qrb = krb + kbuf;
-    if (rope) {
+    if (krot) {
+        // keys at their absolute positions; local rows [0, c) sit at rank * c,
+        // zigzag rows [c, 2c) at (2P - 1 - rank) * c
+        const int parts = zigzag ? 2 : 1;
+        const int c = Tl / parts;
+        err = launch_rope_rotate_bf16(rope_job(k, krb, B, T, H, d, T, 0, 0),
+                                      rope_job(q, qrb, B, Tl, H, d, c, (long long)rank * c,
+                                               (long long)(2 * P - 1 - rank) * c),
+                                      H, d, std::log(rope_base), s);
+        if (err != hipSuccess) return hip_fail(err, "key / query rotation launch");
+    } else if (rope) {
         err = launch_rope_table((double2*)wp, 0, T, d, std::log(rope_base), s);
         if (err != hipSuccess) return hip_fail(err, "rotary table launch");
-        if (krot) {
-            // local rows [0, c) sit at rank * c, zigzag rows [c, 2c) at (2P - 1 - rank) * c
-            const int parts = zigzag ? 2 : 1;
-            const int c = Tl / parts;
-            err = launch_rope_copy_bf16(k, krb, tab, B, T, H, d, s);
-            if (err == hipSuccess)
-                err = launch_rope_copy_bf16(q, qrb, tab, B, Tl, H, d, c, (long long)rank * c,
-                                            (long long)(2 * P - 1 - rank) * c, s);
-            if (err != hipSuccess) return hip_fail(err, "key / query rotation launch");
-        }
     }
     for (int i = 0; i < n_live; ++i) {
         Call& c = calls[i];

@@ -255,6 +255,24 @@ hipError_t launch_merge(float* oa, float* la, const void* ob, const float* lb, i
 hipError_t launch_cast(const float* src, void* dst, long long n, int to_bf16, hipStream_t s);
 hipError_t launch_rope_apply(void* x, const long long* pos, double log_base, int B, int T, int H, int d,
                              int is_bf16, hipStream_t s);
+// One tensor of a rope_rotate launch: B x T tokens of H x d bf16 values;
+// token t of a batch row sits at position t < split ? off0 + t : off1 + (t - split).
+struct RopeJob {
+    const void* src;
+    void* dst;
+    long long n_threads;       // B * T * (H / heads per thread) * (d / 8); 0 = no work
+    int T;
+    int split;
+    long long off0, off1;
+};
+inline RopeJob rope_job(const void* src, void* dst, int B, int T, int H, int d, int split, long long off0,
+                        long long off1) {
+    const int hpt = (H % 4 == 0) ? 4 : 1;   // heads per thread, as the launch picks them
+    return RopeJob{src, dst, (long long)B * T * (H / hpt) * (d / 8), T, split, off0, off1};
+}
+// Rotary copies of jobs a and b (same H and d) in one launch, with the (cos, sin)
+// values computed in the kernel: no table needed.
+hipError_t launch_rope_rotate_bf16(const RopeJob& a, const RopeJob& b, int H, int d, double log_base, hipStream_t s);
 hipError_t launch_rope_copy_bf16(const void* src, void* dst, const double2* tab, int B, int T, int H, int d,
                                  hipStream_t s);
 // The same with row t taking table row t + off0 for t < split, else

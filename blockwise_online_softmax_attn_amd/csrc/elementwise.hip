@@ -217,6 +217,54 @@ __global__ __launch_bounds__(256) void rope_copy_bf16_kernel(const uint4* __rest
     }
 }
 
+// Rotary copies of up to two bf16 tensors in one launch (the keys and the
+// queries of a call), each pair rotated in float64 and rounded once, with the
+// float64 cos and sin of every (token, pair) a workgroup touches computed by
+// that workgroup (rope_cs64, one evaluation each, shared through LDS) instead
+// of read from a table: the values are the table's, bit for bit, and the
+// table pass and its launch go away.  Workgroups [0, nblk0) serve job 0, the
+// rest job 1.  Thread layout as rope_copy_bf16_kernel: a thread owns one
+// 16-byte granule column (4 pairs) of one token in HPT heads.
+template <int HPT>
+__global__ __launch_bounds__(256) void rope_rotate_bf16_kernel(const RopeJob j0, const RopeJob j1, long long nblk0,
+                                                               int H, int gpr, double log_base) {
+    extern __shared__ double2 cs[];   // [token of the workgroup][pair]
+    const bool second = (long long)blockIdx.x >= nblk0;
+    const RopeJob& J = second ? j1 : j0;
+    const long long g0 = ((long long)blockIdx.x - (second ? nblk0 : 0)) * 256;
+    const int hs = H / HPT;
+    const int tpt = hs * gpr;                // threads per token
+    const int np = 4 * gpr;                  // pairs per token (d / 2)
+    const long long tok0 = g0 / tpt;
+    const long long ntok = J.n_threads / tpt;
+    const long long tok1 = min((g0 + 255) / tpt, ntok - 1);
+    const int nent = (int)(tok1 - tok0 + 1) * np;
+    for (int e = threadIdx.x; e < nent; e += 256) {
+        const long long tok = tok0 + e / np;
+        const int t = (int)(tok % J.T);
+        const long long pos = t < J.split ? J.off0 + t : J.off1 + (t - J.split);
+        cs[e] = rope_cs64(pos, e % np, 2 * np, log_base);
+    }
+    __syncthreads();
+    const long long g = g0 + threadIdx.x;
+    if (g >= J.n_threads) return;
+    const long long tok = g / tpt;
+    const int r = (int)(g - tok * tpt);
+    const int c = r % gpr, j = r / gpr;
+    const double2* tp = cs + (tok - tok0) * np + 4 * c;
+    const double2 c0 = tp[0], c1 = tp[1], c2 = tp[2], c3 = tp[3];
+    const uint4* src = (const uint4*)J.src;
+    uint4* dst = (uint4*)J.dst;
+    const long long row0 = tok * H * gpr + c;
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+        const long long at = row0 + (long long)(j + k * hs) * gpr;
+        const uint4 x = src[at];
+        dst[at] = make_uint4(rot_pair_bf16(x.x, c0.x, c0.y), rot_pair_bf16(x.y, c1.x, c1.y),
+                             rot_pair_bf16(x.z, c2.x, c2.y), rot_pair_bf16(x.w, c3.x, c3.y));
+    }
+}
+
 // Rows [0, rows) become the merge identity: out = 0 (float32 or bf16), lse = -inf.
 template <bool BF16>
 __global__ __launch_bounds__(256) void fill_empty_kernel(void* __restrict__ out, float* __restrict__ lse, int B, int H,
@@ -306,6 +354,23 @@ hipError_t launch_rope_copy_bf16(const void* src, void* dst, const double2* tab,
 hipError_t launch_rope_copy_bf16(const void* src, void* dst, const double2* tab, int B, int T, int H, int d,
                                  hipStream_t s) {
     return launch_rope_copy_bf16(src, dst, tab, B, T, H, d, T, 0, 0, s);
+}
+
+hipError_t launch_rope_rotate_bf16(const RopeJob& a, const RopeJob& b, int H, int d, double log_base, hipStream_t s) {
+    const int gpr = d / 8;
+    const int hpt = (H % 4 == 0) ? 4 : 1;
+    const int tpt = (H / hpt) * gpr;
+    const long long nb0 = (a.n_threads + 255) / 256, nb1 = (b.n_threads + 255) / 256;
+    if (nb0 + nb1 == 0) return hipSuccess;
+    // tokens a workgroup touches: at most 256 / tpt + 2, each d / 2 (cos, sin) pairs
+    const size_t lds = (size_t)(256 / tpt + 2) * (d / 2) * sizeof(double2);
+    if (hpt == 4)
+        hipLaunchKernelGGL(rope_rotate_bf16_kernel<4>, dim3((unsigned)(nb0 + nb1)), dim3(256), lds, s, a, b, nb0, H, gpr,
+                           log_base);
+    else
+        hipLaunchKernelGGL(rope_rotate_bf16_kernel<1>, dim3((unsigned)(nb0 + nb1)), dim3(256), lds, s, a, b, nb0, H, gpr,
+                           log_base);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_empty(void* out, int out_bf16, float* lse, int B, int H, int rows, int d, long long o_bstride,

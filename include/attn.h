@@ -106,12 +106,12 @@ enum {
  *  dtype      ATTN_BF16 (bf16 MFMA, float32 accumulation and softmax) or
  *             ATTN_F32 (float32 throughout).
  *  flags      ATTN_ACCUMULATE | ATTN_OUT_F32 | ATTN_NO_TILE_SKIP.
- * Scratch:    with rope_base > 0 and Tkv > 0, the float64 (cos, sin) tables
- *             (Tq + Tkv) * (d/2) * 16; in bf16 also the rotated copies of k
+ * Scratch:    with rope_base > 0 and Tkv > 0: in bf16 the rotated copies of k
  *             and q, 2 * B * (Tkv + Tq) * H * d (the kernel streams
- *             rotated operands).  In bf16 with kpm (without
- *             ATTN_NO_TILE_SKIP) the live key-tile list,
- *             4 * B * (ceil(Tkv / 64) + 2).
+ *             rotated operands; the rotation computes its own cos and sin);
+ *             in float32 the float64 (cos, sin) tables (Tq + Tkv) * (d/2) * 16.
+ *             In bf16 with kpm (without ATTN_NO_TILE_SKIP) the live key-tile
+ *             list, 4 * B * (ceil(Tkv / 64) + 2).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int Tq, int Tkv, int d,
@@ -328,14 +328,14 @@ int attn_ring_plan(int T, int P, int rank, int zigzag, int causal, attn_ring_cal
  *  one attn_fwd call per launch over that launch's keys in ring order, and
  *  one attn_fwd call per sub-call up to rounding.  With RoPE the call rotates
  *  every key block and the local queries once into scratch copies.
- * Scratch:    with rope_base > 0, the float64 (cos, sin) table over the T
- *             positions, T * (d/2) * 16; in bf16 also the rotated keys and
- *             local queries, 2 * B * (T + T/P) * H * d.  In bf16 with kpm
+ * Scratch:    with rope_base > 0: in bf16 the rotated keys and local queries,
+ *             2 * B * (T + T/P) * H * d; in float32 the float64 (cos, sin)
+ *             table over the T positions, T * (d/2) * 16.  In bf16 with kpm
  *             (without ATTN_NO_TILE_SKIP) one live key-tile list per
  *             sub-call, 4 * B * (ceil(c / 64) + 2) each, c = the sub-call's
  *             key rows (T/P, or T/(2P) under zigzag).  The 128K zigzag share
  *             (B = 1, H = 32, d = 128, T = 131072, P = 8) with RoPE:
- *             128 MiB + 1 GiB + 128 MiB.
+ *             1 GiB + 128 MiB.
  */
 int attn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse, float* acc,
                   int B, int H, int T, int d, int P, int rank, int zigzag, int causal,

@@ -205,6 +205,15 @@ hipError_t launch_rope_apply(void* x, const long long* pos, double, int B, int T
     touch(x, (size_t)B * T * H * d * (is_bf16 ? 2 : 4), true);
     return launched();
 }
+hipError_t launch_rope_rotate_bf16(const RopeJob& a, const RopeJob& b, int H, int d, double, hipStream_t) {
+    const int hpt = (H % 4 == 0) ? 4 : 1;
+    for (const RopeJob* j : {&a, &b}) {
+        const long long tokens = j->n_threads / ((H / hpt) * (d / 8));
+        touch(j->src, (size_t)tokens * H * d * 2, false);
+        touch(j->dst, (size_t)tokens * H * d * 2, true);
+    }
+    return launched();
+}
 hipError_t launch_rope_copy_bf16(const void* src, void* dst, const double2* tab, int B, int T, int H, int d, int split,
                                  long long off0, long long off1, hipStream_t) {
     touch(src, (size_t)B * T * H * d * 2, false);
@@ -347,7 +356,7 @@ static void forward_cases() {
                                       ATTN_OUT_F32, nullptr);
                     CHECK(rc == ATTN_OK, "attn_fwd rc %d (%s)", rc, attn_last_error());
                     size_t want = 0;
-                    if (rope) want += au((size_t)Tq * (d / 2) * 16) + au((size_t)Tkv * (d / 2) * 16);
+                    if (rope && dtype == ATTN_F32) want += au((size_t)Tq * (d / 2) * 16) + au((size_t)Tkv * (d / 2) * 16);
                     if (rope && dtype == ATTN_BF16) want += au((size_t)B * Tkv * H * d * 2) + au((size_t)B * Tq * H * d * 2);
                     if (kp && dtype == ATTN_BF16) want += au((size_t)B * ((Tkv + 63) / 64 + 2) * 4);
                     CHECK(g_alloc_bytes == want, "attn_fwd dtype %d d %d rope %d kpm %d: scratch %zu, formula %zu",
@@ -474,7 +483,7 @@ static void ring_fwd_cases() {
                                 CHECK(rc == ATTN_OK, "ring fwd rc %d (%s)", rc, attn_last_error());
                                 if (!win) {
                                     size_t want = 0;
-                                    if (rope) want += au((size_t)T * (d / 2) * 16);
+                                    if (rope && dtype == ATTN_F32) want += au((size_t)T * (d / 2) * 16);
                                     if (rope && dtype == ATTN_BF16)
                                         want += au((size_t)B * T * H * d * 2) + au((size_t)B * Tl * H * d * 2);
                                     const int n = attn_ring_plan(T, P, rank, zz, 1, nullptr, 0);
