@@ -671,12 +671,28 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restri
         const double2* tr = tab ? tab + (long long)t * (d / 2) : nullptr;
         for (int i = threadIdx.x; i < n4; i += blockDim.x) {
             const float4 x = ((const float4*)sp)[i];
-            double2 y0 = make_double2(x.x, x.y), y1 = make_double2(x.z, x.w);
-            if (tr) {
-                const double2 ca = tr[2 * (i & (d / 4 - 1))], cb = tr[2 * (i & (d / 4 - 1)) + 1];
-                y0 = rot64(x.x, x.y, ca.x, -ca.y);
-                y1 = rot64(x.z, x.w, cb.x, -cb.y);
+            if (!tr) {
+                // no rotation: the float32 value rounded once (the float64
+                // path below gives the same bits, at several times the cost)
+                if (BF16) {
+                    ((uint2*)((uint16_t*)dst + doff))[i] = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+                } else {
+                    float4* o = (float4*)((float*)dst + doff) + i;
+                    float4 r = x;
+                    if (accumulate) {
+                        const float4 a = *o;
+                        r.x += a.x;
+                        r.y += a.y;
+                        r.z += a.z;
+                        r.w += a.w;
+                    }
+                    *o = r;
+                }
+                continue;
             }
+            const double2 ca = tr[2 * (i & (d / 4 - 1))], cb = tr[2 * (i & (d / 4 - 1)) + 1];
+            const double2 y0 = rot64(x.x, x.y, ca.x, -ca.y);
+            const double2 y1 = rot64(x.z, x.w, cb.x, -cb.y);
             if (BF16) {
                 ((uint2*)((uint16_t*)dst + doff))[i] =
                     make_uint2(bf16_bits_rn(y0.x) | (bf16_bits_rn(y0.y) << 16),
@@ -759,8 +775,10 @@ hipError_t launch_bwd_finalize(const float* src, void* dst, const double2* tab, 
                                hipStream_t s) {
     const long long rows = (long long)B * T;
     if (rows == 0 || H == 0) return hipSuccess;
-    // at most 2^20 workgroups (2^28 work-items, far below the 2^32 limit); more rows go round the grid stride
-    const unsigned grid = (unsigned)(rows < (1LL << 20) ? rows : (1LL << 20));
+    // 2048 workgroups of 256 threads fill the 256 CUs once at 8 per CU, with
+    // far more loads in flight per CU than HBM latency needs; more rows go
+    // round the grid stride.
+    const unsigned grid = (unsigned)(rows < 2048 ? rows : 2048);
     if (dst_bf16)
         hipLaunchKernelGGL(bwd_finalize_kernel<true>, dim3(grid), dim3(256), 0, s, src, dst, tab, rows, T, H, d,
                            src_bstride, dst_bstride, 0);

@@ -54,17 +54,18 @@ __device__ __forceinline__ double2 rot64(double x0, double x1, double c, double 
     return make_double2(fma(x0, c, -(x1 * s)), fma(x0, s, x1 * c));
 }
 
-// float64 -> bf16 bit pattern, rounded once to nearest even: the value is
-// first narrowed to float32 rounding to odd (truncate, then set the last bit
-// when anything was dropped), which keeps the information a final
-// round-to-nearest-even to 8 significant bits needs, then rounded to bf16.
+// float64 -> bf16 bit pattern, rounded once to nearest even.  The value is
+// first rounded to the nearest float32 f; a second rounding of f to bf16 can
+// only differ from rounding the value itself when f lands exactly on a bf16
+// midpoint (low 16 bits 0x8000) without being equal to the value, and then
+// the value lies on the side f moved away from: f is stepped one float32
+// unit toward the value, off the midpoint, before the round to nearest even.
 __host__ __device__ __forceinline__ uint32_t bf16_bits_rn(double y) {
     const float f = (float)y;                       // nearest
     uint32_t u = __builtin_bit_cast(uint32_t, f);
-    const double back = (double)f;
-    if (back != y) {
-        if (__builtin_fabs(back) > __builtin_fabs(y)) u -= 1u;   // it rounded away from zero: step back toward zero
-        u |= 1u;                                                  // sticky
+    if ((u & 0xFFFFu) == 0x8000u) {
+        const double back = (double)f;
+        if (back != y) u = __builtin_fabs(back) > __builtin_fabs(y) ? u - 1u : u + 1u;
     }
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
