@@ -1,29 +1,37 @@
 // Blockwise online-softmax attention forward, float32 inputs.
 //
 // True float32 products and accumulation (no bf16 or reduced-precision
-// operand rounding).  One wave of 64 lanes owns 32 query rows; the two lanes
-// of a pair (2i, 2i+1) share row i, each holding half of the (rotated) query
-// and of the output accumulator in registers, and add their partial dot
-// products with one lane exchange.  Key/value tiles of 32 rows are staged in
-// LDS and read by every pair at once (LDS broadcast); scores are folded into
-// the running max / denominator / weighted sum 8 keys at a time, the
-// safe-softmax accumulator rescale of the brunomaga.github.io
-// sequence-context-parallelism post ("Improving numerical stability").
+// operand rounding).  A workgroup of four waves owns 32 query rows; in each
+// wave the two lanes of a pair (2i, 2i+1) share row i, each holding half of
+// the (rotated) query and of the output accumulator in registers, and add
+// their partial dot products with one lane exchange.  Key/value tiles of 32
+// rows are staged in LDS by the whole workgroup; wave w folds keys
+// 8w .. 8w + 7 of every tile into its own running max / denominator /
+// weighted sum, the safe-softmax accumulator rescale of the
+// brunomaga.github.io sequence-context-parallelism post ("Improving
+// numerical stability"), and the four states are combined at the end in wave
+// order.  The key -> wave assignment depends only on the key's position in its
+// tile, so skipping tiles changes no bit.
 #include "common.h"
 
 namespace bosa {
 namespace {
 
-constexpr int BMF = 32;  // query rows per workgroup (one wave, two lanes per row)
+constexpr int BMF = 32;  // query rows per workgroup (two lanes per row in each wave)
 constexpr int BNF = 32;  // keys per LDS tile
-constexpr int SUB = 8;   // keys per online-softmax update
+constexpr int SUB = 8;   // keys per online-softmax update: one group per wave and tile
+constexpr int NWF = BNF / SUB;   // waves per workgroup
 
 template <int D>
-__global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(const FwdParams p) {
+__global__ __launch_bounds__(64 * NWF, 2) void attn_fwd_f32_kernel(const FwdParams p) {
     constexpr int HD = D / 2;
-    __shared__ float4 sK[BNF * D / 4];
-    __shared__ float4 sV[BNF * D / 4];
-    const int lane = threadIdx.x;
+    __shared__ float4 sKV[2 * BNF * D / 4];   // the K tile, then the V tile
+    float4* sK = sKV;
+    float4* sV = sKV + BNF * D / 4;
+    static_assert((HD + 2) * 64 <= 2 * BNF * D, "one wave's state must fit in the tile buffers");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane & 1;
 
     int bid = blockIdx.x;
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(const FwdParams p) 
 
     float m_i = -INFINITY, l_i = 0.f;
     for (long long key0 = klo / BNF * BNF; key0 < nk; key0 += BNF) {
-        for (int idx = lane; idx < BNF * D / 4; idx += 64) {
+        for (int idx = tid; idx < BNF * D / 4; idx += 64 * NWF) {
             const int row = idx / (D / 4), c4 = idx % (D / 4);
             const long long key = key0 + row;
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
@@ -92,7 +100,8 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(const FwdParams p) 
         }
         __syncthreads();
 
-        for (int j0 = 0; j0 < BNF; j0 += SUB) {
+        {
+            const int j0 = w * SUB;   // this wave's keys of the tile
             float s[SUB];
             float mx = -INFINITY;
 #pragma unroll
@@ -151,6 +160,33 @@ __global__ __launch_bounds__(64, 2) void attn_fwd_f32_kernel(const FwdParams p) 
         __syncthreads();
     }
 
+    // combine the waves' states in wave order: wave u leaves its state in
+    // the tile buffers (free after the loop's last barrier) and wave 0 folds
+    // it in; every wave passes the same barriers
+    float* xs = (float*)sKV;   // [HD + 2][64 lanes]
+    for (int u = 1; u < NWF; ++u) {
+        if (w == u) {
+            xs[lane] = m_i;
+            xs[64 + lane] = l_i;
+#pragma unroll
+            for (int c = 0; c < HD; ++c) xs[(2 + c) * 64 + lane] = o[c];
+        }
+        __syncthreads();
+        if (w == 0) {
+            const float mu = xs[lane], lu = xs[64 + lane];
+            const float mn = fmaxf(m_i, mu);
+            if (mn != -INFINITY) {   // else neither state has an allowed key yet
+                const float a = __builtin_amdgcn_exp2f(m_i - mn), bu = __builtin_amdgcn_exp2f(mu - mn);
+                l_i = fmaf(l_i, a, lu * bu);
+#pragma unroll
+                for (int c = 0; c < HD; ++c) o[c] = fmaf(o[c], a, xs[(2 + c) * 64 + lane] * bu);
+                m_i = mn;
+            }
+        }
+        __syncthreads();
+    }
+    if (w > 0) return;
+
     if (!qvalid) return;
     const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
     const float lse_b = l_i > 0.f ? (m_i + log2f(l_i)) * kLn2 : -INFINITY;
@@ -183,7 +219,7 @@ hipError_t launch(const FwdParams& p, hipStream_t s) {
     FwdParams q = p;
     q.n_qtiles = (p.Tq + BMF - 1) / BMF;
     const long long grid = (long long)q.n_qtiles * p.H * p.B;
-    hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)grid), dim3(64), 0, s, q);
+    hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)grid), dim3(64 * NWF), 0, s, q);
     return hipGetLastError();
 }
 
