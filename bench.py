@@ -3,9 +3,10 @@
 
 Default workload: one rank's share of an 8-way zigzag ring at 128K context
 (B=1, H=32, d=128, bf16, causal, RoPE base 10000): 16384 local query rows
-against 131072 keys in ring order, 17 attention sub-calls merged into a float32
-accumulator and cast to bf16 (the sub-calls of each query half run up to four
-to a launch of the chained kernel: 6 launches per step).  One step is one whole
+against 131072 keys in ring order, 17 attention sub-calls (those of each query
+half run up to sixteen to a launch of the chained kernel, which carries the
+softmax state across them: 3 launches per step, the last launch of each half
+writing the bf16 output).  One step is one whole
 share (attn_ring_fwd), inputs resident in HBM.  `--workload N` selects another
 of the five workloads.
 

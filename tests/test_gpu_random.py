@@ -175,7 +175,7 @@ N_CHAIN = 40
 
 @pytest.mark.parametrize("case", range(N_CHAIN))
 def test_random_ring_share_bitwise_against_its_subcalls(case):
-    """attn_ring_fwd (bf16: sub-calls chained up to four to a launch, the
+    """attn_ring_fwd (bf16: sub-calls chained up to sixteen to a launch, the
     softmax state carried across them) against one attn_fwd call per launch
     over that launch's keys in ring order (causal order as an attention mask,
     rotations applied beforehand), merging into a float32 accumulator, then
