@@ -754,6 +754,10 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
                 }
                 ChainParams cpm{};
                 cpm.p = fwd_params(calls[idx[j0]]);
+                // all workgroups at once (one per CU): pair light and heavy
+                // query units, since the heaviest workgroup sets the time
+                const long long wgs = (long long)B * H * ((plan[idx[j0]].q_rows + kChainRows - 1) / kChainRows);
+                cpm.p.paired = causal && wgs <= n_cu ? 1 : 0;
                 if (j0 + n1 == idx.size())   // the query block's last launch
                     cpm.out_bf16 = (uint16_t*)out + (size_t)plan[idx[j0]].q_row0 * rs;
                 cpm.nblk = (int)n1;

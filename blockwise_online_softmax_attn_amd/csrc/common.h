@@ -132,6 +132,12 @@ struct FwdParams {
     long long win_left, win_right;
     const float* alibi;        // [H] slopes: score -= slope_h |pos_q - pos_k| (after 1/sqrt(d)), or null
     float sqrt_d;              // sqrt(d): the bias in units of the unscaled dot product
+    // chained kernel only: workgroup t holds the 128-row query units t (waves
+    // 0-3) and n - 1 - t (waves 4-7) of the n = ceil(Tq / 128) instead of 256
+    // consecutive rows, so that under causal order every workgroup has about
+    // the same number of allowed pairs (for a launch whose workgroups all run
+    // at once, where the heaviest one sets the launch time)
+    int paired;
 };
 
 // One query block of a ring share against a sequence of key/value blocks in

@@ -667,13 +667,23 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
     const float sl2 = p.scale_log2;
     const int nb = cp.nblk;
 
-    const int q0 = qt * BM;
-    const int qw0 = q0 + w * 32;
+    // this wave's 32 rows: of the workgroup's 256 consecutive rows, or, when
+    // paired, of unit qt (waves 0-3) or unit nu - 1 - qt (waves 4-7; idle when
+    // that is unit qt itself, the middle of an odd count).  Waves w and w + 4
+    // share a SIMD, so each SIMD then runs one wave of each unit.
+    int qw0, qlast;
+    if (p.paired) {
+        const int hi = ((Tq + 127) >> 7) - 1 - qt;   // >= qt
+        qw0 = w < 4 ? qt * 128 + 32 * w : (hi > qt ? hi * 128 + 32 * (w - 4) : Tq);
+        qlast = min(hi * 128 + 128, Tq) - 1;
+    } else {
+        qw0 = qt * BM + w * 32;
+        qlast = min(qt * BM + BM, Tq) - 1;
+    }
     const int qi = qw0 + l32;
     const bool qvalid = qi < Tq;
     const bool wvalid = qw0 < Tq;
     const int qwlast = min(qw0 + 31, Tq - 1);
-    const int qlast = min(q0 + BM, Tq) - 1;
 
     // ---- Q operand (rotated when the rotary embedding is on)
     bf16x8 qreg[G::NC];
@@ -685,8 +695,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-    // ---- per block: live tiles of the workgroup, leading tiles every row
-    // allows, tiles that hold allowed keys for this wave's rows; kept in this
+    // ---- per block: live tiles of the workgroup, leading tiles every row of
+    // the wave allows, tiles that hold allowed keys for this wave's rows; kept in this
     // wave's LDS table (ntiles | nfull | nact, kMaxChain entries each).
     typedef const __attribute__((address_space(4))) int* cint_ptr;
     auto block_list = [&](int s) __attribute__((always_inline)) -> cint_ptr {
@@ -716,7 +726,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_chain_kernel(const ChainP
             ntl = lo;
         }
         long long kf_hi = Tkv;
-        if (causal) kf_hi = min(kf_hi, q0 + delta + 1);
+        if (causal) kf_hi = min(kf_hi, qw0 + delta + 1);   // tiles every row of the wave allows
         long long nf = kf_hi < 0 ? 0 : kf_hi / BN;
         if (kl) nf = min(nf, (long long)kl[1]);
         const bool fm = noskip || (cp.blk[s].kpm && !cp.blk[s].kpm_list);
