@@ -125,6 +125,7 @@ struct Call {
     const double2* rope_q; const double2* rope_k;
     long long win_left = -1, win_right = -1;
     const float* alibi = nullptr;
+    int paired = 0;            // bf16 kernel: pair light and heavy query units (FwdParams.paired)
 };
 
 Call plain_call(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Tq, int Tkv,
@@ -197,6 +198,7 @@ int enqueue(const Call& c, int* list, hipStream_t s) {
         return e == hipSuccess ? ATTN_OK : hip_fail(e, "empty-key fill");
     }
     FwdParams p = fwd_params(c);
+    p.paired = c.paired;
     if (c.dtype == ATTN_BF16 && list) {
         if (int rc = build_tile_list(c, list, s)) return rc;
         p.kpm_list = list;
@@ -397,6 +399,16 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
         c.alibi = var->alibi_slopes;
     }
     hipStream_t s = (hipStream_t)stream;
+    // bf16 under causal order without a window, all workgroups at once (at
+    // most one per CU): pair light and heavy query units, since the heaviest
+    // workgroup sets the time.  The CU count is read before anything is enqueued.
+    if (dtype == ATTN_BF16 && causal && Tkv > 0 && c.win_left < 0 && c.win_right < 0) {
+        int dev = 0, n_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "device query");
+        c.paired = (long long)B * H * ((Tq + kChainRows - 1) / kChainRows) <= n_cu ? 1 : 0;
+    }
     const bool rope = rope_base > 0.0 && Tkv > 0;
     // bf16: the queries and the keys are rotated once, in one launch that
     // computes its own (cos, sin) values, into scratch copies that the

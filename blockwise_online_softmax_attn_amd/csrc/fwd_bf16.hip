@@ -327,8 +327,19 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     const bool causal = p.causal != 0;
     const float sl2 = p.scale_log2;
 
+    // this wave's 32 rows: of the workgroup's 256 consecutive rows, or, when
+    // paired (no window), of unit qt (waves 0-3) or unit nu - 1 - qt (waves
+    // 4-7; idle when that is unit qt itself) of the nu 128-row units
     const int q0 = qt * BM;
-    const int qw0 = q0 + w * 32;
+    int qw0 = q0 + w * 32;
+    int qlast = min(q0 + BM, Tq) - 1;
+    if constexpr (!WIN) {
+        if (p.paired) {
+            const int hi = ((Tq + 127) >> 7) - 1 - qt;   // >= qt
+            qw0 = w < 4 ? qt * 128 + 32 * w : (hi > qt ? hi * 128 + 32 * (w - 4) : Tq);
+            qlast = min(hi * 128 + 128, Tq) - 1;
+        }
+    }
     const int qi = qw0 + l32;
     const bool qvalid = qi < Tq;
     const bool wvalid = qw0 < Tq;
@@ -353,7 +364,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     // window bound them unless every tile is to be visited).  Without a window
     // (WIN false) every window term folds away at compile time.
     const bool wl_on = WIN && p.win_left >= 0, wr_on = WIN && p.win_right >= 0;
-    const int qlast = min(q0 + BM, Tq) - 1;
     long long khi = Tkv, klo = 0;
     if (!noskip) {
         if (causal) khi = min(khi, delta + qlast + 1);
@@ -363,9 +373,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const FwdParams p)
     khi = max(khi, 0LL);
     const int t_hi = (int)((khi + BN - 1) / BN);
     const int t_lo = klo >= khi ? t_hi : (int)(klo / BN);
-    // Tiles whose every key is allowed for every row: [tf_lo, tf_hi).
+    // Tiles whose every key is allowed for every row: [tf_lo, tf_hi) (of the
+    // wave without a window, of the workgroup with one).
     long long kf_hi = Tkv, kf_lo = 0;
-    if (causal) kf_hi = min(kf_hi, q0 + delta + 1);
+    if (causal) kf_hi = min(kf_hi, (WIN ? q0 : qw0) + delta + 1);
     if (wr_on) kf_hi = min(kf_hi, q0 + delta + p.win_right + 1);
     if (wl_on) kf_lo = max(kf_lo, qlast + delta - p.win_left);
     const long long tf_lo = (kf_lo + BN - 1) / BN;

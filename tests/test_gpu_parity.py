@@ -329,6 +329,32 @@ def test_ring_share_with_key_padding(case):
         compare(out.cpu(), lse.cpu(), ro, rl, dt_name(q), f"rank{rank}")
 
 
+@pytest.mark.parametrize("Tq,Tkv,q_off,kp,rope", [(1000, 1000, 0, 0.0, 0.0), (650, 900, 250, 0.2, 10000.0),
+                                                 (300, 300, 0, 0.0, 0.0)])
+def test_paired_query_units_equal_unpaired_bitwise(Tq, Tkv, q_off, kp, rope):
+    """A causal bf16 attn_fwd whose workgroups all run at once (at most one
+    per CU) pairs 128-row query units: workgroup t takes units t and n - 1 - t
+    (300 rows: three units, the middle one alone).  With more workgroups than
+    CUs each keeps 256 consecutive rows.  A row's result does not depend on
+    which workgroup computes it: one head alone against the same head
+    repeated until the grid exceeds the CU count, bit for bit."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    d, bf = 128, torch.bfloat16
+    q = rnd((1, Tq, 1, d), 9701, bf)
+    k = rnd((1, Tkv, 1, d), 9702, bf)
+    v = rnd((1, Tkv, 1, d), 9703, bf)
+    kpm = workloads.random_mask((1, Tkv), 9704, kp).to(DEV) if kp else None
+    H = n_cu // ((Tq + 255) // 256) + 1
+    note(f"paired vs unpaired: Tq={Tq} Tkv={Tkv} q_off={q_off} kpm={kp} rope={rope}: 1 head, then {H} heads")
+    o1, l1 = bosa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), q_off=q_off, causal=True, kpm=kpm, rope_base=rope)
+    rep = lambda x: x.expand(1, x.shape[1], H, d).contiguous().to(DEV)
+    oH, lH = bosa.attn_fwd(rep(q), rep(k), rep(v), q_off=q_off, causal=True, kpm=kpm, rope_base=rope)
+    torch.cuda.synchronize()
+    for h in (0, H // 2, H - 1):
+        assert torch.equal(oH[:, :, h:h + 1].view(torch.int16).cpu(), o1.view(torch.int16).cpu()), f"head {h}: out"
+        assert torch.equal(lH[:, h:h + 1].cpu(), l1.cpu()), f"head {h}: lse"
+
+
 @pytest.mark.parametrize("zigzag,causal,kp,rope,d", [(True, True, 0.0, 10000.0, 128), (False, True, 0.2, 10000.0, 128),
                                                     (True, False, 0.2, 0.0, 64), (False, False, 0.0, 500.0, 64)])
 def test_ring_share_equals_its_subcalls_bitwise(zigzag, causal, kp, rope, d):
