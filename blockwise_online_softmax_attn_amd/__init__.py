@@ -321,6 +321,12 @@ def attn_ring_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
     return dq, dk, dv
 
 
+def release_scratch() -> None:
+    """Free the scratch buffers the library keeps for the current device
+    (attn_release_scratch); waits for the device's work first."""
+    check(load().attn_release_scratch())
+
+
 class KernelTimer:
     """Times every attention-kernel launch the library makes on this thread
     (HIP events on the launch's own stream).  ``ms`` holds the per-launch

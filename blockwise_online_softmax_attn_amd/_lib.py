@@ -16,7 +16,8 @@ ATTN_ACCUMULATE, ATTN_OUT_F32, ATTN_NO_TILE_SKIP = 1, 2, 4
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan", "attn_ring_fwd",
            "attn_ring_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_ring_bwd", "attn_ring_bwd_ex", "attn_kv_append", "attn_decode",
-           "attn_decode_noalloc", "attn_profile_start", "attn_profile_stop", "attn_last_error", "attn_version")
+           "attn_decode_noalloc", "attn_profile_start", "attn_profile_stop", "attn_release_scratch",
+           "attn_last_error", "attn_version")
 
 
 class RingCall(ctypes.Structure):
@@ -77,10 +78,11 @@ def load() -> ctypes.CDLL:
     lib.attn_ring_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, d, i, u, vp]
     lib.attn_profile_start.argtypes = [i]
     lib.attn_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_float), i]
+    lib.attn_release_scratch.argtypes = []
     for name in ("attn_fwd", "attn_fwd_ex", "attn_merge", "rope_apply", "attn_cast", "attn_ring_plan",
                  "attn_ring_fwd", "attn_ring_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_ring_bwd", "attn_ring_bwd_ex",
                  "attn_kv_append", "attn_decode", "attn_decode_noalloc",
-                 "attn_profile_start", "attn_profile_stop", "attn_version"):
+                 "attn_profile_start", "attn_profile_stop", "attn_release_scratch", "attn_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p

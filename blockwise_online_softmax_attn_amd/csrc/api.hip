@@ -1,12 +1,17 @@
 // Host side of the C ABI: argument validation (before any HIP call), dtype /
-// head-dim dispatch, stream-ordered workspace for the rotary table and the
-// live-tile list, the ring-share plan and its executor.
+// head-dim dispatch, the per-stream scratch for rotated copies, tables and
+// live-tile lists, the ring-share plan and its executor.
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
 #include <string>
+#include <thread>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -45,18 +50,79 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int kTile = 64;   // key tile of the bf16 kernel (live-tile list granularity)
 constexpr int kChainRows = 256;   // query rows per workgroup of the chained bf16 kernel
 
-// Stream-ordered scratch: allocated on the call's stream, released on it after
-// the last kernel that uses it, so nothing outlives the call.
+// Device scratch of one call.  Outside stream capture it is the calling
+// stream's buffer, which the library keeps (one per device and stream; per
+// host thread as well for the per-thread default stream) and reuses from call
+// to call, growing it when a call needs more.  Freeing device memory at the
+// end of every call (hipFreeAsync) waits here for the stream's pending work,
+// which made each call synchronous with the one before it.  A call holds the
+// buffer's lock while it enqueues, so calls from several host threads on one
+// stream take turns: each call's kernels follow the previous call's in the
+// stream and never share the buffer with another call's.  Under stream
+// capture the scratch is allocated and freed in stream order instead (graph
+// allocation nodes), since a captured graph must not keep pointing at a
+// buffer that a later, larger call replaces.  attn_release_scratch frees the
+// kept buffers of the current device.
+struct ScratchSlot {
+    std::mutex m;
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+using SlotKey = std::tuple<int, uintptr_t, std::thread::id>;
+std::mutex g_slots_m;
+// never destroyed: no buffer is freed from a static destructor after the
+// HIP runtime has gone
+std::map<SlotKey, std::unique_ptr<ScratchSlot>>& scratch_slots() {
+    static auto* m = new std::map<SlotKey, std::unique_ptr<ScratchSlot>>();
+    return *m;
+}
+ScratchSlot* scratch_slot(int dev, hipStream_t s) {
+    const std::thread::id tid = s == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
+    std::lock_guard<std::mutex> g(g_slots_m);
+    auto& p = scratch_slots()[SlotKey(dev, reinterpret_cast<uintptr_t>(s), tid)];
+    if (!p) p = std::make_unique<ScratchSlot>();
+    return p.get();
+}
+constexpr size_t kScratchGrain = size_t(2) << 20;   // kept buffers grow in 2 MiB steps
+
 struct Scratch {
     void* ptr = nullptr;
     hipStream_t s = nullptr;
+    bool owned = false;               // allocated for this call in stream order (under capture)
+    std::unique_lock<std::mutex> lk;  // the stream's kept buffer, held while the call enqueues
     ~Scratch() {
-        if (ptr) (void)hipFreeAsync(ptr, s);
+        if (owned && ptr) (void)hipFreeAsync(ptr, s);
     }
     hipError_t alloc(size_t bytes, hipStream_t stream) {
         s = stream;
         if (bytes == 0) return hipSuccess;
-        return hipMallocAsync(&ptr, bytes, stream);
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(stream, &cs);
+        if (e != hipSuccess) return e;
+        if (cs != hipStreamCaptureStatusNone) {
+            owned = true;
+            return hipMallocAsync(&ptr, bytes, stream);
+        }
+        int dev = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+        ScratchSlot* slot = scratch_slot(dev, stream);
+        lk = std::unique_lock<std::mutex>(slot->m);
+        if (slot->bytes < bytes) {
+            if (slot->ptr) {
+                // after the stream's earlier work, which may still use it
+                if ((e = hipFreeAsync(slot->ptr, stream)) != hipSuccess) return e;
+                slot->ptr = nullptr;
+                slot->bytes = 0;
+            }
+            const size_t want = (bytes + kScratchGrain - 1) / kScratchGrain * kScratchGrain;
+            if ((e = hipMallocAsync(&slot->ptr, want, stream)) != hipSuccess) {
+                slot->ptr = nullptr;
+                return e;
+            }
+            slot->bytes = want;
+        }
+        ptr = slot->ptr;
+        return hipSuccess;
     }
 };
 
@@ -341,6 +407,29 @@ int attn_profile_start(int max_launches) {
     g_prof.cap = max_launches;
     g_prof.n = 0;
     g_prof.on = true;
+    return ATTN_OK;
+}
+
+int attn_release_scratch(void) {
+    g_err.clear();
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "device query");
+    std::lock_guard<std::mutex> g(g_slots_m);
+    bool synced = false;
+    for (auto& kv : scratch_slots()) {
+        if (std::get<0>(kv.first) != dev) continue;
+        ScratchSlot& slot = *kv.second;
+        std::lock_guard<std::mutex> l(slot.m);   // no call is enqueuing with it
+        if (!slot.ptr) continue;
+        if (!synced) {   // the kept buffers' streams may be gone: wait for all work instead
+            if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "device synchronisation");
+            synced = true;
+        }
+        if ((e = hipFreeAsync(slot.ptr, nullptr)) != hipSuccess) return hip_fail(e, "scratch release");
+        slot.ptr = nullptr;
+        slot.bytes = 0;
+    }
     return ATTN_OK;
 }
 

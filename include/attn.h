@@ -27,14 +27,20 @@
  *  - A row with no allowed key yields out = 0 and lse = -inf, so that
  *    (0, -inf) is the identity of attn_merge.
  *  - Ownership: every pointer is caller-owned device memory (except where a
- *    host pointer is stated).  The library keeps no device state between
- *    calls.  Some calls need device scratch: they allocate it stream-ordered
- *    on `stream` (hipMallocAsync) before their first launch and free it on
- *    the same stream after their last one (hipFreeAsync), so it lives only
- *    as long as the call's work.  Each entry point below states its scratch
- *    in bytes as a formula of its sizes ("Scratch:"); every term is rounded
- *    up to a multiple of 256 bytes.  Entry points without a "Scratch:" line
- *    allocate nothing.
+ *    host pointer is stated).  Some calls need device scratch.  Each entry
+ *    point below states it in bytes as a formula of its sizes ("Scratch:");
+ *    every term is rounded up to a multiple of 256 bytes.  Entry points
+ *    without a "Scratch:" line use none.  The scratch comes from a buffer the
+ *    library keeps per (device, stream) -- per host thread as well for the
+ *    per-thread default stream -- and reuses from call to call: it is
+ *    allocated stream-ordered (hipMallocAsync) by the first call that needs
+ *    it, replaced by a larger one (the old one freed in stream order) when a
+ *    call needs more, rounded up to 2 MiB, and kept until
+ *    attn_release_scratch.  A call holds its stream's buffer while it
+ *    enqueues, so calls on one stream from several host threads take turns.
+ *    Under stream capture a call allocates its scratch stream-ordered and
+ *    frees it after its last launch instead (graph allocation nodes), and
+ *    leaves the kept buffers alone.
  *  - Streams: every call only enqueues work on `stream` (NULL = the null
  *    stream) and returns; there is no host synchronisation inside.
  *  - Errors: arguments are validated on the host before any HIP call; a call
@@ -464,6 +470,14 @@ int attn_ring_bwd_ex(const void* q, const void* k, const void* v, const void* ou
  */
 int attn_profile_start(int max_launches);
 int attn_profile_stop(float* ms, int cap);
+
+/*
+ * Free the scratch buffers the library keeps for the current device (see
+ * Ownership above): waits for all work on the device first, since the
+ * buffers' streams may have been destroyed, then frees each buffer.  Calls
+ * made afterwards allocate again.  Returns ATTN_OK or ATTN_ERR_HIP.
+ */
+int attn_release_scratch(void);
 
 /* Thread-local description of the last failure ("" if none). */
 const char* attn_last_error(void);

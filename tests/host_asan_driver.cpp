@@ -29,6 +29,12 @@ static size_t g_alloc_bytes = 0;      // scratch bytes requested since the last 
 static int g_allocs = 0;
 static bool g_fail_alloc = false;
 static bool g_fail_launch = false;
+// the stand-in reports stream capture by default: each call then allocates
+// exactly its scratch in stream order, which the size checks compare with
+// the formulas; kept_scratch_cases() turns it off
+static bool g_capturing = true;
+static int g_frees = 0;
+static int g_syncs = 0;
 static int g_failures = 0;
 
 #define CHECK(cond, ...)                                          \
@@ -78,6 +84,15 @@ hipError_t hipMallocAsync(void** p, size_t n, hipStream_t) {
 }
 hipError_t hipFreeAsync(void* p, hipStream_t) {
     std::free(p);
+    ++g_frees;
+    return hipSuccess;
+}
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* st) {
+    *st = g_capturing ? hipStreamCaptureStatusActive : hipStreamCaptureStatusNone;
+    return hipSuccess;
+}
+hipError_t hipDeviceSynchronize() {
+    ++g_syncs;
     return hipSuccess;
 }
 hipError_t hipGetDevice(int* d) {
@@ -606,6 +621,54 @@ static void failure_cases() {
     CHECK(rc == ATTN_OK && attn_profile_stop(ms, 8) == 1, "profiled launch count");
 }
 
+// Outside capture a call's scratch is the stream's kept buffer: allocated
+// once, replaced only when a call needs more, freed by attn_release_scratch.
+static void kept_scratch_cases() {
+    Buf m;
+    const int B = 1, H = 2, d = 64;
+    const int Tq = 300, Tkv = 300, Tbig = 4800;   // rotated copies of 0.15 MB and 2.5 MB
+    void* q = m.get((size_t)B * Tbig * H * d * 2);
+    void* k = m.get((size_t)B * Tbig * H * d * 2);
+    void* v = m.get((size_t)B * Tbig * H * d * 2);
+    void* out = m.get((size_t)B * Tbig * H * d * 2);
+    float* lse = (float*)m.get((size_t)B * H * Tbig * 4);
+    g_capturing = false;
+    CHECK(attn_release_scratch() == ATTN_OK, "release with nothing kept");
+    reset();
+    g_frees = 0;
+    for (int i = 0; i < 3; ++i)
+        CHECK(attn_fwd(q, k, v, out, lse, B, H, Tq, Tkv, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16, 0, nullptr) ==
+                  ATTN_OK, "kept scratch call %d (%s)", i, attn_last_error());
+    CHECK(g_allocs == 1 && g_frees == 0, "three equal calls: %d allocations, %d frees", g_allocs, g_frees);
+    // a smaller call reuses the buffer, a larger one replaces it
+    CHECK(attn_fwd(q, k, v, out, lse, B, H, Tq / 2, Tkv / 2, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16, 0,
+                   nullptr) == ATTN_OK, "smaller call");
+    CHECK(g_allocs == 1 && g_frees == 0, "smaller call: %d allocations, %d frees", g_allocs, g_frees);
+    CHECK(attn_fwd(q, k, v, out, lse, B, H, Tbig, Tbig, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16, 0,
+                   nullptr) == ATTN_OK, "larger call");
+    CHECK(g_allocs == 2 && g_frees == 1, "larger call: %d allocations, %d frees", g_allocs, g_frees);
+    CHECK(g_alloc_bytes % (size_t(2) << 20) == 0, "kept buffers grow in 2 MiB steps (%zu bytes)", g_alloc_bytes);
+    // the per-thread default stream keeps one buffer per host thread
+    CHECK(attn_fwd(q, k, v, out, lse, B, H, Tq, Tkv, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16, 0,
+                   (attn_stream_t)hipStreamPerThread) == ATTN_OK, "per-thread stream call");
+    CHECK(g_allocs == 3, "per-thread stream: %d allocations", g_allocs);
+    // an allocation failure while growing leaves nothing kept and returns ATTN_ERR_HIP
+    g_fail_alloc = true;
+    const int rc = attn_fwd(q, k, v, out, lse, B, H, Tbig, Tbig, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16,
+                            0, (attn_stream_t)hipStreamPerThread);
+    CHECK(rc == ATTN_ERR_HIP, "growth failure: rc %d", rc);
+    g_fail_alloc = false;
+    g_syncs = 0;
+    const int fr = g_frees;
+    CHECK(attn_release_scratch() == ATTN_OK, "release (%s)", attn_last_error());
+    CHECK(g_syncs == 1 && g_frees == fr + 1, "release: %d synchronisations, %d frees", g_syncs, g_frees - fr);
+    CHECK(attn_fwd(q, k, v, out, lse, B, H, Tq, Tkv, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16, 0, nullptr) ==
+              ATTN_OK, "call after release");
+    CHECK(g_allocs == 4, "call after release: %d allocations", g_allocs);
+    CHECK(attn_release_scratch() == ATTN_OK, "final release");
+    g_capturing = true;
+}
+
 int main() {
     invalid_cases();
     forward_cases();
@@ -614,6 +677,7 @@ int main() {
     backward_cases();
     decode_cases();
     failure_cases();
+    kept_scratch_cases();
     if (g_failures) {
         std::fprintf(stderr, "%d check(s) failed\n", g_failures);
         return 1;
