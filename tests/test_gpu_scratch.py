@@ -115,3 +115,39 @@ def test_release_then_call_again():
     again = bosa.attn_fwd(*a, causal=True, rope_base=10000.0)
     torch.cuda.synchronize()
     assert _same(again, ref)
+
+
+def test_two_host_threads_on_one_stream():
+    """Two host threads calling on the same stream at once (ctypes releases
+    the interpreter lock during a call, so the library's host code runs
+    concurrently): each call holds the stream's buffer while it enqueues, so
+    its kernels never share the scratch with the other thread's, and every
+    result has the bits of the same call made alone."""
+    import threading
+    a = _qkv(2500, 4, 7700)
+    b = _qkv(4000, 4, 7800)
+    ref_a = bosa.attn_fwd(*a, causal=True, rope_base=10000.0)
+    ref_b = bosa.attn_fwd(*b, causal=True, rope_base=10000.0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    results = {0: [], 1: []}
+    errors = []
+
+    def worker(idx, x):
+        try:
+            for _ in range(12):
+                results[idx].append(bosa.attn_fwd(*x, causal=True, rope_base=10000.0, stream=stream))
+        except Exception as e:   # surfaced below
+            errors.append(e)
+
+    ts = [threading.Thread(target=worker, args=(0, a)), threading.Thread(target=worker, args=(1, b))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for r in results[0]:
+        assert _same(r, ref_a)
+    for r in results[1]:
+        assert _same(r, ref_b)
