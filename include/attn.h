@@ -42,7 +42,11 @@
  *    frees it after its last launch instead (graph allocation nodes), and
  *    leaves the kept buffers alone.
  *  - Streams: every call only enqueues work on `stream` (NULL = the null
- *    stream) and returns; there is no host synchronisation inside.
+ *    stream) and returns; there is no host synchronisation inside, except
+ *    that a call which must replace its stream's scratch buffer by a larger
+ *    one frees the old buffer in stream order, which can wait for the
+ *    stream's earlier work (once per growth), and attn_release_scratch
+ *    waits for the device.
  *  - Errors: arguments are validated on the host before any HIP call; a call
  *    that fails validation returns ATTN_ERR_INVALID_ARG or
  *    ATTN_ERR_UNSUPPORTED, enqueues nothing, and attn_last_error() describes
