@@ -113,18 +113,22 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int cc) {
 
 // Workgroup renumbering for the eight XCDs: workgroup b runs on XCD b % 8,
 // and the result l gives the (batch row, head) pair l / nt and its tile
-// l % nt.  Each XCD receives whole pairs (their tiles share its L2): a
-// contiguous range of them, or, with `spread` (the pairs' work differs, as
-// with a key-padding length per batch row) and a pair count that is a
-// multiple of 8, the pairs round-robin, so that one batch row's pairs are
-// spread over all XCDs.
+// l % nt (tiles heaviest first).  With a multiple of 8 pairs each XCD
+// receives whole pairs (their tiles share its L2): a contiguous range of
+// them, or, with `spread` (the pairs' work differs, as with a key-padding
+// length per batch row), the pairs round-robin, so that one batch row's pairs
+// are spread over all XCDs.  With any other pair count contiguous ranges
+// would cut pairs into a heavy piece on one XCD and a light one on another;
+// there workgroup b takes tile rank b / n of pair b % n (n pairs), every 8th
+// tile of the list ordered heaviest first over all pairs.
 __device__ __forceinline__ int xcd_order(int bid, int nt, bool spread) {
-    if (spread && (((int)gridDim.x / nt) & 7) == 0) {
+    const int npairs = (int)gridDim.x / nt;
+    if (npairs & 7) return (bid % npairs) * nt + bid / npairs;
+    if (spread) {
         const int k = bid >> 3;
         return ((k / nt) * 8 + (bid & 7)) * nt + k % nt;
     }
-    const int full = (int)gridDim.x & ~7;
-    return bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
+    return (bid & 7) * ((int)gridDim.x >> 3) + (bid >> 3);
 }
 
 // ============================================================== dQ

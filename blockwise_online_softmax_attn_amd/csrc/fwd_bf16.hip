@@ -275,27 +275,32 @@ __device__ __forceinline__ void accumulate_pv(uint32_t Vt, const uint32_t (&voff
 
 // Query tile, batch row and head of this workgroup.  Workgroup b is
 // dispatched to XCD b % 8 (each XCD has its own L2), so the k-th workgroup of
-// XCD x is b = 8k + x.  Each XCD takes whole (batch row, head) pairs, so the
-// query tiles of one head share that XCD's L2 for K and V: a contiguous range
-// of pairs, or, when the pairs' work differs (`spread`: the batch rows have
-// their own key-padding lengths), pairs round-robin (pair 8j + x is its j-th),
-// so that the pairs of one batch row are spread over all XCDs instead of
-// filling some of them.  Within a pair the heaviest query tiles (most keys
-// under causal order) come first.  Round-robin needs a pair count that is a
-// multiple of 8.
+// XCD x is b = 8k + x.  With a multiple of 8 (batch row, head) pairs each XCD
+// takes whole pairs, so the query tiles of one head share that XCD's L2 for K
+// and V: a contiguous range of pairs, or, when the pairs' work differs
+// (`spread`: the batch rows have their own key-padding lengths), pairs
+// round-robin (pair 8j + x is its j-th), so that the pairs of one batch row
+// are spread over all XCDs instead of filling some of them.  Within a pair
+// the heaviest query tiles (most keys under causal order) come first.  With
+// any other pair count a pair's tiles would be cut into contiguous pieces on
+// different XCDs, the heavy piece on one and the light on another; there
+// workgroup b takes tile rank b / n of pair b % n (n pairs), so every XCD gets
+// every 8th tile of the list ordered heaviest first over all pairs (with 4
+// pairs, XCDs x and x + 4 share pair x % 4).
 __device__ __forceinline__ void wg_tile(const FwdParams& p, bool spread, int& qt, int& b, int& h) {
     const int nq = p.n_qtiles;
     const int bid = blockIdx.x;
     const int npairs = (int)gridDim.x / nq;
     int bh, t;
-    if (spread && (npairs & 7) == 0) {
+    if (npairs & 7) {
+        bh = bid % npairs;
+        t = bid / npairs;
+    } else if (spread) {
         const int k = bid >> 3;
         bh = (k / nq) * 8 + (bid & 7);
         t = k % nq;
     } else {
-        int l = bid;
-        const int full = (int)gridDim.x & ~7;
-        if (l < full) l = (l & 7) * (full >> 3) + (l >> 3);
+        const int l = (bid & 7) * ((int)gridDim.x >> 3) + (bid >> 3);
         bh = l / nq;
         t = l % nq;
     }

@@ -104,6 +104,28 @@ def test_encoder_full_size_sampled():
             compare(oc[b:b + 1, rows, h:h + 1], lc[b:b + 1, h:h + 1, rows], ro, rl, "bf16", f"b{b}h{h}")
 
 
+def test_head_parallel_share_full_size_sampled():
+    """One rank's share under the head-parallel (Ulysses) layout of the 128K
+    sequence: 4 of 32 heads over all 131072 tokens, causal, RoPE, in one
+    attn_fwd call (the call that rank makes after its all-to-all).  Sampled
+    rows of every head against the oracle; every row finite."""
+    w = workloads.WORKLOADS[6]
+    note(f"{w.name}: drawing inputs")
+    q, k, v = (workloads.draw_tokens(w, t, range(w.n_chunks)) for t in (0, 1, 2))
+    out, lse = bosa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(6)
+    rows = _sample_rows(w.T, w.chunk, rng, extra=16)
+    oc, lc = out.cpu(), lse.cpu()
+    for h in range(w.H):
+        nk = int(rows.max()) + 1
+        note(f"  oracle: {len(rows)} rows of head {h}")
+        ro, rl = oracle.sdpa(np64(q[:, rows, h:h + 1]), np64(k[:, :nk, h:h + 1]), np64(v[:, :nk, h:h + 1]), rows,
+                             np.arange(nk), causal=True, rope_base=w.rope_base, dtype="bf16")
+        compare(oc[:, rows, h:h + 1], lc[:, h:h + 1, rows], ro, rl, "bf16", f"head{h}")
+
+
 def test_ring_backward_full_size_sampled():
     """The backward of the 128K zigzag share (rank 0) in the launch
     configuration `bench.py --pass bwd` times: attn_ring_bwd (bf16 gradients)

@@ -16,10 +16,12 @@ float32 from N(0, sigma^2) and rounded once (round-to-nearest-even) to the
 workload dtype; the same rounded values go to the GPU and, widened to float64,
 to the oracle.
 
-The five workloads are the shapes the attention-forward measurements are
-quoted on (a small fp32 case, a GPT-2-small-shaped causal case with key
-padding, an 8K ring-attention share, a 16K bidirectional encoder with key
-padding, and one rank's zigzag share of an 8-way ring at 128K context).
+Workloads 0-4 are the shapes the attention-forward measurements are quoted
+on (a small fp32 case, a GPT-2-small-shaped causal case with key padding, an
+8K ring-attention share, a 16K bidirectional encoder with key padding, and
+one rank's zigzag share of an 8-way ring at 128K context); 5 is one decoding
+step over a static cache, and 6 one rank's share of the same 128K sequence
+under the head-parallel layout (4 of 32 heads, every token).
 """
 from __future__ import annotations
 
@@ -78,6 +80,11 @@ WORKLOADS = {
                 128, True, 10000.0, 1.0, None, 8, 0, True, 8192),
     5: Workload(5, "decode_step_bf16_b8_h32_d128_cache32768_rope", "bf16", 8, 32, 32768, 128, True, 10000.0,
                 1.0, (16384, 32000), 1, 0, False, 4096, decode=True),
+    # one rank's share under the head-parallel (Ulysses) layout of the same
+    # 128K sequence: after the all-to-all a rank holds H/P = 32/8 heads of
+    # every token, so its attention is one call over the whole sequence
+    6: Workload(6, "ulysses_share_bf16_h4_d128_T131072_causal_rope", "bf16", 1, 4, 131072, 128, True, 10000.0,
+                1.0, None, 1, 0, False, 8192),
 }
 
 
