@@ -8,7 +8,8 @@ half run up to sixteen to a launch of the chained kernel, which carries the
 softmax state across them: 3 launches per step, the last launch of each half
 writing the bf16 output).  One step is one whole
 share (attn_ring_fwd), inputs resident in HBM.  `--workload N` selects another
-of the five workloads.
+workload (workloads.py: 0-4 the forward configurations, 5 one decoding step,
+6 the same 128K sequence's share under the head-parallel layout).
 
 value  = algorithmic TFLOP/s of the step: 4 d FLOPs per allowed (query, key)
          pair (two contractions, 2 FLOPs per multiply-add); masked work that
