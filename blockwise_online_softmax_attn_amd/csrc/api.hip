@@ -313,6 +313,12 @@ struct BwdCall {
     // ring sub-calls: the first to touch a gradient's rows writes them (the
     // flags without ATTN_ACCUMULATE), later ones add
     int write_dq = 0, write_dkdv = 0;
+    // the final bf16 dk, dv of this call's key rows (no other call adds to
+    // them), written by the dK/dV kernel instead of dk / dv; dk_rope: the
+    // (cos, sin) rows of those keys when dk is to be rotated back
+    uint16_t* dk_out = nullptr;
+    uint16_t* dv_out = nullptr;
+    const double2* dk_rope = nullptr;
 };
 
 // Enqueue the dQ and dK/dV kernels of one sub-call; `list` is scratch of
@@ -334,6 +340,9 @@ int enqueue_bwd(const BwdCall& c, int* list, hipStream_t s) {
     p.win_right = c.win_right;
     p.alibi = c.alibi;
     p.sqrt_d = (float)std::sqrt((double)c.d);
+    p.dk_out = c.dk_out;
+    p.dv_out = c.dv_out;
+    p.dk_rope = c.dk_rope;
     hipError_t e;
     if (list) {
         const int ntk = (c.Tkv + kTile - 1) / kTile;
@@ -964,8 +973,11 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
     }
     const bool rope = rope_base > 0.0;
     // float32 results go straight to the caller's buffers unless they must
-    // still be rotated back (dq, dk with RoPE) or cast (bf16 outputs)
-    const bool dq_direct = f32 && !rope, dk_direct = dq_direct, dv_direct = dq_direct;
+    // still be rotated back (dq, dk with RoPE) or cast (bf16 outputs); bf16
+    // dk and dv are written by the dK/dV kernel itself (rounded once, dk
+    // rotated back first), so only dq goes through a finalize pass
+    const bool dq_direct = f32 && !rope, kv_final = !f32;
+    const bool dk_direct = dq_direct || kv_final, dv_direct = dk_direct;
     const size_t ld_b = align_up((size_t)B * H * Tq * sizeof(float2));
     const size_t tab_q = rope ? align_up((size_t)Tq * (d / 2) * sizeof(double2)) : 0;
     const size_t tab_k = rope ? align_up((size_t)Tkv * (d / 2) * sizeof(double2)) : 0;
@@ -1019,6 +1031,12 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
     c.flags = (flags & ATTN_NO_TILE_SKIP) | (accum && dq_direct ? ATTN_ACCUMULATE : 0u);
     c.q_bstride = (long long)Tq * rs; c.kv_bstride = (long long)Tkv * rs; c.kpm_bstride = Tkv;
     c.lse_bstride = (long long)H * Tq; c.lse_hstride = Tq; c.amask_stride = Tkv;
+    if (kv_final) {
+        c.dk = c.dv = nullptr;
+        c.dk_out = (uint16_t*)dk;
+        c.dv_out = (uint16_t*)dv;
+        c.dk_rope = rope ? tk : nullptr;
+    }
     if (int rc = enqueue_bwd(c, list, s)) return rc;
     // finalize: rotate back, cast, accumulate
     const int tobf = f32 ? 0 : 1;
@@ -1153,6 +1171,22 @@ int attn_ring_bwd_ex(const void* q, const void* k, const void* v, const void* ou
         if (e == hipSuccess) e = launch_rope_copy_bf16(k, kr, tk, B, T, H, d, s);
         if (e != hipSuccess) return hip_fail(e, "rotary launch");
     }
+    // A key block only one sub-call touches gets its final bf16 dk, dv from
+    // that sub-call's dK/dV kernel (rounded once, dk rotated back first, as
+    // the finalize pass would); the finalize covers the other rows.
+    const int tobf = (flags & ATTN_OUT_F32) ? 0 : 1;
+    std::vector<int> kv_final(n_live, 0);
+    std::vector<std::pair<int, int>> final_rows;   // (first row, rows)
+    if (disjoint && tobf)
+        for (int i = 0; i < n_live; ++i) {
+            int touched = 0;
+            for (int j = 0; j < n_live; ++j)
+                touched += plan[j].kv_pos0 == plan[i].kv_pos0 && plan[j].kv_rows == plan[i].kv_rows;
+            if (touched == 1) {
+                kv_final[i] = 1;
+                final_rows.push_back({(int)plan[i].kv_pos0, plan[i].kv_rows});
+            }
+        }
     const size_t esz = 2;
     for (int i = 0; i < n_live; ++i) {
         const attn_ring_call& pc = plan[i];
@@ -1175,17 +1209,29 @@ int attn_ring_bwd_ex(const void* q, const void* k, const void* v, const void* ou
         c.flags = (flags & ATTN_NO_TILE_SKIP) | ATTN_ACCUMULATE;
         c.write_dq = write_dq[i];
         c.write_dkdv = write_kv[i];
+        if (kv_final[i]) {
+            c.dk = c.dv = nullptr;
+            c.dk_out = (uint16_t*)dk + (size_t)pc.kv_pos0 * rs;
+            c.dv_out = (uint16_t*)dv + (size_t)pc.kv_pos0 * rs;
+            c.dk_rope = rope ? tk + (size_t)pc.kv_pos0 * (d / 2) : nullptr;
+        }
         c.q_bstride = (long long)Tl * rs; c.kv_bstride = (long long)T * rs; c.kpm_bstride = T;
         c.lse_bstride = (long long)H * Tl; c.lse_hstride = Tl; c.amask_stride = 0;
         const size_t lb = kpm_list_bytes(c.kpm, dtype, flags, B, c.Tkv);
         if (int rc = enqueue_bwd(c, lb ? (int*)(base + lst_off[i]) : nullptr, s)) return rc;
     }
-    const int tobf = (flags & ATTN_OUT_F32) ? 0 : 1;
     e = launch_bwd_finalize(gq, dq, rope ? tq : nullptr, B, Tl, H, d, (long long)Tl * rs, (long long)Tl * rs, tobf, 0, s);
-    if (e == hipSuccess)
-        e = launch_bwd_finalize(gk, dk, rope ? tk : nullptr, B, T, H, d, (long long)T * rs, (long long)T * rs, tobf, 0, s);
-    if (e == hipSuccess)
-        e = launch_bwd_finalize(gv, dv, nullptr, B, T, H, d, (long long)T * rs, (long long)T * rs, tobf, 0, s);
+    const size_t osz = tobf ? 2 : 4;
+    for (const auto& r : complement_rows(final_rows, T)) {
+        const int r0 = r.first, nr = r.second - r.first;
+        if (e == hipSuccess)
+            e = launch_bwd_finalize(gk + (size_t)r0 * rs, (char*)dk + (size_t)r0 * rs * osz,
+                                    rope ? tk + (size_t)r0 * (d / 2) : nullptr, B, nr, H, d, (long long)T * rs,
+                                    (long long)T * rs, tobf, 0, s);
+        if (e == hipSuccess)
+            e = launch_bwd_finalize(gv + (size_t)r0 * rs, (char*)dv + (size_t)r0 * rs * osz, nullptr, B, nr, H, d,
+                                    (long long)T * rs, (long long)T * rs, tobf, 0, s);
+    }
     return e == hipSuccess ? ATTN_OK : hip_fail(e, "finalize launch");
 }
 

@@ -595,8 +595,37 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     if (!kvalid) return;
     // A key excluded by the key-padding mask gets exactly zero (its lane may
     // hold anything: its scores were not masked, since they reach no other key).
-    float* og = (roleA ? p.dv : p.dk) + b * p.kv_bstride + (long long)kj * rs + (long long)h * D;
     const float sc = roleA ? 1.f : p.scale;
+    uint16_t* fb = roleA ? p.dv_out : p.dk_out;
+    if (fb) {
+        // the final bf16 gradient: the float32 value as the float32 path
+        // stores it, then (dk with RoPE) rotated back in float64, rounded once
+        fb += b * p.kv_bstride + (long long)kj * rs + (long long)h * D;
+        const double2* tr = (!roleA && p.dk_rope) ? p.dk_rope + (long long)kj * (D / 2) : nullptr;
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = db * 32 + 8 * g + 4 * hh;
+                float4 r = make_float4(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc, acc[db][4 * g + 2] * sc,
+                                       acc[db][4 * g + 3] * sc);
+                if (kmasked) r = make_float4(0.f, 0.f, 0.f, 0.f);
+                uint2 u;
+                if (tr) {
+                    const double2 ca = tr[c / 2], cb = tr[c / 2 + 1];
+                    const double2 y0 = rot64(r.x, r.y, ca.x, -ca.y);
+                    const double2 y1 = rot64(r.z, r.w, cb.x, -cb.y);
+                    u = make_uint2(bf16_bits_rn(y0.x) | (bf16_bits_rn(y0.y) << 16),
+                                   bf16_bits_rn(y1.x) | (bf16_bits_rn(y1.y) << 16));
+                } else {
+                    u = make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
+                }
+                *(uint2*)(fb + c) = u;
+            }
+        }
+        return;
+    }
+    float* og = (roleA ? p.dv : p.dk) + b * p.kv_bstride + (long long)kj * rs + (long long)h * D;
     const bool accum = (p.flags & ATTN_ACCUMULATE) != 0;
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {

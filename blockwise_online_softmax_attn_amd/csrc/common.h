@@ -196,6 +196,13 @@ struct BwdParams {
     long long win_left, win_right;   // sliding window as in FwdParams; -1 = no limit
     const float* alibi;        // [H] slopes or null
     float sqrt_d;
+    // dK/dV kernel: when set, the final bf16 gradients of a key block no other
+    // call adds to ((B, Tkv, H, d), strides of k), written instead of dk / dv:
+    // dv rounded once, dk rotated back by R(-pos) with the float64 (cos, sin)
+    // rows of dk_rope (row j at key j, or null without RoPE) and rounded once
+    uint16_t* dk_out;
+    uint16_t* dv_out;
+    const double2* dk_rope;
 };
 
 // Entry of a live-tile list: tile index, top bit set when no key of the tile is masked.

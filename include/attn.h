@@ -397,11 +397,14 @@ int attn_ring_fwd_ex(const void* q, const void* k, const void* v, void* out, flo
  * Scratch:       the per-row (lse, delta) pairs, 8 * B * H * Tq; with
  *                rope_base > 0 the float64 (cos, sin) tables
  *                (Tq + Tkv) * (d/2) * 16 and the rotated q and k,
- *                2 * B * (Tq + Tkv) * H * d; float32 gradients
- *                4 * B * H * d * (Tq + 2 * Tkv) unless the call writes
- *                float32 gradients without RoPE (then the kernels write
- *                dq, dk, dv directly); with kpm (without ATTN_NO_TILE_SKIP)
- *                the live key-tile list, 4 * B * (ceil(Tkv / 64) + 2).
+ *                2 * B * (Tq + Tkv) * H * d; the float32 dq,
+ *                4 * B * H * d * Tq, unless the call writes float32
+ *                gradients without RoPE (then the kernels write dq, dk, dv
+ *                directly); the float32 dk and dv, 8 * B * H * d * Tkv, only
+ *                when it writes float32 gradients with RoPE (bf16 dk and dv
+ *                are written by the dK/dV kernel itself); with kpm (without
+ *                ATTN_NO_TILE_SKIP) the live key-tile list,
+ *                4 * B * (ceil(Tkv / 64) + 2).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
              const float* lse, void* dq, void* dk, void* dv,

@@ -35,6 +35,7 @@ static bool g_fail_launch = false;
 static bool g_capturing = true;
 static int g_frees = 0;
 static int g_syncs = 0;
+static int g_kv_final = 0;     // dK/dV launches that wrote final bf16 rows
 static int g_failures = 0;
 
 #define CHECK(cond, ...)                                          \
@@ -263,8 +264,16 @@ hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t) {
 }
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t) {
     bwd_common(p, d);
-    rows(p.dk, p.B, p.Tkv, p.H, d, p.kv_bstride, p.row_stride, 4, true);
-    rows(p.dv, p.B, p.Tkv, p.H, d, p.kv_bstride, p.row_stride, 4, true);
+    if (p.dk_out || p.dv_out) {
+        CHECK(p.dk_out && p.dv_out && !p.dk && !p.dv, "dK/dV launch with a mix of final and float32 outputs");
+        rows(p.dk_out, p.B, p.Tkv, p.H, d, p.kv_bstride, p.row_stride, 2, true);
+        rows(p.dv_out, p.B, p.Tkv, p.H, d, p.kv_bstride, p.row_stride, 2, true);
+        if (p.dk_rope) touch(p.dk_rope, (size_t)p.Tkv * (d / 2) * sizeof(double2), false);
+        ++g_kv_final;
+    } else {
+        rows(p.dk, p.B, p.Tkv, p.H, d, p.kv_bstride, p.row_stride, 4, true);
+        rows(p.dv, p.B, p.Tkv, p.H, d, p.kv_bstride, p.row_stride, 4, true);
+    }
     return launched();
 }
 hipError_t launch_bwd_delta(const void* dout, const void* out, const float* lse, float2* ld2, int B, int H, int Tq,
@@ -535,18 +544,20 @@ static void backward_cases() {
                 size_t want = au((size_t)B * H * Tq * 8);
                 if (rope) want += au((size_t)Tq * (d / 2) * 16) + au((size_t)Tkv * (d / 2) * 16) +
                                   au((size_t)B * Tq * H * d * 2) + au((size_t)B * Tkv * H * d * 2);
-                if (!(f32 && !rope))
-                    want += au((size_t)B * Tq * H * d * 4) + 2 * au((size_t)B * Tkv * H * d * 4);
+                if (!(f32 && !rope)) want += au((size_t)B * Tq * H * d * 4);
+                if (f32 && rope) want += 2 * au((size_t)B * Tkv * H * d * 4);
                 if (kp) want += au((size_t)B * ((Tkv + 63) / 64 + 2) * 4);
                 CHECK(g_alloc_bytes == want, "bwd f32 %d rope %d kpm %d: scratch %zu, formula %zu", f32, rope, kp,
                       g_alloc_bytes, want);
             }
-    // ring backward, every rank
+    // ring backward, every rank; key blocks a single sub-call touches get
+    // their final bf16 rows from that sub-call (none with float32 outputs)
     for (int P : {2, 3, 4})
         for (int zz : {0, 1})
-            for (int win : {0, 1}) {
+            for (int win : {0, 1})
+              for (int B : {1, 2}) {
                 Buf m;
-                const int B = 1, H = 2, d = 64, c = 29, T = (zz ? 2 * P : P) * c, Tl = T / P;
+                const int H = 2, d = 64, c = 29, T = (zz ? 2 * P : P) * c, Tl = T / P;
                 void* q = m.get((size_t)B * Tl * H * d * 2);
                 void* k = m.get((size_t)B * T * H * d * 2);
                 void* v = m.get((size_t)B * T * H * d * 2);
@@ -558,12 +569,23 @@ static void backward_cases() {
                 void* dv = m.get((size_t)B * T * H * d * 2);
                 uint8_t* kpm = (uint8_t*)m.get((size_t)B * T);
                 attn_variant var{15, -1, nullptr};
+                void* dk32 = m.get((size_t)B * T * H * d * 4);
+                void* dv32 = m.get((size_t)B * T * H * d * 4);
+                void* dq32 = m.get((size_t)B * Tl * H * d * 4);
                 for (int rank = 0; rank < P; ++rank) {
-                    const int rc = attn_ring_bwd_ex(q, k, v, out, dout, lse, dq, dk, dv, B, H, T, d, P, rank, zz, 1,
-                                                    kpm, 1e4, ATTN_BF16, 0, win ? &var : nullptr, nullptr);
+                    g_kv_final = 0;
+                    int rc = attn_ring_bwd_ex(q, k, v, out, dout, lse, dq, dk, dv, B, H, T, d, P, rank, zz, 1,
+                                              kpm, 1e4, ATTN_BF16, 0, win ? &var : nullptr, nullptr);
                     CHECK(rc == ATTN_OK, "ring bwd rc %d (%s)", rc, attn_last_error());
+                    CHECK(win || g_kv_final > 0, "ring bwd P %d zz %d rank %d: no key block written final", P, zz,
+                          rank);
+                    g_kv_final = 0;
+                    rc = attn_ring_bwd_ex(q, k, v, out, dout, lse, dq32, dk32, dv32, B, H, T, d, P, rank, zz, 1, kpm,
+                                          1e4, ATTN_BF16, ATTN_OUT_F32, win ? &var : nullptr, nullptr);
+                    CHECK(rc == ATTN_OK && g_kv_final == 0, "ring bwd float32 rc %d, %d final launches", rc,
+                          g_kv_final);
                 }
-            }
+              }
 }
 
 static void decode_cases() {
