@@ -10,8 +10,6 @@
 #include <memory>
 #include <mutex>
 #include <string>
-#include <thread>
-#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -51,9 +49,8 @@ constexpr int kTile = 64;   // key tile of the bf16 kernel (live-tile list granu
 constexpr int kChainRows = 256;   // query rows per workgroup of the chained bf16 kernel
 
 // Device scratch of one call.  Outside stream capture it is the calling
-// stream's buffer, which the library keeps (one per device and stream; per
-// host thread as well for the per-thread default stream) and reuses from call
-// to call, growing it when a call needs more.  Freeing device memory at the
+// stream's buffer, which the library keeps (one per device and stream) and
+// reuses from call to call, growing it when a call needs more.  Freeing device memory at the
 // end of every call (hipFreeAsync) waits here for the stream's pending work,
 // which made each call synchronous with the one before it.  A call holds the
 // buffer's lock while it enqueues, so calls from several host threads on one
@@ -61,14 +58,17 @@ constexpr int kChainRows = 256;   // query rows per workgroup of the chained bf1
 // stream and never share the buffer with another call's.  Under stream
 // capture the scratch is allocated and freed in stream order instead (graph
 // allocation nodes), since a captured graph must not keep pointing at a
-// buffer that a later, larger call replaces.  attn_release_scratch frees the
-// kept buffers of the current device.
+// buffer that a later, larger call replaces; so it is on the per-thread
+// default stream, whose one handle names another stream in every host thread
+// and whose thread may end with work still queued on it, so that a buffer
+// kept for it could not be handed safely to the next thread.
+// attn_release_scratch frees the kept buffers of the current device.
 struct ScratchSlot {
     std::mutex m;
     void* ptr = nullptr;
     size_t bytes = 0;
 };
-using SlotKey = std::tuple<int, uintptr_t, std::thread::id>;
+using SlotKey = std::pair<int, uintptr_t>;
 std::mutex g_slots_m;
 // never destroyed: no buffer is freed from a static destructor after the
 // HIP runtime has gone
@@ -77,9 +77,8 @@ std::map<SlotKey, std::unique_ptr<ScratchSlot>>& scratch_slots() {
     return *m;
 }
 ScratchSlot* scratch_slot(int dev, hipStream_t s) {
-    const std::thread::id tid = s == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
     std::lock_guard<std::mutex> g(g_slots_m);
-    auto& p = scratch_slots()[SlotKey(dev, reinterpret_cast<uintptr_t>(s), tid)];
+    auto& p = scratch_slots()[SlotKey(dev, reinterpret_cast<uintptr_t>(s))];
     if (!p) p = std::make_unique<ScratchSlot>();
     return p.get();
 }
@@ -88,7 +87,7 @@ constexpr size_t kScratchGrain = size_t(2) << 20;   // kept buffers grow in 2 Mi
 struct Scratch {
     void* ptr = nullptr;
     hipStream_t s = nullptr;
-    bool owned = false;               // allocated for this call in stream order (under capture)
+    bool owned = false;   // allocated for this call in stream order (capture, per-thread stream)
     std::unique_lock<std::mutex> lk;  // the stream's kept buffer, held while the call enqueues
     ~Scratch() {
         if (owned && ptr) (void)hipFreeAsync(ptr, s);
@@ -99,7 +98,7 @@ struct Scratch {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         hipError_t e = hipStreamIsCapturing(stream, &cs);
         if (e != hipSuccess) return e;
-        if (cs != hipStreamCaptureStatusNone) {
+        if (cs != hipStreamCaptureStatusNone || stream == hipStreamPerThread) {
             owned = true;
             return hipMallocAsync(&ptr, bytes, stream);
         }
@@ -427,7 +426,7 @@ int attn_release_scratch(void) {
     std::lock_guard<std::mutex> g(g_slots_m);
     bool synced = false;
     for (auto& kv : scratch_slots()) {
-        if (std::get<0>(kv.first) != dev) continue;
+        if (kv.first.first != dev) continue;
         ScratchSlot& slot = *kv.second;
         std::lock_guard<std::mutex> l(slot.m);   // no call is enqueuing with it
         if (!slot.ptr) continue;

@@ -31,22 +31,23 @@
  *    point below states it in bytes as a formula of its sizes ("Scratch:");
  *    every term is rounded up to a multiple of 256 bytes.  Entry points
  *    without a "Scratch:" line use none.  The scratch comes from a buffer the
- *    library keeps per (device, stream) -- per host thread as well for the
- *    per-thread default stream -- and reuses from call to call: it is
+ *    library keeps per (device, stream) and reuses from call to call: it is
  *    allocated stream-ordered (hipMallocAsync) by the first call that needs
  *    it, replaced by a larger one (the old one freed in stream order) when a
  *    call needs more, rounded up to 2 MiB, and kept until
  *    attn_release_scratch.  A call holds its stream's buffer while it
  *    enqueues, so calls on one stream from several host threads take turns.
- *    Under stream capture a call allocates its scratch stream-ordered and
- *    frees it after its last launch instead (graph allocation nodes), and
- *    leaves the kept buffers alone.
+ *    Under stream capture (graph allocation nodes) and on the per-thread
+ *    default stream (hipStreamPerThread) a call allocates its scratch
+ *    stream-ordered and frees it after its last launch instead, and leaves
+ *    the kept buffers alone.
  *  - Streams: every call only enqueues work on `stream` (NULL = the null
  *    stream) and returns; there is no host synchronisation inside, except
  *    that a call which must replace its stream's scratch buffer by a larger
  *    one frees the old buffer in stream order, which can wait for the
- *    stream's earlier work (once per growth), and attn_release_scratch
- *    waits for the device.
+ *    stream's earlier work (once per growth), a call with scratch on the
+ *    per-thread default stream can wait likewise when it frees it, and
+ *    attn_release_scratch waits for the device.
  *  - Errors: arguments are validated on the host before any HIP call; a call
  *    that fails validation returns ATTN_ERR_INVALID_ARG or
  *    ATTN_ERR_UNSUPPORTED, enqueues nothing, and attn_last_error() describes

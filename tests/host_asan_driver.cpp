@@ -670,15 +670,23 @@ static void kept_scratch_cases() {
                    nullptr) == ATTN_OK, "larger call");
     CHECK(g_allocs == 2 && g_frees == 1, "larger call: %d allocations, %d frees", g_allocs, g_frees);
     CHECK(g_alloc_bytes % (size_t(2) << 20) == 0, "kept buffers grow in 2 MiB steps (%zu bytes)", g_alloc_bytes);
-    // the per-thread default stream keeps one buffer per host thread
-    CHECK(attn_fwd(q, k, v, out, lse, B, H, Tq, Tkv, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16, 0,
-                   (attn_stream_t)hipStreamPerThread) == ATTN_OK, "per-thread stream call");
-    CHECK(g_allocs == 3, "per-thread stream: %d allocations", g_allocs);
-    // an allocation failure while growing leaves nothing kept and returns ATTN_ERR_HIP
+    // the per-thread default stream keeps nothing: each call allocates its
+    // scratch and frees it after its last launch
+    for (int i = 0; i < 2; ++i)
+        CHECK(attn_fwd(q, k, v, out, lse, B, H, Tq, Tkv, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16, 0,
+                       (attn_stream_t)hipStreamPerThread) == ATTN_OK, "per-thread stream call %d", i);
+    CHECK(g_allocs == 4 && g_frees == 3, "per-thread stream: %d allocations, %d frees", g_allocs, g_frees);
+    // another stream keeps a buffer of its own; an allocation failure while
+    // growing it leaves nothing kept there and returns ATTN_ERR_HIP
+    const attn_stream_t s2 = (attn_stream_t)(uintptr_t)0x7000;
+    CHECK(attn_fwd(q, k, v, out, lse, B, H, Tq, Tkv, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16, 0, s2) ==
+              ATTN_OK, "second stream call");
+    CHECK(g_allocs == 5 && g_frees == 3, "second stream: %d allocations, %d frees", g_allocs, g_frees);
     g_fail_alloc = true;
     const int rc = attn_fwd(q, k, v, out, lse, B, H, Tbig, Tbig, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16,
-                            0, (attn_stream_t)hipStreamPerThread);
+                            0, s2);
     CHECK(rc == ATTN_ERR_HIP, "growth failure: rc %d", rc);
+    CHECK(g_frees == 4, "growth failure frees the old buffer: %d frees", g_frees);
     g_fail_alloc = false;
     g_syncs = 0;
     const int fr = g_frees;
@@ -686,7 +694,7 @@ static void kept_scratch_cases() {
     CHECK(g_syncs == 1 && g_frees == fr + 1, "release: %d synchronisations, %d frees", g_syncs, g_frees - fr);
     CHECK(attn_fwd(q, k, v, out, lse, B, H, Tq, Tkv, d, 0, 0, 1, nullptr, nullptr, 1e4, ATTN_BF16, 0, nullptr) ==
               ATTN_OK, "call after release");
-    CHECK(g_allocs == 4, "call after release: %d allocations", g_allocs);
+    CHECK(g_allocs == 6, "call after release: %d allocations", g_allocs);
     CHECK(attn_release_scratch() == ATTN_OK, "final release");
     g_capturing = true;
 }

@@ -5,7 +5,8 @@ call waited for the stream's pending work, which made each call synchronous
 with the one before it.  These tests check that calls run ahead of the GPU,
 that two streams with their own buffers give the same bits as one stream,
 that a graph captured with the library's calls replays correctly between
-eager calls, and that releasing the buffers leaves later calls correct.
+eager calls, that releasing the buffers leaves later calls correct, and that
+calls on the per-thread default stream, which keep no buffer, are correct.
 """
 import time
 
@@ -151,3 +152,37 @@ def test_two_host_threads_on_one_stream():
         assert _same(r, ref_a)
     for r in results[1]:
         assert _same(r, ref_b)
+
+
+class _PerThreadStream:
+    cuda_stream = 2   # hipStreamPerThread: a different stream in every host thread
+
+
+def test_per_thread_default_stream():
+    """Calls on the per-thread default stream allocate and free their scratch
+    per call, since a buffer kept for that one handle could pass from a host
+    thread that ended with work queued to the next thread that reuses its id.
+    Three threads in turn, each making three calls and ending without waiting
+    for them, give the bits of the same call on torch's stream."""
+    import threading
+    a = _qkv(2500, 4, 7900)
+    ref = bosa.attn_fwd(*a, causal=True, rope_base=10000.0)
+    torch.cuda.synchronize()
+    results, errors = [], []
+
+    def worker():
+        try:
+            for _ in range(3):
+                results.append(bosa.attn_fwd(*a, causal=True, rope_base=10000.0, stream=_PerThreadStream))
+        except Exception as e:   # surfaced below
+            errors.append(e)
+
+    for _ in range(3):
+        t = threading.Thread(target=worker)
+        t.start()
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    assert len(results) == 9
+    for i, r in enumerate(results):
+        assert _same(r, ref), f"call {i}"
