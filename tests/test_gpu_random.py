@@ -20,6 +20,7 @@ from test_gpu_backward import compare_grads
 pytestmark = pytest.mark.gpu
 
 N_FWD, N_BWD, N_RING, N_DEC = 200, 60, 40, 40
+N_BWD_BF16 = 40
 # cases of a longer sweep that sit at the edges of the float32 tolerances:
 # forward with ALiBi at distances near 1000 (|lse| in the hundreds), backward
 # with rows that see a single key (exact gradients cancel to zero)
@@ -79,8 +80,8 @@ def test_random_forward(case):
     compare(out.cpu(), lse.cpu(), ro, rl, "f32" if dtype == torch.float32 else "bf16", f"case {case}")
 
 
-@pytest.mark.parametrize("case", list(range(N_BWD)) + EXTRA_BWD)
-def test_random_backward(case):
+def _backward_case(case):
+    """Inputs and call arguments of random backward case `case`."""
     rng = np.random.default_rng(22000 + case)
     d = int(rng.choice([64, 128]))
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
@@ -101,6 +102,12 @@ def test_random_backward(case):
     kw = dict(q_off=q_off, kv_off=kv_off, causal=causal, kpm=None if kpm is None else kpm.to(DEV),
               attn_mask=None if am is None else am.to(DEV), rope_base=rope, window=window,
               alibi_slopes=None if slopes is None else slopes.to(DEV))
+    return (q, k, v, dout, kpm, am), kw, (q_off, kv_off, causal, rope, window, slopes)
+
+
+@pytest.mark.parametrize("case", list(range(N_BWD)) + EXTRA_BWD)
+def test_random_backward(case):
+    (q, k, v, dout, kpm, am), kw, (q_off, kv_off, causal, rope, window, slopes) = _backward_case(case)
     qd, kd, vd, od = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV)
     out, lse = bosa.attn_fwd(qd, kd, vd, **kw)
     grads = bosa.attn_bwd(qd, kd, vd, out, od, lse, flags=bosa.ATTN_OUT_F32, **kw)
@@ -110,6 +117,35 @@ def test_random_backward(case):
                                     attn_mask=None if am is None else am.numpy(), rope_base=rope, dtype="bf16",
                                     **_oracle_kw(window, slopes))
     compare_grads([g.cpu() for g in grads], ref, f"case {case}")
+
+
+@pytest.mark.parametrize("case", range(N_BWD_BF16))
+def test_random_backward_bf16_gradients_equal_rounded_float32(case):
+    """The bf16 gradients of a call (dk and dv written as final bf16 by the
+    dK/dV kernel, dk rotated back first; dq through the finalize pass) equal
+    the float32 gradients of the same call rounded to bf16: bit for bit for
+    dv, and for dk and dq without RoPE.  With RoPE the bf16 path rounds the
+    float64 back-rotation once, the float32 path rounds it to float32 and then
+    to bf16, which can differ by one bf16 unit where the float32 value lands
+    on a bf16 midpoint."""
+    (q, k, v, dout, _, _), kw, (_, _, _, rope, _, _) = _backward_case(1000 + case)
+    qd, kd, vd, od = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV)
+    out, lse = bosa.attn_fwd(qd, kd, vd, **kw)
+    g16 = bosa.attn_bwd(qd, kd, vd, out, od, lse, **kw)
+    g32 = bosa.attn_bwd(qd, kd, vd, out, od, lse, flags=bosa.ATTN_OUT_F32, **kw)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), g16, g32):
+        assert a.dtype == torch.bfloat16 and b.dtype == torch.float32, name
+        ia = a.cpu().view(torch.int16).to(torch.int32)
+        ib = b.cpu().to(torch.bfloat16).view(torch.int16).to(torch.int32)
+        if rope > 0 and name != "dv":
+            # one unit apart at most (same sign: the bit patterns are adjacent)
+            diff = (ia - ib).abs()
+            n = int((diff != 0).sum())
+            assert int(diff.max()) <= 1 if diff.numel() else True, f"case {case} {name}: more than one bf16 unit"
+            assert n <= max(2, diff.numel() // 1000), f"case {case} {name}: {n} of {diff.numel()} differ"
+        else:
+            assert torch.equal(ia, ib), f"case {case} {name}: not bit-identical"
 
 
 @pytest.mark.parametrize("case", range(N_RING))
