@@ -34,6 +34,7 @@ from .reference import (  # noqa: F401
     rope_frequencies,
     sdpa,
     sdpa_backward,
+    key_block_gradients,
     attention,
     attention_backward,
     alibi_bias,

@@ -269,6 +269,66 @@ def sdpa_backward(q, k, v, dout, q_pos, kv_pos, *, causal: bool = False, kpm=Non
     return dq, dk, dv
 
 
+def key_block_gradients(q, k, v, dout, out, lse, q_pos, kv_pos, key_rows, *, causal: bool = False, kpm=None,
+                        rope_base: float = 0.0, dtype: str = "bf16") -> Tuple[np.ndarray, np.ndarray]:
+    """dk, dv of the key rows ``key_rows`` alone, from dout, q, k, v and the
+    forward's final out and lse of every query row.
+
+    This is the block gradient of the brunomaga.github.io post ("Ring
+    Attention", item 3; "Implementation", the backward pass): a K/V block's
+    dk, dv follow from dout, the operands, the final out and the saved
+    log-sum-exp, without the other keys.  With s_ij the scaled score of the
+    rotated q'_i, k'_j and lse_i, out_i those of ``sdpa`` over all keys:
+        P_ij  = exp(s_ij - lse_i) on allowed pairs, 0 elsewhere,
+        dP_ij = dout_i . v_j,   delta_i = dout_i . out_i (= sum_l P_il dP_il),
+        dv_j  = sum_i P_ij dout_i,
+        dk'_j = (1/sqrt(d)) sum_i P_ij (dP_ij - delta_i) q'_i,   dk_j = R(pos_j)^T dk'_j,
+    the same chain rule as ``sdpa_backward``, restricted to the listed keys
+    (rows with lse = -inf see no key and contribute nothing).
+
+    q, dout: (B, Tq, H, d); k, v: (B, Tkv, H, d); out: (B, Tq, H, d) and lse
+    (B, H, Tq) from ``sdpa`` with the same arguments; key_rows: indices into
+    the key axis.  Returns float64 dk, dv of shape (B, len(key_rows), H, d).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    key_rows = np.asarray(key_rows, dtype=np.int64)
+    B, Tq, H, d = q.shape
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    kv_pos = np.asarray(kv_pos, dtype=np.int64)[key_rows]
+    k = k[:, key_rows]
+    v = v[:, key_rows]
+    qr, kr = q, k
+    if rope_base > 0:
+        qr = _rotated(q, q_pos, rope_base, dtype)
+        kr = _rotated(k, kv_pos, rope_base, dtype)
+    kpm_sel = None if kpm is None else np.asarray(kpm)[:, key_rows]
+    allowed = _allowed(B, Tq, len(key_rows), q_pos, kv_pos, causal, kpm_sel, None)
+    scale = 1.0 / math.sqrt(d)
+    dk = np.zeros_like(kr)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            ls = lse[b, h]
+            ok = allowed[b] & np.isfinite(ls)[:, None]
+            s = scale * (qr[b, :, h, :] @ kr[b, :, h, :].T)           # (Tq, n keys)
+            with np.errstate(over="ignore", invalid="ignore"):
+                p = np.where(ok, np.exp(s - np.where(np.isfinite(ls), ls, 0.0)[:, None]), 0.0)
+            g = dout[b, :, h, :]
+            dp = g @ v[b, :, h, :].T
+            delta = (g * out[b, :, h, :]).sum(axis=1)
+            ds = p * (dp - delta[:, None])
+            dv[b, :, h, :] = p.T @ g
+            dk[b, :, h, :] = scale * (ds.T @ qr[b, :, h, :])
+    if rope_base > 0:
+        dk = rope_rotate(dk, -kv_pos, rope_base)
+    return dk, dv
+
+
 def attention_backward(q, k, v, dout, *, q_off: int = 0, kv_off: int = 0, **kw):
     """``sdpa_backward`` with contiguous positions q_off + i and kv_off + j."""
     Tq = np.asarray(q).shape[1]

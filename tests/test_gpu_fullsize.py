@@ -134,10 +134,12 @@ def test_ring_backward_full_size_sampled():
     and dv obeys the exact identity sum_j dv_j = sum_i dout_i per (head,
     coordinate), since every row's probabilities sum to one.  The identity is
     checked within the rounding it allows: bf16 probabilities and bf16
-    outputs, at most 2^-9 relative each (doubled for margin).  The full
-    oracle of dk and dv at this size (all 16384 rows against 131072 keys) is
-    beyond the CPU budget of the suite; the ring backward at 8K keys covers
-    them element by element."""
+    outputs, at most 2^-9 relative each (doubled for margin).  dk and dv of
+    sampled key rows of every chunk (chunk 0, which two sub-calls touch, goes
+    through the float32 finalize pass; the other chunks get their final bf16
+    gradients from the dK/dV kernel) on one head match the oracle's block
+    gradients, built from the oracle's own out and lse of all 16384 local
+    rows."""
     w = workloads.WORKLOADS[4]
     note(f"{w.name}: drawing inputs")
     q, k, v, qpos = _ring_inputs(w)
@@ -152,6 +154,13 @@ def test_ring_backward_full_size_sampled():
     torch.cuda.synchronize()
     for name, g in (("dq", gq), ("dk", gk), ("dv", gv)):
         assert torch.isfinite(g.float()).all(), f"{name}: non-finite gradient"
+    rng_k = np.random.default_rng(45)
+    hk = int(rng_k.integers(w.H))
+    krows = _sample_rows(w.T, w.chunk, rng_k, extra=16)
+    krows = np.array(sorted(set(krows.tolist()) | {c0 + 4095 for c0 in range(0, w.T, w.chunk)}))
+    kidx = torch.from_numpy(krows).to(DEV)
+    gk_s = gk[:, kidx, hk:hk + 1].cpu()
+    gv_s = gv[:, kidx, hk:hk + 1].cpu()
     gq, gv = gq.cpu(), gv.cpu()
     del out, lse, gk, dq_, dk_, dv_
     # dq of sampled rows
@@ -180,3 +189,22 @@ def test_ring_backward_full_size_sampled():
     bound = 2.0 * 2.0 ** -9 * (av + ao)
     note(f"  sum dv - sum dout: max {err.max():.3e}, worst fraction of its bound {(err / bound).max():.3f}")
     assert np.all(err <= bound)
+    # dk, dv of sampled key rows of head hk: the oracle's out and lse of every
+    # local row (rows are independent in the forward), then its block gradients
+    Tl = q.shape[1]
+    qh, kh, vh, gh = (np64(x[:, :, hk:hk + 1]) for x in (q, k, v, dout))
+    o_ref = np.zeros((1, Tl, 1, w.d))
+    l_ref = np.zeros((1, 1, Tl))
+    note(f"  oracle: out and lse of all {Tl} local rows of head {hk}")
+    for r0 in range(0, Tl, 512):
+        rr = np.arange(r0, min(r0 + 512, Tl))
+        nk = int(qpos[rr].max()) + 1
+        o_ref[:, rr], l_ref[:, :, rr] = oracle.sdpa(qh[:, rr], kh[:, :nk], vh[:, :nk], qpos[rr], np.arange(nk),
+                                                    causal=True, rope_base=w.rope_base, dtype="bf16")
+    note(f"  oracle: dk, dv of {len(krows)} key rows of head {hk}")
+    rk, rv = oracle.key_block_gradients(qh, kh, vh, gh, o_ref, l_ref, qpos, np.arange(w.T), krows, causal=True,
+                                        rope_base=w.rope_base, dtype="bf16")
+    for name, got, ref in (("dk", gk_s, rk), ("dv", gv_s, rv)):
+        e = float(np.abs(np64(got) - ref).max()) / float(np.abs(ref).max())
+        note(f"  head {hk} {name} of sampled keys: max|err|/max|ref| = {e:.3e}")
+        assert e <= 2e-2, f"{name} head {hk}: relative error {e}"

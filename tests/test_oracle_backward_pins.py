@@ -164,3 +164,55 @@ def test_share_gradients_equal_full_sequence_gradients():
     np.testing.assert_allclose(dq_s, dq_f[:, rows], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(dk_s, dk_f, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(dv_s, dv_f, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", [
+    dict(causal=False, kp=0.0, rope=0.0, q_off=0, kv_off=0),
+    dict(causal=True, kp=0.0, rope=10000.0, q_off=40, kv_off=0),
+    dict(causal=True, kp=0.3, rope=500.0, q_off=5, kv_off=20),    # rows before the first key: lse = -inf
+    dict(causal=False, kp=0.5, rope=0.0, q_off=0, kv_off=0),
+])
+def test_key_block_gradients_equal_the_full_backward(case):
+    """``key_block_gradients`` (a key block's dk, dv from dout, the operands
+    and the forward's out and lse) against the rows of ``sdpa_backward``'s
+    full chain rule, for key subsets in any order, padded keys included.
+    Catches a delta summed over the block's keys only, a normalisation other
+    than the full row's lse, a missing back-rotation of dk, and a mask taken
+    for the wrong keys."""
+    B, Tq, Tkv, H, d = 2, 37, 53, 2, 16
+    rng = np.random.default_rng(3000 + Tq + int(case["rope"]) + int(10 * case["kp"]))
+    q, k, v, g = (_rand(s, 300 + i) for i, s in enumerate([(B, Tq, H, d), (B, Tkv, H, d), (B, Tkv, H, d),
+                                                            (B, Tq, H, d)]))
+    kpm = (rng.random((B, Tkv)) < case["kp"]).astype(np.uint8) if case["kp"] else None
+    qpos, kpos = case["q_off"] + np.arange(Tq), case["kv_off"] + np.arange(Tkv)
+    kw = dict(causal=case["causal"], kpm=kpm, rope_base=case["rope"], dtype="f32")
+    out, lse = oracle.sdpa(q, k, v, qpos, kpos, **kw)
+    rdq, rdk, rdv = oracle.sdpa_backward(q, k, v, g, qpos, kpos, **kw)
+    for rows in (np.arange(Tkv), rng.permutation(Tkv)[:11], np.array([0, Tkv - 1, 7])):
+        dk, dv = oracle.key_block_gradients(q, k, v, g, out, lse, qpos, kpos, rows, **kw)
+        sk = max(np.abs(rdk).max(), 1e-30)
+        sv = max(np.abs(rdv).max(), 1e-30)
+        assert np.abs(dk - rdk[:, rows]).max() <= 1e-10 * sk
+        assert np.abs(dv - rdv[:, rows]).max() <= 1e-10 * sv
+
+
+def test_key_block_gradients_finite_differences():
+    """Central finite differences of the forward oracle's loss with respect to
+    two listed key rows (causal, offsets, RoPE, key padding): the block
+    gradient is the derivative of the whole attention, not of the block's
+    own softmax."""
+    B, Tq, Tkv, H, d = 1, 9, 12, 1, 4
+    q, k, v, g = (_rand(s, 400 + i) for i, s in enumerate([(B, Tq, H, d), (B, Tkv, H, d), (B, Tkv, H, d),
+                                                            (B, Tq, H, d)]))
+    kpm = np.zeros((B, Tkv), dtype=np.uint8)
+    kpm[0, 5] = 1
+    kw = dict(q_off=6, kv_off=0, causal=True, kpm=kpm, rope_base=100.0, dtype="f64")
+    qpos, kpos = 6 + np.arange(Tq), np.arange(Tkv)
+    out, lse = oracle.sdpa(q, k, v, qpos, kpos, causal=True, kpm=kpm, rope_base=100.0, dtype="f64")
+    rows = np.array([2, 9])
+    dk, dv = oracle.key_block_gradients(q, k, v, g, out, lse, qpos, kpos, rows, causal=True, kpm=kpm,
+                                        rope_base=100.0, dtype="f64")
+    fk = _fd_grad(k, lambda x: _loss(q, x, v, g, **kw))
+    fv = _fd_grad(v, lambda x: _loss(q, k, x, g, **kw))
+    assert np.abs(dk - fk[:, rows]).max() <= 1e-6 * np.abs(fk).max()
+    assert np.abs(dv - fv[:, rows]).max() <= 1e-6 * np.abs(fv).max()
