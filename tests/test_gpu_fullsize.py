@@ -208,3 +208,61 @@ def test_ring_backward_full_size_sampled():
         e = float(np.abs(np64(got) - ref).max()) / float(np.abs(ref).max())
         note(f"  head {hk} {name} of sampled keys: max|err|/max|ref| = {e:.3e}")
         assert e <= 2e-2, f"{name} head {hk}: relative error {e}"
+
+
+def test_head_parallel_backward_full_size_sampled():
+    """The backward of the head-parallel share (4 heads x 131072 tokens,
+    causal, RoPE) in the configuration `bench.py --workload 6 --pass bwd`
+    times: one attn_bwd call (bf16 gradients, so every key block's dk and dv
+    are written as final bf16 by the dK/dV kernel).  Every gradient is
+    finite; dq of sampled rows on two heads matches the oracle; dk and dv of
+    sampled keys of the last chunk on one head match the oracle's block
+    gradients, built from the oracle's own out and lse of the rows that see
+    those keys (causal order: the last 8192 rows)."""
+    w = workloads.WORKLOADS[6]
+    note(f"{w.name}: drawing inputs")
+    q, k, v = (workloads.draw_tokens(w, t, range(w.n_chunks)) for t in (0, 1, 2))
+    dout = workloads.draw_tokens(w, 4, range(w.n_chunks))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    note("  running attn_fwd + attn_bwd")
+    out, lse = bosa.attn_fwd(qd, kd, vd, causal=True, rope_base=w.rope_base)
+    gq, gk, gv = bosa.attn_bwd(qd, kd, vd, out, dout.to(DEV), lse, causal=True, rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    for name, g in (("dq", gq), ("dk", gk), ("dv", gv)):
+        assert torch.isfinite(g.float()).all(), f"{name}: non-finite gradient"
+    gq, gk, gv = gq.cpu(), gk.cpu(), gv.cpu()
+    del out, lse, qd, kd, vd
+    pos = np.arange(w.T)
+    rng = np.random.default_rng(66)
+    rows = _sample_rows(w.T, w.chunk, rng, extra=8)
+    for h in (0, w.H - 1):
+        nk = int(rows.max()) + 1
+        note(f"  oracle: dq of {len(rows)} rows of head {h}")
+        rq, _, _ = oracle.sdpa_backward(np64(q[:, rows, h:h + 1]), np64(k[:, :nk, h:h + 1]), np64(v[:, :nk, h:h + 1]),
+                                        np64(dout[:, rows, h:h + 1]), rows, np.arange(nk), causal=True,
+                                        rope_base=w.rope_base, dtype="bf16")
+        e = float(np.abs(np64(gq[:, rows, h:h + 1]) - rq).max()) / float(np.abs(rq).max())
+        note(f"  head {h} dq: max|err|/max|ref| = {e:.3e}")
+        assert e <= 2e-2, f"dq head {h}: relative error {e}"
+    # dk, dv of sampled keys of the last chunk: only rows r0.. see them
+    r0 = w.T - w.chunk
+    krows = np.array(sorted({r0, r0 + 1, r0 + 63, r0 + 64, r0 + 4095, w.T - 2, w.T - 1}
+                            | set((r0 + rng.choice(w.chunk, size=24, replace=False)).tolist())))
+    h = int(rng.integers(w.H))
+    seen = np.arange(r0, w.T)
+    qh, kh, vh, gh = np64(q[:, seen, h:h + 1]), np64(k[:, :, h:h + 1]), np64(v[:, :, h:h + 1]), np64(dout[:, seen, h:h + 1])
+    o_ref = np.zeros((1, len(seen), 1, w.d))
+    l_ref = np.zeros((1, 1, len(seen)))
+    note(f"  oracle: out and lse of rows {r0}..{w.T - 1} of head {h}")
+    for b0 in range(0, len(seen), 512):
+        rr = np.arange(b0, min(b0 + 512, len(seen)))
+        nk = int(seen[rr].max()) + 1
+        o_ref[:, rr], l_ref[:, :, rr] = oracle.sdpa(qh[:, rr], kh[:, :nk], vh[:, :nk], seen[rr], np.arange(nk),
+                                                    causal=True, rope_base=w.rope_base, dtype="bf16")
+    note(f"  oracle: dk, dv of {len(krows)} key rows of head {h}")
+    rk, rv = oracle.key_block_gradients(qh, kh, vh, gh, o_ref, l_ref, seen, pos, krows, causal=True,
+                                        rope_base=w.rope_base, dtype="bf16")
+    for name, got, ref in (("dk", gk[:, krows, h:h + 1], rk), ("dv", gv[:, krows, h:h + 1], rv)):
+        e = float(np.abs(np64(got) - ref).max()) / float(np.abs(ref).max())
+        note(f"  head {h} {name} of sampled keys: max|err|/max|ref| = {e:.3e}")
+        assert e <= 2e-2, f"{name} head {h}: relative error {e}"
