@@ -668,7 +668,7 @@ def main() -> int:
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the ring on a single GPU (the ring itself is emulated "
-              "on that GPU); runs on more than one GPU are not part of this build. Use --gpus 1.",
+              "on that GPU); the library has no multi-GPU path (the ring's transfers are design only). Use --gpus 1.",
               file=sys.stderr)
         return 2
     # the default run also times workloads 2 and 3, in child processes started
