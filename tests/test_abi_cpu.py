@@ -194,3 +194,14 @@ def test_variant_and_decode_entry_points_reject_bad_arguments():
     assert app(k=None) == _lib.ATTN_ERR_INVALID_ARG
     assert app(k=P + 4) == _lib.ATTN_ERR_INVALID_ARG
     assert app(B=0, k=None, len=None) == 0
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    """With libattn.so absent, the loader and the entry points raise: there is
+    no CPU path to fall back to."""
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libattn.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError, match="no CPU fallback"):
+        _lib.load()
+    with pytest.raises(ImportError):
+        bosa.attn_ring_plan(8192, 4, 3, False, True)
